@@ -1,0 +1,166 @@
+/*
+ * c3d.h - C ABI of the MI355X (gfx950) library for the forward pass of 3D
+ * convolution and 3D transposed convolution, with fused epilogues.
+ *
+ * Sources ("page" = a POPCORNBENCH agent transcript, cited by its title):
+ *   "Kimi-K2.6 l1_p59"  Conv3d with a (k,k,1) kernel on a depth-last tensor
+ *   "Kimi-K2.6 l2_p72"  ConvTranspose3d -> BatchNorm3d -> AvgPool3d -> AvgPool3d
+ *   "Kimi-K2.6 l2_p43"  Conv3d -> MaxPool3d -> logsumexp(dim=1) -> ReLU
+ *   "Kimi-K2.6 l1_p77"  ConvTranspose3d with stride, padding and dilation
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are contiguous float32 in device memory, allocated and owned by
+ *   the caller; the library never allocates, frees or synchronises.
+ * - Shapes are int64_t[5] = {N, C, S0, S1, S2} with S2 fastest.  The kernel,
+ *   stride, padding and dilation triples apply to S0, S1, S2 in that order.
+ *   A depth-last tensor x[N,C,H,W,D] therefore needs no flag: it is S0=H,
+ *   S1=W, S2=D, and a (k,k,1) kernel convolves H and W only ("Kimi-K2.6
+ *   l1_p59", the passage that settles how PyTorch reads that kernel).
+ * - Arguments are validated on the host before anything is launched; on any
+ *   error nothing is launched and a non-zero c3d_status is returned.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *   null stream).  A launch failure reported by hipGetLastError maps to
+ *   C3D_ERR_HIP.  No exceptions cross the ABI; the calls keep no global
+ *   mutable state and are thread-safe.  Index arithmetic is 64-bit.
+ * - Pointers must be 4-byte aligned; 16-byte alignment enables the fast paths.
+ */
+#ifndef C3D_H
+#define C3D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    C3D_OK = 0,
+    C3D_ERR_NULL = 1,        /* a required pointer is NULL                           */
+    C3D_ERR_SHAPE = 2,       /* a dim is non-positive, channels/groups mismatch,     */
+                             /* or an output dim would be < 1                        */
+    C3D_ERR_PARAM = 3,       /* kernel/stride/dilation < 1, padding < 0, bad output  */
+                             /* padding, bad pool window, eps not finite and > 0     */
+    C3D_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the query returns  */
+    C3D_ERR_UNSUPPORTED = 5, /* valid request outside what this build implements     */
+    C3D_ERR_HIP = 6,         /* the HIP runtime reported an error at launch          */
+    C3D_ERR_ALIGN = 7        /* a pointer is not 4-byte aligned                      */
+} c3d_status;
+
+/* Convolution hyper-parameters, as in PyTorch's Conv3d / ConvTranspose3d
+ * constructors ("Kimi-K2.6 l1_p59", the module signature with stride,
+ * padding, dilation, groups and bias; "Kimi-K2.6 l1_p77", the transposed
+ * module with output_padding). */
+typedef struct {
+    int32_t kernel[3];     /* >= 1                                               */
+    int32_t stride[3];     /* >= 1                                               */
+    int32_t pad[3];        /* >= 0                                               */
+    int32_t dilation[3];   /* >= 1                                               */
+    int32_t output_pad[3]; /* transposed conv only: 0 <= op < max(stride, dil);  */
+                           /* must be 0 for the direct-conv calls                */
+    int32_t groups;        /* >= 1, divides both channel counts                  */
+} c3d_conv_params;
+
+/* Output shape of conv3d_fwd: per dim floor((S + 2p - d(k-1) - 1)/s) + 1
+ * ("Kimi-K2.6 l2_p43", the conv output-size formula).  Writes y_shape on
+ * success. */
+int c3d_conv3d_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+                         int64_t y_shape[5]);
+
+/* Output shape of conv_transpose3d_fwd: per dim (S-1)s - 2p + d(k-1) + op + 1
+ * ("Kimi-K2.6 l1_p77", the output-size formula with dilation). */
+int c3d_conv_transpose3d_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+                                   int64_t y_shape[5]);
+
+/* Output shape of convT_bn_avgpool: the transposed-conv shape with each
+ * spatial dim pooled in floor mode, floor((O - pool)/pool) + 1
+ * ("Kimi-K2.6 l2_p72", the AvgPool3d sizes 63 -> 31 -> 15). */
+int c3d_convT_bn_avgpool_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+                                   int32_t pool, int64_t y_shape[5]);
+
+/* Output shape of conv_maxpool_lse_relu: [N, 1, P0, P1, P2] with the conv
+ * shape pooled in floor mode ("Kimi-K2.6 l2_p43", MaxPool3d(2) then the
+ * keepdim logsumexp). */
+int c3d_conv_maxpool_lse_relu_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+                                        int32_t pool, int64_t y_shape[5]);
+
+/* Direct 3D convolution ("Kimi-K2.6 l1_p59", the output formula summed over
+ * the input channels of the group; "Kimi-K2.6 l2_p43", the per-output sum
+ * over c_in and the 3x3x3 window):
+ *   y[n,oc,o] = bias[oc] + sum_{icg,k} w[oc,icg,k] * x[n, g*Cin_g + icg, o*s - p + k*d]
+ * with g = oc / (Cout/groups) and zero outside x.
+ *   x     [N, Cin, S0, S1, S2]                (device, read)
+ *   w     [Cout, Cin/groups, k0, k1, k2]      (device, read)
+ *   bias  [Cout] or NULL                      (device, read)
+ *   y     [N, Cout, O0, O1, O2]               (device, written in full)
+ */
+int conv3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+               const c3d_conv_params* p, const float* bias, float* y, void* stream);
+
+/* 3D transposed convolution in its gather form ("Kimi-K2.6 l1_p77", the
+ * passages that map input i and tap k to output o = i*s - p + k*d and invert
+ * it as i = (o + p - k*d)/s when divisible; "Kimi-K2.6 l2_p72", the same test
+ * for stride 2, padding 1):
+ *   y[n, g*Cout_g + ocg, o] = bias + sum over ic of group g and taps k with
+ *       (o + p - k*d) divisible by s and i = (o + p - k*d)/s inside x
+ *       of x[n, ic, i] * w[ic, ocg, k]
+ *   x     [N, Cin, S0, S1, S2]                (device, read)
+ *   w     [Cin, Cout/groups, k0, k1, k2]      (device, read; PyTorch's layout)
+ *   bias  [Cout] or NULL                      (device, read)
+ *   y     [N, Cout, O0, O1, O2]               (device, written in full,
+ *                                              including positions no tap reaches)
+ */
+int conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+                         const c3d_conv_params* p, const float* bias, float* y, void* stream);
+
+/* Bytes of device workspace convT_bn_avgpool needs for these arguments. */
+size_t convT_bn_avgpool_workspace_bytes(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+                                        int32_t pool);
+
+/* Transposed conv -> BatchNorm3d with batch statistics -> average pool
+ * ("Kimi-K2.6 l2_p72": the module, the training-mode statistics with biased
+ * variance, and the proof that two AvgPool3d(2) stages equal one
+ * AvgPool3d(4, stride 4)).
+ *   t = conv_transpose3d(x, w, conv_bias)           (never written to HBM)
+ *   mean_c, var_c = batch mean and biased variance of t[:, c] over N and all
+ *                   O0*O1*O2 positions (including those pooling drops)
+ *   y[n,c,j] = gamma_c * (avg_{u in [0,pool)^3} t[n,c,pool*j+u] - mean_c)
+ *              / sqrt(var_c + eps) + beta_c
+ * Pooling is floor mode with window = stride = pool (pool = 4 is the module's
+ * two AvgPool3d(2)).
+ *   gamma, beta [Cout]                        (device, read; required)
+ *   y      [N, Cout, O0/pool, O1/pool, O2/pool] (device, written)
+ *   ws     >= convT_bn_avgpool_workspace_bytes(...) bytes (device, scratch;
+ *          its contents on entry do not matter)
+ *   batch_mean, batch_var [Cout] or NULL      (device, written if given: the
+ *          statistics of t including conv_bias; var is the biased one)
+ */
+int convT_bn_avgpool(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+                     const c3d_conv_params* p, const float* conv_bias, const float* gamma, const float* beta,
+                     float eps, int32_t pool, float* y, void* ws, size_t ws_bytes, float* batch_mean,
+                     float* batch_var, void* stream);
+
+/* Conv3d -> MaxPool3d(pool, stride pool) -> logsumexp over channels
+ * (keepdim) -> ReLU ("Kimi-K2.6 l2_p43": the module, floor-mode pooling and
+ * the max-shifted logsumexp):
+ *   t = conv3d(x, w, bias)                    (never written to HBM)
+ *   m[n,c,j] = max_{u in [0,pool)^3} t[n,c,pool*j+u]
+ *   y[n,0,j] = max(0, M + log(sum_c exp(m[n,c,j] - M))),  M = max_c m[n,c,j]
+ *   y      [N, 1, O0/pool, O1/pool, O2/pool]  (device, written)
+ */
+int conv_maxpool_lse_relu(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+                          const c3d_conv_params* p, const float* bias, int32_t pool, float* y, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* c3d_status_string(int status);
+
+/* Kernel-variant override for A/B tests: 0 = automatic (default), 1 = force
+ * the generic direct kernels.  Returns the previous value.  Process-wide;
+ * not for concurrent use with different settings. */
+int c3d_set_variant(int variant);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* C3D_H */

@@ -1,0 +1,154 @@
+"""Host-side checks of the C ABI: the library loads and exports every symbol
+include/c3d.h declares, the shape queries agree with the oracle's size rules,
+and invalid arguments are rejected before anything is launched.  No GPU is
+needed: every call here returns during host validation.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from transposed_convolution_epilogues_amd import binding as B
+from transposed_convolution_epilogues_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "c3d.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    syms = header_symbols()
+    for name in ("conv3d_fwd", "conv_transpose3d_fwd", "convT_bn_avgpool", "conv_maxpool_lse_relu"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.library()
+    syms = header_symbols()
+    assert len(syms) >= 10
+    for name in syms:
+        assert hasattr(lib, name), name
+    assert set(B.EXPORTS) == set(syms)
+
+
+def _p(k=3, s=1, p=0, d=1, op=0, g=1):
+    return B.make_params(k, s, p, d, op, g)
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_shape_queries_match_oracle(name):
+    wl = W.CONFIGS[name]
+    p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+    if wl.op == "conv3d":
+        got = B.conv3d_out_shape(wl.x_shape, wl.cout, p)
+    elif wl.op == "conv_transpose3d":
+        got = B.conv_transpose3d_out_shape(wl.x_shape, wl.cout, p)
+    elif wl.op == "convT_bn_avgpool":
+        got = B.convT_bn_avgpool_out_shape(wl.x_shape, wl.cout, p, wl.pool)
+    else:
+        got = B.conv_maxpool_lse_relu_out_shape(wl.x_shape, wl.cout, p, wl.pool)
+    assert got == O.output_shape(wl)
+
+
+def test_shape_queries_random_match_oracle():
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        op = "conv3d" if rng.integers(0, 2) else "conv_transpose3d"
+        wl = W.random_small_workload(op, rng)
+        p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+        ref = O.output_shape(wl)
+        fn = B.conv3d_out_shape if op == "conv3d" else B.conv_transpose3d_out_shape
+        if all(v > 0 for v in ref):
+            assert fn(wl.x_shape, wl.cout, p) == ref
+        else:
+            with pytest.raises(B.C3DError) as e:
+                fn(wl.x_shape, wl.cout, p)
+            assert e.value.status == 2
+
+
+def _call_conv(lib, x=1, w=1, y=1, shape=(1, 4, 8, 8, 8), cout=8, params=None, bias=None, fn="conv3d_fwd"):
+    params = params or _p(3, 1, 1)
+    vp = ctypes.c_void_p
+    # fake non-null aligned device addresses: these calls must fail validation
+    # before any pointer is dereferenced or any kernel is launched
+    ptr = lambda v: None if v is None else vp(4096 * v)
+    return getattr(lib, fn)(ptr(x), B._shape5(shape), ptr(w), cout, ctypes.byref(params),
+                            ptr(bias) if bias is not None else None, ptr(y), None)
+
+
+def test_errors_are_reported_before_launch():
+    lib = B.library()
+    assert _call_conv(lib, x=None) == 1
+    assert _call_conv(lib, w=None) == 1
+    assert _call_conv(lib, y=None) == 1
+    assert _call_conv(lib, shape=(1, 4, 0, 8, 8)) == 2
+    assert _call_conv(lib, shape=(1, 6, 8, 8, 8), params=_p(3, 1, 1, 1, 0, 4)) == 2  # Cin % groups
+    assert _call_conv(lib, cout=6, params=_p(3, 1, 1, 1, 0, 4), shape=(1, 8, 8, 8, 8)) == 2  # Cout % groups
+    assert _call_conv(lib, shape=(1, 4, 2, 8, 8), params=_p(3, 1, 0)) == 2  # empty output
+    assert _call_conv(lib, params=_p(0, 1, 1)) == 3
+    assert _call_conv(lib, params=_p(3, 0, 1)) == 3
+    assert _call_conv(lib, params=_p(3, 1, -1)) == 3
+    assert _call_conv(lib, params=_p(3, 1, 1, 0)) == 3
+    assert _call_conv(lib, params=_p(3, 1, 1, 1, 1)) == 3  # output_pad on a direct conv
+    assert _call_conv(lib, params=_p(3, 1, 1, 1, 0, 0)) == 3
+    # output_pad must be < max(stride, dilation) for the transposed conv
+    assert _call_conv(lib, fn="conv_transpose3d_fwd", params=_p(3, 2, 1, 1, 2)) == 3
+    assert _call_conv(lib, fn="conv_transpose3d_fwd", params=_p(3, 2, 1, 3, 2), x=None) == 1
+    # misaligned pointer
+    vp = ctypes.c_void_p
+    assert lib.conv3d_fwd(vp(4098), B._shape5((1, 4, 8, 8, 8)), vp(4096), 8, ctypes.byref(_p(3, 1, 1)), None,
+                          vp(8192), None) == 7
+
+
+def test_fused_op_errors_are_reported_before_launch():
+    lib = B.library()
+    vp = ctypes.c_void_p
+    p = _p(3, 2, 1)
+    xs = B._shape5((2, 3, 8, 8, 8))
+    ws_need = lib.convT_bn_avgpool_workspace_bytes(xs, 16, ctypes.byref(p), 4)
+    assert ws_need > 0
+    ok = dict(x=vp(4096), w=vp(8192), b=None, g=vp(12288), be=vp(16384), y=vp(20480), ws=vp(24576))
+
+    def call(eps=1e-5, pool=4, ws_bytes=ws_need, **kw):
+        a = dict(ok, **kw)
+        return lib.convT_bn_avgpool(a["x"], xs, a["w"], 16, ctypes.byref(p), a["b"], a["g"], a["be"], eps, pool,
+                                    a["y"], a["ws"], ws_bytes, None, None, None)
+
+    assert call(g=None) == 1
+    assert call(be=None) == 1
+    assert call(eps=0.0) == 3
+    assert call(eps=float("nan")) == 3
+    assert call(pool=0) == 3
+    assert call(pool=16) == 2  # ConvT output 15 < pool
+    assert call(ws=None) == 4
+    assert call(ws_bytes=ws_need - 1) == 4
+    assert call(ws=vp(24580)) == 7  # workspace must be 8-byte aligned
+    pc = _p(3, 1, 1)
+    assert lib.conv_maxpool_lse_relu(vp(4096), B._shape5((1, 4, 8, 8, 8)), vp(8192), 8, ctypes.byref(pc), None,
+                                     0, vp(12288), None) == 3
+    assert lib.conv_maxpool_lse_relu(vp(4096), B._shape5((1, 4, 1, 8, 8)), vp(8192), 8, ctypes.byref(pc), None,
+                                     2, vp(12288), None) == 2
+
+
+def test_status_strings():
+    lib = B.library()
+    for code in range(8):
+        assert lib.c3d_status_string(code)
+    assert lib.c3d_status_string(99) == b"unknown status"
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    x = torch.zeros(1, 4, 8, 8, 8)
+    w = torch.zeros(8, 4, 3, 3, 3)
+    with pytest.raises(TypeError):
+        B.conv3d_fwd(x, w, None, 1, 1, out=torch.zeros(1, 8, 8, 8, 8))

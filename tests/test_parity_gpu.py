@@ -1,0 +1,297 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle, on the
+same seeded inputs, element by element, at |gpu - ref| <= 1e-4 + 1e-4 |ref|
+(fp32 with inputs in [-1, 1]).
+
+Small and medium shapes (several tiles and a ragged tail) are compared in
+full; the five workload configurations run at full size in the same launch
+configuration the benchmark uses, compared on sampled outputs the oracle
+evaluates one by one, plus properties that hold on every output.  Outputs
+are poisoned with NaN first, so an unwritten element fails.  Both the
+automatic kernel choice and the forced generic kernels are exercised.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from transposed_convolution_epilogues_amd import binding as B
+from transposed_convolution_epilogues_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-4
+RTOL = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.library()
+    yield
+    B.set_variant(0)
+
+
+@pytest.fixture(params=[0, 1], ids=["auto", "generic"])
+def variant(request):
+    old = B.set_variant(request.param)
+    yield request.param
+    B.set_variant(old)
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def poisoned(shape):
+    return torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+
+
+def assert_close(name, got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    err = np.abs(got - ref)
+    bad = ~(err <= ATOL + RTOL * np.abs(ref))  # NaN counts as bad
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{name}: {int(bad.sum())}/{bad.size} outside tolerance; first {idx.tolist()} "
+                             f"got {got[bad][:5]} ref {ref[bad][:5]}")
+
+
+def run_gpu(wl, inp, out=None, ws=None, stats=False):
+    kw = dict(stride=wl.stride, pad=wl.pad, dilation=wl.dilation, groups=wl.groups)
+    x, w, b = dev(inp.x), dev(inp.w), dev(inp.b)
+    shape = O.output_shape(wl)
+    out = poisoned(shape) if out is None else out
+    if wl.op == "conv3d":
+        return B.conv3d_fwd(x, w, b, out=out, **kw)
+    if wl.op == "conv_transpose3d":
+        return B.conv_transpose3d_fwd(x, w, b, output_pad=wl.output_pad, out=out, **kw)
+    if wl.op == "convT_bn_avgpool":
+        mean = poisoned((wl.cout,))
+        var = poisoned((wl.cout,))
+        y = B.convT_bn_avgpool(x, w, b, dev(inp.gamma), dev(inp.beta), wl.eps, wl.pool, output_pad=wl.output_pad,
+                               out=out, workspace=ws, batch_mean=mean, batch_var=var, **kw)
+        return (y, mean, var) if stats else y
+    return B.conv_maxpool_lse_relu(x, w, b, wl.pool, out=out, **kw)
+
+
+def check_full(wl, inp, name):
+    ref = O.run_workload(wl, inp)
+    if wl.op == "convT_bn_avgpool":
+        y, mean, var = run_gpu(wl, inp, stats=True)
+        torch.cuda.synchronize()
+        assert_close(name + " out", y.cpu().numpy(), ref[0])
+        assert_close(name + " mean", mean.cpu().numpy(), ref[1])
+        assert_close(name + " var", var.cpu().numpy(), ref[2])
+        return y
+    y = run_gpu(wl, inp)
+    torch.cuda.synchronize()
+    assert_close(name, y.cpu().numpy(), ref)
+    return y
+
+
+# ------------------------------------------------------- random small sweep
+def _valid(wl):
+    try:
+        shape = O.output_shape(wl)
+    except Exception:
+        return False
+    return all(v > 0 for v in shape)
+
+
+def _random_cases(op, n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        base = "conv3d" if op in ("conv3d", "conv_maxpool_lse_relu") else "conv_transpose3d"
+        wl = W.random_small_workload(base, rng, max_spatial=9)
+        if op == "convT_bn_avgpool":
+            wl = wl.with_(op=op, pool=int(rng.integers(1, 4)))
+        elif op == "conv_maxpool_lse_relu":
+            wl = wl.with_(op=op, pool=int(rng.integers(1, 3)))
+        if _valid(wl):
+            out.append(wl)
+    return out
+
+
+@pytest.mark.parametrize("op", ["conv3d", "conv_transpose3d", "convT_bn_avgpool", "conv_maxpool_lse_relu"])
+def test_random_small_shapes(op, variant):
+    for i, wl in enumerate(_random_cases(op, 25, {"conv3d": 1, "conv_transpose3d": 2, "convT_bn_avgpool": 3,
+                                                  "conv_maxpool_lse_relu": 4}[op])):
+        inp = W.make_inputs(wl)
+        print(f"[{op} v{variant}] case {i}: {wl}", flush=True)
+        check_full(wl, inp, f"{op}#{i}")
+
+
+# ----------------------------------------------- medium shapes (many tiles)
+MEDIUM = {
+    # the fast paths' shapes, reduced so the oracle finishes in seconds, with ragged tails
+    "conv3d_k333": W.CONFIGS["c1"].with_(x_shape=(2, 32, 5, 11, 37), cout=64),
+    "conv3d_k333_cin20": W.CONFIGS["c1"].with_(x_shape=(1, 20, 4, 9, 70), cout=40),
+    "conv3d_k331_depthlast": W.CONFIGS["c2"].with_(x_shape=(2, 3, 19, 37, 10)),
+    "conv3d_k331_depthlast_d7": W.CONFIGS["c2"].with_(x_shape=(1, 3, 9, 40, 7), cout=48),
+    "convT_s2p1d2": W.CONFIGS["c3"].with_(x_shape=(2, 32, 5, 7, 19)),
+    "convT_s2p1d2_small_c": W.CONFIGS["c3"].with_(x_shape=(1, 12, 4, 6, 9), cout=24),
+    "convT_bn_pool": W.CONFIGS["c4"].with_(x_shape=(3, 3, 14, 13, 18)),
+    "convT_bn_pool_exact": W.CONFIGS["c4"].with_(x_shape=(2, 3, 16, 16, 16)),
+    "conv_pool_lse": W.CONFIGS["c5"].with_(x_shape=(1, 32, 6, 18, 70)),
+    "conv_pool_lse_odd": W.CONFIGS["c5"].with_(x_shape=(2, 32, 5, 9, 35), cout=64),
+}
+
+
+@pytest.mark.parametrize("name", list(MEDIUM))
+def test_medium_shapes(name, variant):
+    wl = MEDIUM[name]
+    print(f"[medium {name} v{variant}] {wl}", flush=True)
+    check_full(wl, W.make_inputs(wl), name)
+
+
+def test_c1_full():
+    wl = W.CONFIGS["c1"]
+    check_full(wl, W.make_inputs(wl), "c1")
+
+
+# ------------------------------------------- full-size workloads (sampled)
+def _sample(size, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(rng.integers(0, size, n))
+
+
+def test_c2_full_size_sampled():
+    wl = W.CONFIGS["c2"]
+    inp = W.make_inputs(wl)
+    y = run_gpu(wl, inp)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any().item()
+    flat = np.concatenate([_sample(y.numel(), 200_000, 21),
+                           np.arange(0, 2540 * 3), y.numel() - 1 - np.arange(2540 * 3)])
+    got = y.view(-1)[torch.from_numpy(flat).cuda()].cpu().numpy()
+    ref = O.conv3d_at(inp.x, inp.w, flat, inp.b, wl.stride, wl.pad, wl.dilation, wl.groups)
+    assert_close("c2 sampled", got, ref)
+    # repeat and compare bit for bit
+    y2 = run_gpu(wl, inp)
+    assert torch.equal(y, y2)
+
+
+def test_c3_full_size_sampled_and_checkerboard():
+    wl = W.CONFIGS["c3"]
+    inp = W.make_inputs(wl)
+    y = run_gpu(wl, inp)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (16, 64, 33, 65, 65)
+    # every output with an even coordinate is exactly zero (no bias)
+    odd = torch.zeros(y.shape[2:], dtype=torch.bool, device="cuda")
+    odd[1::2, 1::2, 1::2] = True
+    assert (y[:, :, ~odd] == 0).all().item()
+    assert not torch.isnan(y).any().item()
+    assert (y[:, :, odd] != 0).float().mean().item() > 0.999
+    # sampled values, weighted towards the odd sub-lattice
+    S = y.shape
+    rng = np.random.default_rng(31)
+    k = 150_000
+    n, c = rng.integers(0, S[0], k), rng.integers(0, S[1], k)
+    o0, o1, o2 = 2 * rng.integers(0, 16, k) + 1, 2 * rng.integers(0, 32, k) + 1, 2 * rng.integers(0, 32, k) + 1
+    flat = np.unique(np.concatenate([(((n * S[1] + c) * S[2] + o0) * S[3] + o1) * S[4] + o2,
+                                     _sample(y.numel(), 20_000, 32)]))
+    got = y.view(-1)[torch.from_numpy(flat).cuda()].cpu().numpy()
+    ref = O.conv_transpose3d_at(inp.x, inp.w, flat, inp.b, wl.stride, wl.pad, wl.dilation, wl.output_pad,
+                                wl.groups)
+    assert_close("c3 sampled", got, ref)
+    y2 = run_gpu(wl, inp)
+    assert torch.equal(y, y2)
+
+
+def test_c4_full_size():
+    wl = W.CONFIGS["c4"]
+    inp = W.make_inputs(wl)
+    y = check_full(wl, inp, "c4")
+    # repeat (the workspace is reused) and compare bit for bit
+    y2 = run_gpu(wl, inp)
+    assert torch.equal(y, y2)
+
+
+def test_c5_full_size_sampled():
+    wl = W.CONFIGS["c5"]
+    inp = W.make_inputs(wl)
+    y = run_gpu(wl, inp)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (4, 1, 16, 64, 64)
+    assert torch.isfinite(y).all().item() and (y >= 0).all().item()
+    flat = np.concatenate([_sample(y.numel(), 3000, 51), np.arange(0, 64), y.numel() - 1 - np.arange(64)])
+    got = y.view(-1)[torch.from_numpy(flat).cuda()].cpu().numpy()
+    ref = O.conv_maxpool_lse_relu_at(inp.x, inp.w, inp.b, flat, wl.pool, wl.stride, wl.pad, wl.dilation,
+                                     wl.groups)
+    assert_close("c5 sampled", got, ref)
+    y2 = run_gpu(wl, inp)
+    assert torch.equal(y, y2)
+
+
+# ----------------------------------------------------------- edge cases
+EDGE = {
+    "conv_1x1x1_single": W.make("e", "conv3d", (1, 1, 1, 1, 1), 1, 1, bias=True, seed=7),
+    "conv_kernel_equals_input": W.make("e", "conv3d", (2, 3, 3, 3, 3), 5, 3, seed=8),
+    "conv_big_stride": W.make("e", "conv3d", (1, 2, 9, 9, 9), 3, 2, stride=5, pad=2, seed=9),
+    "conv_groups_depthwise": W.make("e", "conv3d", (1, 4, 6, 6, 6), 4, 3, pad=1, groups=4, seed=10),
+    "convT_1x1x1": W.make("e", "conv_transpose3d", (1, 2, 1, 1, 1), 3, 1, seed=11),
+    "convT_outpad_max": W.make("e", "conv_transpose3d", (1, 2, 3, 4, 5), 2, 3, stride=3, pad=1, dilation=2,
+                               output_pad=2, seed=12),
+    "convT_pad_exceeds_taps": W.make("e", "conv_transpose3d", (1, 2, 6, 6, 6), 2, 3, stride=1, pad=3, seed=13),
+    "bn_pool_single_window": W.make("e", "convT_bn_avgpool", (1, 3, 2, 2, 2), 4, 3, stride=2, pad=1, pool=3,
+                                    seed=14),
+    "bn_pool_pool1": W.make("e", "convT_bn_avgpool", (2, 2, 3, 3, 3), 3, 3, stride=2, pad=1, pool=1, seed=15),
+    "lse_single_channel": W.make("e", "conv_maxpool_lse_relu", (1, 2, 4, 4, 4), 1, 3, pad=1, pool=2, seed=16),
+    "lse_pool_whole": W.make("e", "conv_maxpool_lse_relu", (1, 3, 4, 4, 4), 6, 3, pad=1, pool=4, seed=17),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_cases(name, variant):
+    wl = EDGE[name]
+    check_full(wl, W.make_inputs(wl), name)
+
+
+def test_lse_all_negative_gives_zero_and_large_values():
+    # a strongly negative bias makes every logsumexp negative: ReLU gives exactly 0;
+    # a large positive input exercises the max shift
+    wl = W.make("e", "conv_maxpool_lse_relu", (1, 4, 4, 6, 6), 8, 3, pad=1, pool=2, seed=18)
+    inp = W.make_inputs(wl)
+    inp.b[:] = -50.0
+    y = run_gpu(wl, inp)
+    torch.cuda.synchronize()
+    assert (y == 0).all().item()
+    inp.b[:] = 80.0
+    inp.x[:] = inp.x * 30
+    check_full(wl, inp, "lse_large")
+
+
+def test_c4_module_with_random_bias_and_stats_outputs():
+    wl = W.CONFIGS["c4"].with_(x_shape=(2, 3, 10, 12, 9))
+    inp = W.make_inputs(wl)
+    check_full(wl, inp, "c4 small stats")
+
+
+def test_nonpositive_eps_and_small_workspace_rejected():
+    wl = W.CONFIGS["c4"].with_(x_shape=(1, 3, 8, 8, 8))
+    inp = W.make_inputs(wl)
+    x, w = dev(inp.x), dev(inp.w)
+    with pytest.raises(B.C3DError) as e:
+        B.convT_bn_avgpool(x, w, dev(inp.b), dev(inp.gamma), dev(inp.beta), eps=0.0)
+    assert e.value.status == 3
+    with pytest.raises(B.C3DError) as e:
+        B.convT_bn_avgpool(x, w, dev(inp.b), dev(inp.gamma), dev(inp.beta),
+                           workspace=torch.empty(8, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == 4
+
+
+def test_runs_on_a_side_stream():
+    wl = W.CONFIGS["c1"]
+    inp = W.make_inputs(wl)
+    ref = O.run_workload(wl, inp)
+    s = torch.cuda.Stream()
+    x, w, b = dev(inp.x), dev(inp.w), dev(inp.b)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y = B.conv3d_fwd(x, w, b, wl.stride, wl.pad, out=poisoned(ref.shape), stream=s)
+    s.synchronize()
+    assert_close("side stream", y.cpu().numpy(), ref)

@@ -1,0 +1,248 @@
+"""ctypes binding of the C ABI in include/c3d.h (argument marshalling only).
+
+Each function takes PyTorch tensors that already live on the GPU, checks that
+they are contiguous float32 device tensors, and passes raw device pointers,
+shapes and the current HIP stream to libc3d.so.  Every step of the
+computation runs in the library's HIP kernels; there is no CPU or PyTorch
+fallback, and a missing library is an error.  Output and workspace tensors
+are allocated with PyTorch when the caller does not pass them (memory only).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libc3d.so")
+
+C3D_OK = 0
+STATUS = {0: "C3D_OK", 1: "C3D_ERR_NULL", 2: "C3D_ERR_SHAPE", 3: "C3D_ERR_PARAM", 4: "C3D_ERR_WORKSPACE",
+          5: "C3D_ERR_UNSUPPORTED", 6: "C3D_ERR_HIP", 7: "C3D_ERR_ALIGN"}
+
+EXPORTS = ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_bn_avgpool_out_shape",
+           "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
+           "convT_bn_avgpool_workspace_bytes", "convT_bn_avgpool", "conv_maxpool_lse_relu", "c3d_status_string",
+           "c3d_set_variant")
+
+
+class C3DError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_lib().c3d_status_string(status).decode()})")
+
+
+class ConvParams(ctypes.Structure):
+    """Mirror of c3d_conv_params."""
+    _fields_ = [("kernel", ctypes.c_int32 * 3), ("stride", ctypes.c_int32 * 3), ("pad", ctypes.c_int32 * 3),
+                ("dilation", ctypes.c_int32 * 3), ("output_pad", ctypes.c_int32 * 3), ("groups", ctypes.c_int32)]
+
+
+Int3 = Union[int, Sequence[int]]
+
+
+def _t3(v: Int3) -> Tuple[int, int, int]:
+    if isinstance(v, int):
+        return (v, v, v)
+    v = tuple(int(a) for a in v)
+    if len(v) != 3:
+        raise ValueError("expected an int or a 3-sequence")
+    return v  # type: ignore[return-value]
+
+
+def make_params(kernel: Int3, stride: Int3 = 1, pad: Int3 = 0, dilation: Int3 = 1, output_pad: Int3 = 0,
+                groups: int = 1) -> ConvParams:
+    p = ConvParams()
+    for name, v in (("kernel", kernel), ("stride", stride), ("pad", pad), ("dilation", dilation),
+                    ("output_pad", output_pad)):
+        arr = getattr(p, name)
+        for j, a in enumerate(_t3(v)):
+            arr[j] = a
+    p.groups = int(groups)
+    return p
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library {LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    P = ctypes.POINTER(ConvParams)
+    vp = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.c3d_conv3d_out_shape.argtypes = [i64p, i64, P, i64p]
+    lib.c3d_conv_transpose3d_out_shape.argtypes = [i64p, i64, P, i64p]
+    lib.c3d_convT_bn_avgpool_out_shape.argtypes = [i64p, i64, P, ctypes.c_int32, i64p]
+    lib.c3d_conv_maxpool_lse_relu_out_shape.argtypes = [i64p, i64, P, ctypes.c_int32, i64p]
+    lib.conv3d_fwd.argtypes = [vp, i64p, vp, i64, P, vp, vp, vp]
+    lib.conv_transpose3d_fwd.argtypes = [vp, i64p, vp, i64, P, vp, vp, vp]
+    lib.convT_bn_avgpool_workspace_bytes.argtypes = [i64p, i64, P, ctypes.c_int32]
+    lib.convT_bn_avgpool_workspace_bytes.restype = ctypes.c_size_t
+    lib.convT_bn_avgpool.argtypes = [vp, i64p, vp, i64, P, vp, vp, vp, ctypes.c_float, ctypes.c_int32, vp, vp,
+                                     ctypes.c_size_t, vp, vp, vp]
+    lib.conv_maxpool_lse_relu.argtypes = [vp, i64p, vp, i64, P, vp, ctypes.c_int32, vp, vp]
+    lib.c3d_status_string.argtypes = [ctypes.c_int]
+    lib.c3d_status_string.restype = ctypes.c_char_p
+    lib.c3d_set_variant.argtypes = [ctypes.c_int]
+    for name in ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_bn_avgpool_out_shape",
+                 "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
+                 "convT_bn_avgpool", "conv_maxpool_lse_relu", "c3d_set_variant"):
+        getattr(lib, name).restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _lib()
+
+
+def _shape5(shape) -> ctypes.Array:
+    if len(shape) != 5:
+        raise ValueError("expected a 5-D shape [N, C, S0, S1, S2]")
+    return (ctypes.c_int64 * 5)(*[int(v) for v in shape])
+
+
+def _dev(t: Optional[torch.Tensor], name: str, required: bool = True):
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.float32:
+        raise TypeError(f"{name} must be a float32 tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(st: int, where: str):
+    if st != C3D_OK:
+        raise C3DError(st, where)
+
+
+def set_variant(variant: int) -> int:
+    """0 = automatic kernel choice, 1 = force the generic direct kernels."""
+    return int(_lib().c3d_set_variant(int(variant)))
+
+
+def conv3d_out_shape(x_shape, cout: int, params: ConvParams) -> Tuple[int, ...]:
+    ys = (ctypes.c_int64 * 5)()
+    _check(_lib().c3d_conv3d_out_shape(_shape5(x_shape), int(cout), ctypes.byref(params), ys),
+           "c3d_conv3d_out_shape")
+    return tuple(int(v) for v in ys)
+
+
+def conv_transpose3d_out_shape(x_shape, cout: int, params: ConvParams) -> Tuple[int, ...]:
+    ys = (ctypes.c_int64 * 5)()
+    _check(_lib().c3d_conv_transpose3d_out_shape(_shape5(x_shape), int(cout), ctypes.byref(params), ys),
+           "c3d_conv_transpose3d_out_shape")
+    return tuple(int(v) for v in ys)
+
+
+def convT_bn_avgpool_out_shape(x_shape, cout: int, params: ConvParams, pool: int) -> Tuple[int, ...]:
+    ys = (ctypes.c_int64 * 5)()
+    _check(_lib().c3d_convT_bn_avgpool_out_shape(_shape5(x_shape), int(cout), ctypes.byref(params), int(pool), ys),
+           "c3d_convT_bn_avgpool_out_shape")
+    return tuple(int(v) for v in ys)
+
+
+def conv_maxpool_lse_relu_out_shape(x_shape, cout: int, params: ConvParams, pool: int) -> Tuple[int, ...]:
+    ys = (ctypes.c_int64 * 5)()
+    _check(_lib().c3d_conv_maxpool_lse_relu_out_shape(_shape5(x_shape), int(cout), ctypes.byref(params),
+                                                      int(pool), ys), "c3d_conv_maxpool_lse_relu_out_shape")
+    return tuple(int(v) for v in ys)
+
+
+def conv3d_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, stride: Int3 = 1,
+               pad: Int3 = 0, dilation: Int3 = 1, groups: int = 1, out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """y = conv3d(x, w, bias); w is [Cout, Cin/groups, k0, k1, k2]."""
+    params = make_params(tuple(w.shape[2:]), stride, pad, dilation, 0, groups)
+    cout = int(w.shape[0])
+    ys = conv3d_out_shape(x.shape, cout, params)
+    if out is None:
+        out = torch.empty(ys, dtype=torch.float32, device=x.device)
+    elif tuple(out.shape) != ys:
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {ys}")
+    _check(_lib().conv3d_fwd(_dev(x, "x"), _shape5(x.shape), _dev(w, "w"), cout, ctypes.byref(params),
+                             _dev(bias, "bias", False), _dev(out, "out"), _stream(stream)), "conv3d_fwd")
+    return out
+
+
+def conv_transpose3d_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, stride: Int3 = 1,
+                         pad: Int3 = 0, dilation: Int3 = 1, output_pad: Int3 = 0, groups: int = 1,
+                         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = conv_transpose3d(x, w, bias); w is [Cin, Cout/groups, k0, k1, k2]."""
+    params = make_params(tuple(w.shape[2:]), stride, pad, dilation, output_pad, groups)
+    cout = int(w.shape[1]) * int(groups)
+    ys = conv_transpose3d_out_shape(x.shape, cout, params)
+    if out is None:
+        out = torch.empty(ys, dtype=torch.float32, device=x.device)
+    elif tuple(out.shape) != ys:
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {ys}")
+    _check(_lib().conv_transpose3d_fwd(_dev(x, "x"), _shape5(x.shape), _dev(w, "w"), cout, ctypes.byref(params),
+                                       _dev(bias, "bias", False), _dev(out, "out"), _stream(stream)),
+           "conv_transpose3d_fwd")
+    return out
+
+
+def convT_bn_avgpool_workspace_bytes(x_shape, cout: int, params: ConvParams, pool: int) -> int:
+    return int(_lib().convT_bn_avgpool_workspace_bytes(_shape5(x_shape), int(cout), ctypes.byref(params),
+                                                       int(pool)))
+
+
+def convT_bn_avgpool(x: torch.Tensor, w: torch.Tensor, conv_bias: Optional[torch.Tensor], gamma: torch.Tensor,
+                     beta: torch.Tensor, eps: float = 1e-5, pool: int = 4, stride: Int3 = 2, pad: Int3 = 1,
+                     dilation: Int3 = 1, output_pad: Int3 = 0, groups: int = 1,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     batch_mean: Optional[torch.Tensor] = None, batch_var: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """ConvTranspose3d -> BatchNorm3d (batch statistics) -> AvgPool3d(pool)."""
+    params = make_params(tuple(w.shape[2:]), stride, pad, dilation, output_pad, groups)
+    cout = int(w.shape[1]) * int(groups)
+    ys = convT_bn_avgpool_out_shape(x.shape, cout, params, pool)
+    if out is None:
+        out = torch.empty(ys, dtype=torch.float32, device=x.device)
+    nbytes = convT_bn_avgpool_workspace_bytes(x.shape, cout, params, pool)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=x.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr())
+    _check(_lib().convT_bn_avgpool(_dev(x, "x"), _shape5(x.shape), _dev(w, "w"), cout, ctypes.byref(params),
+                                   _dev(conv_bias, "conv_bias", False), _dev(gamma, "gamma"), _dev(beta, "beta"),
+                                   float(eps), int(pool), _dev(out, "out"), ws_ptr,
+                                   workspace.numel() * workspace.element_size(),
+                                   _dev(batch_mean, "batch_mean", False), _dev(batch_var, "batch_var", False),
+                                   _stream(stream)), "convT_bn_avgpool")
+    return out
+
+
+def conv_maxpool_lse_relu(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, pool: int = 2,
+                          stride: Int3 = 1, pad: Int3 = 1, dilation: Int3 = 1, groups: int = 1,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Conv3d -> MaxPool3d(pool) -> logsumexp over channels (keepdim) -> ReLU."""
+    params = make_params(tuple(w.shape[2:]), stride, pad, dilation, 0, groups)
+    cout = int(w.shape[0])
+    ys = conv_maxpool_lse_relu_out_shape(x.shape, cout, params, pool)
+    if out is None:
+        out = torch.empty(ys, dtype=torch.float32, device=x.device)
+    _check(_lib().conv_maxpool_lse_relu(_dev(x, "x"), _shape5(x.shape), _dev(w, "w"), cout, ctypes.byref(params),
+                                        _dev(bias, "bias", False), int(pool), _dev(out, "out"), _stream(stream)),
+           "conv_maxpool_lse_relu")
+    return out

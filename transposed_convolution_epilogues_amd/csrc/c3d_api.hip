@@ -1,0 +1,254 @@
+// c3d_api.hip - the C ABI declared in include/c3d.h: host-side validation,
+// output-shape rules, and dispatch to the fast or the generic kernels.
+#include <atomic>
+#include <math.h>
+
+#include "../../include/c3d.h"
+#include "c3d_internal.h"
+
+using c3d::Geom;
+using c3d::PoolGeom;
+
+namespace {
+
+std::atomic<int> g_variant{0};
+
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int64_t conv_len(int64_t L, int32_t k, int32_t s, int32_t p, int32_t d) {
+    // floor((L + 2p - d(k-1) - 1)/s) + 1  ("Kimi-K2.6 l2_p43", conv output size)
+    const int64_t num = L + 2 * (int64_t)p - (int64_t)d * (k - 1) - 1;
+    return num < 0 ? 0 : num / s + 1;
+}
+
+int64_t convT_len(int64_t L, int32_t k, int32_t s, int32_t p, int32_t d, int32_t op) {
+    // (L-1)s - 2p + d(k-1) + op + 1  ("Kimi-K2.6 l1_p77", with dilation)
+    return (L - 1) * s - 2 * (int64_t)p + (int64_t)d * (k - 1) + op + 1;
+}
+
+int check_params(const c3d_conv_params* p, bool transposed) {
+    for (int j = 0; j < 3; ++j) {
+        if (p->kernel[j] < 1 || p->stride[j] < 1 || p->dilation[j] < 1 || p->pad[j] < 0) return C3D_ERR_PARAM;
+        if (p->kernel[j] > 64 || p->stride[j] > 1024 || p->dilation[j] > 1024 || p->pad[j] > 65536)
+            return C3D_ERR_PARAM;
+        if (transposed) {
+            const int32_t lim = p->stride[j] > p->dilation[j] ? p->stride[j] : p->dilation[j];
+            if (p->output_pad[j] < 0 || p->output_pad[j] >= lim) return C3D_ERR_PARAM;
+        } else if (p->output_pad[j] != 0) {
+            return C3D_ERR_PARAM;
+        }
+    }
+    if (p->groups < 1) return C3D_ERR_PARAM;
+    return C3D_OK;
+}
+
+// Resolves and validates the geometry.  No HIP call is made here.
+int resolve(const int64_t xs[5], int64_t cout, const c3d_conv_params* p, bool transposed, Geom* g) {
+    if (!xs || !p || !g) return C3D_ERR_NULL;
+    int st = check_params(p, transposed);
+    if (st) return st;
+    for (int j = 0; j < 5; ++j)
+        if (xs[j] < 1 || xs[j] > ((int64_t)1 << 40)) return C3D_ERR_SHAPE;
+    if (cout < 1 || cout > ((int64_t)1 << 30)) return C3D_ERR_SHAPE;
+    if (xs[1] % p->groups != 0 || cout % p->groups != 0) return C3D_ERR_SHAPE;
+    g->N = xs[0];
+    g->Cin = xs[1];
+    g->Cout = cout;
+    for (int j = 0; j < 3; ++j) {
+        g->S[j] = xs[2 + j];
+        g->k[j] = p->kernel[j];
+        g->s[j] = p->stride[j];
+        g->p[j] = p->pad[j];
+        g->d[j] = p->dilation[j];
+        g->O[j] = transposed ? convT_len(xs[2 + j], p->kernel[j], p->stride[j], p->pad[j], p->dilation[j],
+                                         p->output_pad[j])
+                             : conv_len(xs[2 + j], p->kernel[j], p->stride[j], p->pad[j], p->dilation[j]);
+        if (g->O[j] < 1) return C3D_ERR_SHAPE;
+    }
+    g->groups = p->groups;
+    g->cin_g = (int32_t)(xs[1] / p->groups);
+    g->cout_g = (int32_t)(cout / p->groups);
+    // total element counts must fit comfortably in int64
+    const double outs = (double)g->N * (double)g->Cout * (double)g->O[0] * (double)g->O[1] * (double)g->O[2];
+    const double ins = (double)g->N * (double)g->Cin * (double)g->S[0] * (double)g->S[1] * (double)g->S[2];
+    if (outs > 9.0e15 || ins > 9.0e15) return C3D_ERR_SHAPE;
+    return C3D_OK;
+}
+
+int resolve_pool(const Geom& g, int32_t pool, PoolGeom* pg) {
+    if (pool < 1 || pool > 64) return C3D_ERR_PARAM;
+    pg->g = g;
+    pg->pool = pool;
+    for (int j = 0; j < 3; ++j) {
+        if (g.O[j] < pool) return C3D_ERR_SHAPE;
+        pg->P[j] = (g.O[j] - pool) / pool + 1;  // floor mode
+        pg->C[j] = c3d::ceil_div(g.O[j], pool);
+    }
+    return C3D_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? C3D_OK : C3D_ERR_HIP; }
+
+void write_shape(const Geom& g, int64_t ys[5]) {
+    ys[0] = g.N;
+    ys[1] = g.Cout;
+    for (int j = 0; j < 3; ++j) ys[2 + j] = g.O[j];
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int c3d_set_variant(int variant) { return g_variant.exchange(variant); }
+
+const char* c3d_status_string(int status) {
+    switch (status) {
+        case C3D_OK: return "ok";
+        case C3D_ERR_NULL: return "a required pointer is NULL";
+        case C3D_ERR_SHAPE: return "invalid shape (non-positive dim, channel/groups mismatch or empty output)";
+        case C3D_ERR_PARAM: return "invalid parameter (kernel/stride/dilation/padding/output_padding/pool/eps)";
+        case C3D_ERR_WORKSPACE: return "workspace missing or too small";
+        case C3D_ERR_UNSUPPORTED: return "unsupported request";
+        case C3D_ERR_HIP: return "HIP runtime error at launch";
+        case C3D_ERR_ALIGN: return "pointer not 4-byte aligned";
+        default: return "unknown status";
+    }
+}
+
+int c3d_conv3d_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int64_t y_shape[5]) {
+    if (!y_shape) return C3D_ERR_NULL;
+    Geom g;
+    int st = resolve(x_shape, cout, p, false, &g);
+    if (st) return st;
+    write_shape(g, y_shape);
+    return C3D_OK;
+}
+
+int c3d_conv_transpose3d_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+                                   int64_t y_shape[5]) {
+    if (!y_shape) return C3D_ERR_NULL;
+    Geom g;
+    int st = resolve(x_shape, cout, p, true, &g);
+    if (st) return st;
+    write_shape(g, y_shape);
+    return C3D_OK;
+}
+
+int c3d_convT_bn_avgpool_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+                                   int32_t pool, int64_t y_shape[5]) {
+    if (!y_shape) return C3D_ERR_NULL;
+    Geom g;
+    PoolGeom pg;
+    int st = resolve(x_shape, cout, p, true, &g);
+    if (st) return st;
+    st = resolve_pool(g, pool, &pg);
+    if (st) return st;
+    y_shape[0] = g.N;
+    y_shape[1] = g.Cout;
+    for (int j = 0; j < 3; ++j) y_shape[2 + j] = pg.P[j];
+    return C3D_OK;
+}
+
+int c3d_conv_maxpool_lse_relu_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+                                        int32_t pool, int64_t y_shape[5]) {
+    if (!y_shape) return C3D_ERR_NULL;
+    Geom g;
+    PoolGeom pg;
+    int st = resolve(x_shape, cout, p, false, &g);
+    if (st) return st;
+    st = resolve_pool(g, pool, &pg);
+    if (st) return st;
+    y_shape[0] = g.N;
+    y_shape[1] = 1;
+    for (int j = 0; j < 3; ++j) y_shape[2 + j] = pg.P[j];
+    return C3D_OK;
+}
+
+int conv3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout, const c3d_conv_params* p,
+               const float* bias, float* y, void* stream) {
+    if (!x || !w || !y) return C3D_ERR_NULL;
+    if (!aligned4(x) || !aligned4(w) || !aligned4(y) || !aligned4(bias)) return C3D_ERR_ALIGN;
+    Geom g;
+    int st = resolve(x_shape, cout, p, false, &g);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (g_variant.load() == 0) {
+        if (c3d::conv_k1last_supported(g, x, w, y)) return hip_status(c3d::launch_conv_k1last(x, w, bias, y, g, s));
+        if (c3d::conv3x3x3_mfma_supported(g, x, w, y))
+            return hip_status(c3d::launch_conv3x3x3_mfma(x, w, bias, y, g, s));
+    }
+    return hip_status(c3d::launch_conv3d_direct(x, w, bias, y, g, s));
+}
+
+int conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+                         const c3d_conv_params* p, const float* bias, float* y, void* stream) {
+    if (!x || !w || !y) return C3D_ERR_NULL;
+    if (!aligned4(x) || !aligned4(w) || !aligned4(y) || !aligned4(bias)) return C3D_ERR_ALIGN;
+    Geom g;
+    int st = resolve(x_shape, cout, p, true, &g);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (g_variant.load() == 0 && c3d::convT_s2_sublattice_supported(g, x, w, y))
+        return hip_status(c3d::launch_convT_s2_sublattice(x, w, bias, y, g, s));
+    return hip_status(c3d::launch_convT_gather(x, w, bias, y, g, s));
+}
+
+size_t convT_bn_avgpool_workspace_bytes(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+                                        int32_t pool) {
+    Geom g;
+    PoolGeom pg;
+    if (resolve(x_shape, cout, p, true, &g) || resolve_pool(g, pool, &pg)) return 0;
+    // two float64 partials (sum, sum of squares) per phase-1 block and channel
+    return c3d::convT_bn_pool_partials(pg, 0) * (size_t)g.Cout * 2 * sizeof(double);
+}
+
+int convT_bn_avgpool(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+                     const c3d_conv_params* p, const float* conv_bias, const float* gamma, const float* beta,
+                     float eps, int32_t pool, float* y, void* ws, size_t ws_bytes, float* batch_mean,
+                     float* batch_var, void* stream) {
+    if (!x || !w || !y || !gamma || !beta) return C3D_ERR_NULL;
+    if (!aligned4(x) || !aligned4(w) || !aligned4(y) || !aligned4(conv_bias) || !aligned4(gamma) ||
+        !aligned4(beta) || !aligned4(batch_mean) || !aligned4(batch_var))
+        return C3D_ERR_ALIGN;
+    if (!(eps > 0.f) || !isfinite(eps)) return C3D_ERR_PARAM;
+    Geom g;
+    PoolGeom pg;
+    int st = resolve(x_shape, cout, p, true, &g);
+    if (st) return st;
+    st = resolve_pool(g, pool, &pg);
+    if (st) return st;
+    const size_t parts = c3d::convT_bn_pool_partials(pg, 0);
+    const size_t need = parts * (size_t)g.Cout * 2 * sizeof(double);
+    if (!ws || ws_bytes < need) return C3D_ERR_WORKSPACE;
+    if (((uintptr_t)ws & 7u) != 0) return C3D_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    double* part = (double*)ws;
+    hipError_t e;
+    if (g_variant.load() == 0 && c3d::convT_bn_pool_fast_supported(pg, x))
+        e = c3d::launch_convT_bn_pool_phase1_fast(x, w, y, part, pg, s);
+    else
+        e = c3d::launch_convT_bn_pool_phase1_direct(x, w, y, part, pg, s);
+    if (e != hipSuccess) return C3D_ERR_HIP;
+    return hip_status(c3d::launch_bn_pool_phase2(y, part, (int64_t)parts, conv_bias, gamma, beta, eps, batch_mean,
+                                                 batch_var, pg, s));
+}
+
+int conv_maxpool_lse_relu(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+                          const c3d_conv_params* p, const float* bias, int32_t pool, float* y, void* stream) {
+    if (!x || !w || !y) return C3D_ERR_NULL;
+    if (!aligned4(x) || !aligned4(w) || !aligned4(y) || !aligned4(bias)) return C3D_ERR_ALIGN;
+    Geom g;
+    PoolGeom pg;
+    int st = resolve(x_shape, cout, p, false, &g);
+    if (st) return st;
+    st = resolve_pool(g, pool, &pg);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (g_variant.load() == 0 && c3d::conv_pool_lse_mfma_supported(pg, x, w))
+        return hip_status(c3d::launch_conv_pool_lse_mfma(x, w, bias, y, pg, s));
+    return hip_status(c3d::launch_conv_pool_lse_relu_direct(x, w, bias, y, pg, s));
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

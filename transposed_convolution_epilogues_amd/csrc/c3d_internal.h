@@ -1,0 +1,67 @@
+// c3d_internal.h - geometry block and launch declarations shared by the HIP
+// translation units of the library (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace c3d {
+
+// Resolved geometry of one convolution call (direct or transposed).
+// S = input spatial dims, O = output spatial dims (before any pooling).
+struct Geom {
+    int64_t N, Cin, Cout;
+    int64_t S[3];
+    int64_t O[3];
+    int32_t k[3], s[3], p[3], d[3];
+    int32_t groups, cin_g, cout_g;
+};
+
+// Geometry plus pooled dims for the fused epilogues.
+struct PoolGeom {
+    Geom g;
+    int32_t pool;      // window = stride
+    int64_t P[3];      // pooled dims (floor)
+    int64_t C[3];      // cells per dim = ceil(O / pool): pooled windows plus a partial tail cell
+};
+
+// ------------------------------------------------------------ generic paths
+hipError_t launch_conv3d_direct(const float* x, const float* w, const float* bias, float* y, const Geom& g,
+                                hipStream_t st);
+hipError_t launch_convT_gather(const float* x, const float* w, const float* bias, float* y, const Geom& g,
+                               hipStream_t st);
+hipError_t launch_conv_pool_lse_relu_direct(const float* x, const float* w, const float* bias, float* y,
+                                            const PoolGeom& pg, hipStream_t st);
+
+// convT_bn_avgpool: phase 1 writes pre-normalisation pooled means into y and
+// per-block (sum, sum of squares) partials in float64 into ws; phase 2 merges
+// the partials per channel and applies the affine map in place.
+size_t convT_bn_pool_partials(const PoolGeom& pg, int fast);
+hipError_t launch_convT_bn_pool_phase1_direct(const float* x, const float* w, float* y, double* ws,
+                                              const PoolGeom& pg, hipStream_t st);
+hipError_t launch_bn_pool_phase2(float* y, const double* ws, int64_t parts_per_channel, const float* conv_bias,
+                                 const float* gamma, const float* beta, float eps, float* mean_out,
+                                 float* var_out, const PoolGeom& pg, hipStream_t st);
+
+// ------------------------------------------------------------- fast paths
+// Each returns hipErrorNotSupported (without launching) when the geometry is
+// outside what the kernel handles; the caller then takes the generic path.
+bool conv3x3x3_mfma_supported(const Geom& g, const void* x, const void* w, const void* y);
+hipError_t launch_conv3x3x3_mfma(const float* x, const float* w, const float* bias, float* y, const Geom& g,
+                                 hipStream_t st);
+bool conv_pool_lse_mfma_supported(const PoolGeom& pg, const void* x, const void* w);
+hipError_t launch_conv_pool_lse_mfma(const float* x, const float* w, const float* bias, float* y,
+                                     const PoolGeom& pg, hipStream_t st);
+bool convT_s2_sublattice_supported(const Geom& g, const void* x, const void* w, const void* y);
+hipError_t launch_convT_s2_sublattice(const float* x, const float* w, const float* bias, float* y,
+                                      const Geom& g, hipStream_t st);
+bool conv_k1last_supported(const Geom& g, const void* x, const void* w, const void* y);
+hipError_t launch_conv_k1last(const float* x, const float* w, const float* bias, float* y, const Geom& g,
+                              hipStream_t st);
+bool convT_bn_pool_fast_supported(const PoolGeom& pg, const void* x);
+hipError_t launch_convT_bn_pool_phase1_fast(const float* x, const float* w, float* y, double* ws,
+                                            const PoolGeom& pg, hipStream_t st);
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace c3d
