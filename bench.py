@@ -1,0 +1,275 @@
+"""Benchmark of the fused 3D conv / transposed-conv forward path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+the four full-size workloads back to back, each through its C-ABI entry point
+(inputs resident in HBM, outputs and workspace preallocated):
+
+  c2  conv3d_fwd              Conv3d (3,3,1) kernel, depth-last x[16,3,256,256,10] -> [16,64,254,254,10]
+  c3  conv_transpose3d_fwd    ConvTranspose3d 32->64 k3 s2 p1 d2, x[16,32,16,32,32] -> [16,64,33,65,65]
+  c4  convT_bn_avgpool        ConvTranspose3d 3->16 k3 s2 p1 + BatchNorm3d (batch stats) + AvgPool3d(2) x2
+  c5  conv_maxpool_lse_relu   Conv3d 32->64 k3 p1 + MaxPool3d(2) + logsumexp(dim=1) + ReLU, x[4,32,32,128,128]
+
+value = effective TFLOP/s of the whole step = sum over workloads of 2*MAC / step time, where MAC is the
+algorithmic work: the dense GEMM count for direct convs and the valid-tap count for transposed convs.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 (MFMA and packed VALU)
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
+BENCH_KEYS = ("c2", "c3", "c4", "c5")
+# kernel that carries each workload (the roofline object names the dominant one)
+KERNELS = {
+    "c2": ("conv_k1last", "transposed_convolution_epilogues_amd/csrc/conv_k1last.hip"),
+    "c3": ("convT_s2_sublattice", "transposed_convolution_epilogues_amd/csrc/convT_sublattice.hip"),
+    "c4": ("convT_bn_pool", "transposed_convolution_epilogues_amd/csrc/convT_bn_pool.hip"),
+    "c5": ("conv_pool_lse_mfma", "transposed_convolution_epilogues_amd/csrc/conv_pool_lse.hip"),
+}
+
+
+def valid_pairs(L_in, k, s, p, d, L_out):
+    return sum(1 for i in range(L_in) for kk in range(k) if 0 <= i * s - p + kk * d < L_out)
+
+
+def work(wl, out_shape_conv):
+    """(MAC_metric, algorithmic HBM bytes) of a workload."""
+    N, cin = wl.x_shape[:2]
+    cin_g = cin // wl.groups
+    kvol = wl.kernel[0] * wl.kernel[1] * wl.kernel[2]
+    O = out_shape_conv[2:]
+    if wl.transposed:
+        mac = N * wl.cout * cin_g
+        for j in range(3):
+            mac *= valid_pairs(wl.x_shape[2 + j], wl.kernel[j], wl.stride[j], wl.pad[j], wl.dilation[j], O[j])
+    else:
+        mac = N * wl.cout * O[0] * O[1] * O[2] * cin_g * kvol
+    x_bytes = 4 * math.prod(wl.x_shape)
+    w_bytes = 4 * math.prod(wl.weight_shape)
+    return mac, x_bytes, w_bytes
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0, help="target oracle seconds per workload sample")
+    ap.add_argument("--only", default=",".join(BENCH_KEYS), help="comma-separated subset (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a design "
+              "note, not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from transposed_convolution_epilogues_amd import binding as B
+    from transposed_convolution_epilogues_amd import workloads as W
+
+    keys = [k for k in args.only.split(",") if k]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.library()
+
+    def g(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    runs = {}
+    for key in keys:
+        wl = W.CONFIGS[key]
+        inp = W.make_inputs(wl)
+        x, w, b = g(inp.x), g(inp.w), g(inp.b)
+        p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+        if wl.op == "conv3d":
+            oshape = B.conv3d_out_shape(wl.x_shape, wl.cout, p)
+            conv_shape = oshape
+            y = torch.empty(oshape, device=dev)
+            fn = (lambda x=x, w=w, b=b, y=y, wl=wl: B.conv3d_fwd(x, w, b, wl.stride, wl.pad, wl.dilation,
+                                                                 wl.groups, out=y))
+        elif wl.op == "conv_transpose3d":
+            oshape = B.conv_transpose3d_out_shape(wl.x_shape, wl.cout, p)
+            conv_shape = oshape
+            y = torch.empty(oshape, device=dev)
+            fn = (lambda x=x, w=w, b=b, y=y, wl=wl: B.conv_transpose3d_fwd(x, w, b, wl.stride, wl.pad, wl.dilation,
+                                                                           wl.output_pad, wl.groups, out=y))
+        elif wl.op == "convT_bn_avgpool":
+            conv_shape = B.conv_transpose3d_out_shape(wl.x_shape, wl.cout, p)
+            oshape = B.convT_bn_avgpool_out_shape(wl.x_shape, wl.cout, p, wl.pool)
+            y = torch.empty(oshape, device=dev)
+            ws = torch.empty(B.convT_bn_avgpool_workspace_bytes(wl.x_shape, wl.cout, p, wl.pool),
+                             dtype=torch.uint8, device=dev)
+            gm, bt = g(inp.gamma), g(inp.beta)
+            fn = (lambda x=x, w=w, b=b, y=y, wl=wl, ws=ws, gm=gm, bt=bt:
+                  B.convT_bn_avgpool(x, w, b, gm, bt, wl.eps, wl.pool, wl.stride, wl.pad, wl.dilation,
+                                     wl.output_pad, wl.groups, out=y, workspace=ws))
+        else:
+            conv_shape = B.conv3d_out_shape(wl.x_shape, wl.cout, p)
+            oshape = B.conv_maxpool_lse_relu_out_shape(wl.x_shape, wl.cout, p, wl.pool)
+            y = torch.empty(oshape, device=dev)
+            fn = (lambda x=x, w=w, b=b, y=y, wl=wl: B.conv_maxpool_lse_relu(x, w, b, wl.pool, wl.stride, wl.pad,
+                                                                            wl.dilation, wl.groups, out=y))
+        mac, xb, wb = work(wl, conv_shape)
+        runs[key] = dict(wl=wl, fn=fn, mac=mac, bytes=xb + wb + 4 * math.prod(oshape), out_shape=oshape,
+                         inp=inp, ev=[])
+        print(f"[bench] {key}: {wl.description}; out {oshape}; MAC {mac:,}", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for r in runs.values():
+            r["fn"]()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for r in runs.values():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            r["fn"]()
+            e1.record(stream)
+            r["ev"].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    per = {}
+    total_flop = 0.0
+    for key, r in runs.items():
+        ms = [e0.elapsed_time(e1) for e0, e1 in r["ev"]]
+        avg = float(np.mean(ms))
+        flop = 2.0 * r["mac"]
+        total_flop += flop
+        per[key] = dict(op=r["wl"].op, ms_avg=round(avg, 5), ms_min=round(float(np.min(ms)), 5),
+                        tflops=round(flop / (avg * 1e-3) / 1e12, 3),
+                        frac_fp32_peak=round(flop / (avg * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4),
+                        hbm_gbs=round(r["bytes"] / (avg * 1e-3) / 1e9, 1),
+                        frac_hbm_peak=round(r["bytes"] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        mac=r["mac"], algo_bytes=r["bytes"], out_shape=list(r["out_shape"]))
+    value = total_flop / (ms_per_step * 1e-3) / 1e12
+
+    # roofline object for the dominant kernel (largest average duration)
+    dom = max(per, key=lambda k: per[k]["ms_avg"])
+    kname, ksrc = KERNELS[dom]
+    bound = "mfma" if dom in ("c3", "c5") else ("hbm" if dom == "c2" else "alu")
+    if bound == "hbm":
+        achieved = per[dom]["algo_bytes"] / (per[dom]["ms_avg"] * 1e-3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = 2.0 * per[dom]["mac"] / (per[dom]["ms_avg"] * 1e-3) / 1e12
+        peak, unit = (FP32_PEAK_TFLOPS if bound == "mfma" else FP32_PEAK_TFLOPS / 2), "TFLOP/s"
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"{kname}_traffic.json")
+    if os.path.exists(tfile) and os.path.exists(os.path.join(ROOT, ksrc)):
+        with open(tfile) as f:
+            tr = json.load(f)
+        src_hash = hashlib.sha256(open(os.path.join(ROOT, ksrc), "rb").read()).hexdigest()[:16]
+        if tr.get("source_sha256_16") == src_hash:
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = dict(kernel=kname, workload=dom, bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
+                    frac=round(achieved / peak, 4), traffic=traffic)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(runs, args.cpu_seconds)
+
+    line = {
+        "metric": "effective TFLOP/s (2*MACs/time) and % of MI355X fp32 peak, per config",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded U[-1,1] inputs, PyTorch-default uniform weights)",
+        "config": {
+            "workload": "fused 3D conv suite, one pass of c2+c3+c4+c5 at full size: " +
+                        "; ".join(f"{k}: {runs[k]['wl'].description}" for k in runs),
+            "per_config": per,
+            "frac_fp32_peak_step": round(value / FP32_PEAK_TFLOPS, 4),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(runs, seconds_per_workload):
+    """The CPU oracle, timed on a bounded sample of each workload and scaled to the
+    whole workload; reported in the same effective TFLOP/s as the GPU value."""
+    import oracle as O
+
+    rng = np.random.default_rng(0)
+    total_flop = 0.0
+    total_s = 0.0
+    parts = []
+    for key, r in runs.items():
+        wl, inp = r["wl"], r["inp"]
+        kw = dict(stride=wl.stride, pad=wl.pad, dilation=wl.dilation, groups=wl.groups)
+        full_units = math.prod(r["out_shape"])
+        if wl.op == "convT_bn_avgpool":
+            # the module needs whole-batch statistics: sample = a leading sub-batch
+            nb = 1
+            while True:
+                sub = wl.with_(x_shape=(nb,) + wl.x_shape[1:])
+                t0 = time.perf_counter()
+                O.convT_bn_avgpool(np.ascontiguousarray(inp.x[:nb]), inp.w, inp.b, inp.gamma, inp.beta, wl.eps,
+                                   wl.pool, **dict(kw, output_pad=wl.output_pad))
+                dt = time.perf_counter() - t0
+                if dt > seconds_per_workload / 4 or nb >= wl.x_shape[0]:
+                    break
+                nb *= 2
+            frac = nb / wl.x_shape[0]
+            desc = f"{key}: batch {nb} of {wl.x_shape[0]}"
+        else:
+            n = 256
+            while True:
+                flat = rng.integers(0, full_units, n)
+                t0 = time.perf_counter()
+                if wl.op == "conv3d":
+                    O.conv3d_at(inp.x, inp.w, flat, inp.b, **kw)
+                elif wl.op == "conv_transpose3d":
+                    O.conv_transpose3d_at(inp.x, inp.w, flat, inp.b, output_pad=wl.output_pad, **kw)
+                else:
+                    O.conv_maxpool_lse_relu_at(inp.x, inp.w, inp.b, flat, wl.pool, **kw)
+                dt = time.perf_counter() - t0
+                if dt > seconds_per_workload / 4 or n >= full_units:
+                    break
+                n *= 4
+            frac = n / full_units
+            desc = f"{key}: {n} random outputs of {full_units}"
+        t_full = dt / frac
+        total_s += t_full
+        total_flop += 2.0 * r["mac"]
+        parts.append(f"{desc} in {dt:.2f}s")
+        print(f"[bench] cpu oracle {desc}: {dt:.2f}s -> {t_full:.1f}s for the whole workload", file=sys.stderr,
+              flush=True)
+    return {"value": round(total_flop / total_s / 1e12, 6), "unit": "TFLOP/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": "plain-loop float64 oracle timed on bounded samples, scaled to the whole step: " +
+                      "; ".join(parts)}
+
+
+if __name__ == "__main__":
+    main()

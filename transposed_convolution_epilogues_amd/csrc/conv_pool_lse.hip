@@ -1,0 +1,111 @@
+// conv_pool_lse.hip - Conv3d(k3, s1, d1) -> MaxPool3d(2) -> logsumexp over
+// channels -> ReLU in one kernel ("Kimi-K2.6 l2_p43": the module, and its plan
+// to compute the conv tile by tile and reduce it to the pooled logsumexp in
+// the epilogue instead of writing the conv output).
+//
+// The conv runs on the MFMA engine in conv333_mfma.h.  Epilogue per wave:
+//   - 2x2x2 max pool: each lane already holds whole windows (8 registers of an
+//     accumulator tile), so the max is lane-local; the bias is added after the
+//     max (max(v) + b = max(v + b)).
+//   - logsumexp over the 64 channels: a channel lives in lane%32 of one of two
+//     N tiles, so each lane first combines its two channels, then the max and
+//     the shifted sum are reduced across the 32 lanes of its half; the running
+//     maximum starts from real values, never from -inf ("Kimi-K2.6 l2_p43",
+//     the streaming-logsumexp initialisation caveat).
+//   - ReLU and one 4-byte store per pooled voxel.
+// The 4 x 64 x 32 x 128 x 128 conv output is never written to memory.
+#include "conv333_mfma.h"
+
+namespace c3d {
+namespace {
+
+using namespace mfma333;
+
+__global__ __launch_bounds__(kThreads) void conv_pool_lse_mfma_kernel(Args a) {
+    __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
+    const Tile t = tile_of(a);
+    f32x16 acc[2][2];
+    mainloop<kConvWeights>(a, t, lds, acc);
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int h = lane >> 5;
+    const int64_t j0 = t.d0 >> 1;
+    const int64_t j1 = (t.h0 >> 1) + (wv >> 1);
+    float bias_v[2];
+    bool valid[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int64_t oc = t.oc0 + nt * 32 + (lane & 31);
+        valid[nt] = oc < a.Cout;
+        bias_v[nt] = (a.bias && valid[nt]) ? a.bias[oc] : 0.f;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            float m[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                float v = acc[mt][nt][2 * w];
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    v = fmaxf(v, acc[mt][nt][a4 * 4 + 2 * w]);
+                    v = fmaxf(v, acc[mt][nt][a4 * 4 + 2 * w + 1]);
+                }
+                m[nt] = valid[nt] ? v + bias_v[nt] : -FLT_MAX;
+            }
+            float M = fmaxf(m[0], m[1]);
+#pragma unroll
+            for (int off = 16; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+            float S = expf(m[0] - M) + expf(m[1] - M);
+#pragma unroll
+            for (int off = 16; off > 0; off >>= 1) S += __shfl_xor(S, off, 64);
+            const float L = M + logf(S);
+            if ((lane & 31) == 0) {
+                const int64_t j2 = (t.w0 >> 1) + (wv & 1) * 8 + 4 * mt + 2 * h + w;
+                if (j0 < a.P[0] && j1 < a.P[1] && j2 < a.P[2])
+                    a.y[((t.n * a.P[0] + j0) * a.P[1] + j1) * a.P[2] + j2] = L > 0.f ? L : 0.f;
+            }
+        }
+}
+
+}  // namespace
+
+bool conv_pool_lse_mfma_supported(const PoolGeom& pg, const void*, const void*) {
+    const Geom& g = pg.g;
+    for (int j = 0; j < 3; ++j)
+        if (g.k[j] != 3 || g.s[j] != 1 || g.d[j] != 1 || g.p[j] != g.p[0]) return false;
+    return g.groups == 1 && g.Cout <= OCB && pg.pool == 2 && mfma333::fits_int32_tiles(g.O[0]) &&
+           mfma333::fits_int32_tiles(g.O[1]) && mfma333::fits_int32_tiles(g.O[2]);
+}
+
+hipError_t launch_conv_pool_lse_mfma(const float* x, const float* w, const float* bias, float* y,
+                                     const PoolGeom& pg, hipStream_t st) {
+    const Geom& g = pg.g;
+    Args a{};
+    a.x = x;
+    a.w = w;
+    a.bias = bias;
+    a.y = y;
+    a.N = g.N;
+    a.Cin = g.Cin;
+    a.Cout = g.Cout;
+    for (int j = 0; j < 3; ++j) {
+        a.S[j] = g.S[j];
+        a.O[j] = g.O[j];
+        a.P[j] = pg.P[j];
+    }
+    a.pad = g.p[0];
+    // only tiles holding at least one complete pooling window are needed
+    a.tiles[0] = (int32_t)ceil_div(2 * pg.P[0], TD);
+    a.tiles[1] = (int32_t)ceil_div(2 * pg.P[1], TH);
+    a.tiles[2] = (int32_t)ceil_div(2 * pg.P[2], TW);
+    a.oc_blocks = 1;
+    const int64_t blocks = g.N * a.tiles[0] * a.tiles[1] * a.tiles[2];
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(conv_pool_lse_mfma_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace c3d

@@ -7,11 +7,6 @@ bool conv3x3x3_mfma_supported(const Geom&, const void*, const void*, const void*
 hipError_t launch_conv3x3x3_mfma(const float*, const float*, const float*, float*, const Geom&, hipStream_t) {
     return hipErrorNotSupported;
 }
-bool conv_pool_lse_mfma_supported(const PoolGeom&, const void*, const void*) { return false; }
-hipError_t launch_conv_pool_lse_mfma(const float*, const float*, const float*, float*, const PoolGeom&,
-                                     hipStream_t) {
-    return hipErrorNotSupported;
-}
 bool convT_s2_sublattice_supported(const Geom&, const void*, const void*, const void*) { return false; }
 hipError_t launch_convT_s2_sublattice(const float*, const float*, const float*, float*, const Geom&, hipStream_t) {
     return hipErrorNotSupported;
