@@ -137,6 +137,14 @@ MEDIUM = {
     "convT_bn_pool_exact": W.CONFIGS["c4"].with_(x_shape=(2, 3, 16, 16, 16)),
     "conv_pool_lse": W.CONFIGS["c5"].with_(x_shape=(1, 32, 6, 18, 70)),
     "conv_pool_lse_odd": W.CONFIGS["c5"].with_(x_shape=(2, 32, 5, 9, 35), cout=64),
+    "conv_pool_lse_cout40_pad0": W.CONFIGS["c5"].with_(x_shape=(1, 16, 6, 10, 12), cout=40, pad=0),
+    "conv3d_k333_cout72_pad0": W.CONFIGS["c1"].with_(x_shape=(1, 8, 4, 6, 9), cout=72, pad=0),
+    "conv3d_k333_pad2": W.CONFIGS["c1"].with_(x_shape=(1, 9, 3, 5, 33), cout=16, pad=2),
+    "convT_s2p1d2_cout80": W.CONFIGS["c3"].with_(x_shape=(1, 8, 3, 5, 6), cout=80),
+    "convT_s2p1d2_bias": W.CONFIGS["c3"].with_(x_shape=(2, 5, 3, 4, 33), cout=16, bias=True),
+    "conv3d_k331_bias_dil": W.CONFIGS["c2"].with_(x_shape=(1, 2, 9, 12, 5), cout=20, dilation=(2, 2, 1),
+                                                  bias=True),
+    "convT_bn_pool_cin1_cout5": W.CONFIGS["c4"].with_(x_shape=(2, 1, 6, 9, 8), cout=5),
 }
 
 
