@@ -12,10 +12,13 @@
 //                voxels x 64 output channels
 //   wave       = 2 (D) x 2 (H) x 16 (W) voxels x 64 channels = 2 x 2 MFMA tiles
 //                of 32 x 32 (M = voxels, N = channels), 64 accumulator VGPRs
-//   M tile     = 2 (D) x 2 (H) x 8 (W) voxels: row r = 8a + 4h + b holds
-//                x = 4h + b, y = a % 2, z = a / 2.  In the MFMA result a lane
-//                holds rows {8a + 4*(lane/32) + b}, i.e. two complete 2x2x2
-//                windows per tile, so a 2x2x2 max pool is lane-local.
+//   M tile     = 1 (D) x 2 (H) x 16 (W) voxels: row r holds x = r % 16,
+//                y = r / 16, and the wave's two M tiles are the two D planes.
+//                A-operand lanes 0-15 then read 16 consecutive voxels (256
+//                contiguous bytes of LDS, no bank conflict).  In the MFMA result
+//                a lane holds rows {8a + 4*(lane/32) + b}: x = 8(a%2) + 4h + b,
+//                y = a/2, in both M tiles, i.e. four complete 2x2x2 windows, so
+//                a 2x2x2 max pool is lane-local.
 //   K loop     = input-channel chunks of 8; per chunk the input halo
 //                (TD+2)(TH+2)(TW+2) x 8 and the weights 27 x 8 x 64 are staged
 //                in LDS; per tap a lane fetches 4 K-steps of its A operand
@@ -24,7 +27,7 @@
 //                16-byte LDS read each.
 //   K order    = within a chunk, K-step s and lane half h use channel
 //                4h + s; A and B agree on it, so the contraction is exact.
-// LDS: 26,112 B input + 55,296 B weights = 81,408 B -> two workgroups per CU.
+// LDS: 26,112 B input + 55,728 B weights = 81,840 B -> two workgroups per CU.
 #pragma once
 
 #include <float.h>
@@ -45,7 +48,9 @@ constexpr int HPOS = HD * HH * HW;               // 816 halo positions
 constexpr int ICC = 8;                            // input channels per chunk
 constexpr int OCB = 64;                           // output channels per workgroup
 constexpr int LDS_X = 2 * HPOS * 4;               // floats, layout [g][pos][4]
-constexpr int LDS_W = 27 * 2 * 2 * 32 * 4;        // floats, layout [tap][nt][h][n][s]
+constexpr int WTAP = 2 * 2 * 32 * 4 + 4;          // floats per tap, padded: staging writes
+                                                  // of consecutive taps fall on distinct banks
+constexpr int LDS_W = 27 * WTAP;                  // floats, layout [tap][nt][h][n][s]
 constexpr int LDS_FLOATS = LDS_X + LDS_W;
 
 // How the B operand (weights) is read from global memory.
@@ -98,53 +103,84 @@ __device__ __forceinline__ Tile tile_of(const Args& a) {
 }
 
 // Input halo chunk -> LDS [g][pos][4], channel ic0 + 4g + j at float j.
+// Loads are unconditional (out-of-range elements read a clamped, valid address
+// and are replaced by 0 with a select) and issued in batches, so a thread has
+// many loads in flight before its first LDS write.
 __device__ __forceinline__ void stage_x(const Args& a, const Tile& t, int64_t ic0, float* lx) {
+    constexpr int kItems = 2 * HPOS;
+    constexpr int kIters = (kItems + kThreads - 1) / kThreads;  // 7
     const int64_t plane = a.S[0] * a.S[1] * a.S[2];
     const float* xn = a.x + (t.n * a.Cin) * plane;
-    for (int it = threadIdx.x; it < 2 * HPOS; it += kThreads) {
+    f32x4 v[kIters];
+#pragma unroll
+    for (int q = 0; q < kIters; ++q) {
+        const int it = threadIdx.x + q * kThreads;
         const int g = it / HPOS;
         const int pos = it - g * HPOS;
         const int pw = pos % HW;
         const int ph = (pos / HW) % HH;
         const int pd = pos / (HW * HH);
         const int64_t gd = t.d0 - a.pad + pd, gh = t.h0 - a.pad + ph, gw = t.w0 - a.pad + pw;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (gd >= 0 && gd < a.S[0] && gh >= 0 && gh < a.S[1] && gw >= 0 && gw < a.S[2]) {
-            const int64_t off = (gd * a.S[1] + gh) * a.S[2] + gw;
-            const int64_t ic = ic0 + 4 * g;
+        const bool inb = it < kItems && gd >= 0 && gd < a.S[0] && gh >= 0 && gh < a.S[1] && gw >= 0 &&
+                         gw < a.S[2];
+        const int64_t off = inb ? (gd * a.S[1] + gh) * a.S[2] + gw : 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (ic + j < a.Cin) v[j] = xn[(ic + j) * plane + off];
+        for (int j = 0; j < 4; ++j) {
+            const int64_t ic = ic0 + 4 * g + j;
+            const bool ok = inb && ic < a.Cin;
+            const float e = xn[ok ? ic * plane + off : 0];
+            v[q][j] = ok ? e : 0.f;
         }
-        *reinterpret_cast<f32x4*>(lx + (g * HPOS + pos) * 4) = v;
+    }
+#pragma unroll
+    for (int q = 0; q < kIters; ++q) {
+        const int it = threadIdx.x + q * kThreads;
+        if (q < kIters - 1 || it < kItems) *reinterpret_cast<f32x4*>(lx + it * 4) = v[q];
     }
 }
 
 // Weight chunk -> LDS [tap][nt][h][n][s] with oc = oc0 + 32nt + n and
-// ic = ic0 + 4h + s.  Global reads follow the memory order of w.
+// ic = ic0 + 4h + s.  Global reads follow the memory order of w; like
+// stage_x, loads are unconditional and batched.
 template <int kMode>
 __device__ __forceinline__ void stage_w(const Args& a, const Tile& t, int64_t ic0, float* lw) {
-    for (int e = threadIdx.x; e < 27 * ICC * OCB; e += kThreads) {
-        int oc, j, tap;
-        float v = 0.f;
-        if (kMode == kConvWeights) {
-            oc = e / (ICC * 27);
-            const int rem = e - oc * (ICC * 27);
-            j = rem / 27;
-            tap = rem - j * 27;
-            const int64_t goc = t.oc0 + oc, gic = ic0 + j;
-            if (goc < a.Cout && gic < a.Cin) v = a.w[(goc * a.Cin + gic) * 27 + tap];
-        } else {
-            j = e / (OCB * 27);
-            const int rem = e - j * (OCB * 27);
-            oc = rem / 27;
-            const int tt = rem - oc * 27;
-            tap = 26 - tt;
-            const int64_t goc = t.oc0 + oc, gic = ic0 + j;
-            if (goc < a.Cout && gic < a.Cin) v = a.w[(gic * a.Cout + goc) * 27 + tt];
+    constexpr int kItems = 27 * ICC * OCB;       // 13824 = 54 per thread
+    constexpr int kBatch = 9;
+    static_assert(kItems % (kThreads * kBatch) == 0, "weight staging batches");
+    for (int q0 = 0; q0 < kItems / kThreads; q0 += kBatch) {
+        float v[kBatch];
+        int dst[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int e = threadIdx.x + (q0 + q) * kThreads;
+            int oc, j, tap;
+            int64_t src;
+            bool ok;
+            if (kMode == kConvWeights) {
+                oc = e / (ICC * 27);
+                const int rem = e - oc * (ICC * 27);
+                j = rem / 27;
+                tap = rem - j * 27;
+                const int64_t goc = t.oc0 + oc, gic = ic0 + j;
+                ok = goc < a.Cout && gic < a.Cin;
+                src = (goc * a.Cin + gic) * 27 + tap;
+            } else {
+                j = e / (OCB * 27);
+                const int rem = e - j * (OCB * 27);
+                oc = rem / 27;
+                const int tt = rem - oc * 27;
+                tap = 26 - tt;
+                const int64_t goc = t.oc0 + oc, gic = ic0 + j;
+                ok = goc < a.Cout && gic < a.Cin;
+                src = (gic * a.Cout + goc) * 27 + tt;
+            }
+            const float e2 = a.w[ok ? src : 0];
+            v[q] = ok ? e2 : 0.f;
+            const int nt = oc >> 5, n = oc & 31, h = j >> 2, s = j & 3;
+            dst[q] = tap * WTAP + ((nt * 2 + h) * 32 + n) * 4 + s;
         }
-        const int nt = oc >> 5, n = oc & 31, h = j >> 2, s = j & 3;
-        lw[(((tap * 2 + nt) * 2 + h) * 32 + n) * 4 + s] = v;
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) lw[dst[q]] = v[q];
     }
 }
 
@@ -162,7 +198,7 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
     int abase[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        const int x = (r & 7) + 8 * mt + wx, y = ((r >> 3) & 1) + wy, z = r >> 4;
+        const int x = (r & 15) + wx, y = (r >> 4) + wy, z = mt;
         abase[mt] = (h * HPOS + (z * HH + y) * HW + x) * 4;
     }
     const int bbase = (h * 32 + r) * 4;
@@ -192,7 +228,7 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
                     for (int mt = 0; mt < 2; ++mt) av[mt] = *reinterpret_cast<const f32x4*>(lx + abase[mt] + xoff);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
-                        bv[nt] = *reinterpret_cast<const f32x4*>(lw + bbase + (tap * 2 + nt) * 256);
+                        bv[nt] = *reinterpret_cast<const f32x4*>(lw + bbase + tap * WTAP + nt * 256);
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -209,9 +245,9 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
 // (the MFMA result layout: row = 8*(i/4) + 4*(lane/32) + i%4).
 __device__ __forceinline__ void acc_voxel(int lane, int wv, int mt, int i, int& x, int& y, int& z) {
     const int a = i >> 2, b = i & 3, h = lane >> 5;
-    x = 4 * h + b + 8 * mt + (wv & 1) * 16;
-    y = (a & 1) + (wv >> 1) * 2;
-    z = a >> 1;
+    x = 8 * (a & 1) + 4 * h + b + (wv & 1) * 16;
+    y = (a >> 1) + (wv >> 1) * 2;
+    z = mt;
 }
 
 inline bool fits_int32_tiles(int64_t v) { return v > 0 && v < (1ll << 30); }

@@ -4,9 +4,9 @@
 // the epilogue instead of writing the conv output).
 //
 // The conv runs on the MFMA engine in conv333_mfma.h.  Epilogue per wave:
-//   - 2x2x2 max pool: each lane already holds whole windows (8 registers of an
-//     accumulator tile), so the max is lane-local; the bias is added after the
-//     max (max(v) + b = max(v + b)).
+//   - 2x2x2 max pool: each lane already holds whole windows (4 registers in
+//     each of the two M tiles), so the max is lane-local; the bias is added
+//     after the max (max(v) + b = max(v + b)).
 //   - logsumexp over the 64 channels: a channel lives in lane%32 of one of two
 //     N tiles, so each lane first combines its two channels, then the max and
 //     the shifted sum are reduced across the 32 lanes of its half; the running
@@ -40,34 +40,36 @@ __global__ __launch_bounds__(kThreads) void conv_pool_lse_mfma_kernel(Args a) {
         valid[nt] = oc < a.Cout;
         bias_v[nt] = (a.bias && valid[nt]) ? a.bias[oc] : 0.f;
     }
+    // window q = 2*(a%2) + b/2 holds registers {a%2 + 2*ay, ...}: x = 8(a%2) + 4h + b,
+    // y = a/2 in {0,1}, z = mt in {0,1}; see acc_voxel in conv333_mfma.h
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int q = 0; q < 4; ++q) {
+        const int ax = q >> 1, bx = (q & 1) * 2;
+        float m[2];
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            float m[2];
+        for (int nt = 0; nt < 2; ++nt) {
+            float v = -FLT_MAX;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                float v = acc[mt][nt][2 * w];
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    v = fmaxf(v, acc[mt][nt][a4 * 4 + 2 * w]);
-                    v = fmaxf(v, acc[mt][nt][a4 * 4 + 2 * w + 1]);
-                }
-                m[nt] = valid[nt] ? v + bias_v[nt] : -FLT_MAX;
-            }
-            float M = fmaxf(m[0], m[1]);
+                for (int ay = 0; ay < 2; ++ay)
 #pragma unroll
-            for (int off = 16; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-            float S = expf(m[0] - M) + expf(m[1] - M);
-#pragma unroll
-            for (int off = 16; off > 0; off >>= 1) S += __shfl_xor(S, off, 64);
-            const float L = M + logf(S);
-            if ((lane & 31) == 0) {
-                const int64_t j2 = (t.w0 >> 1) + (wv & 1) * 8 + 4 * mt + 2 * h + w;
-                if (j0 < a.P[0] && j1 < a.P[1] && j2 < a.P[2])
-                    a.y[((t.n * a.P[0] + j0) * a.P[1] + j1) * a.P[2] + j2] = L > 0.f ? L : 0.f;
-            }
+                    for (int u = 0; u < 2; ++u) v = fmaxf(v, acc[mt][nt][(2 * ay + ax) * 4 + bx + u]);
+            m[nt] = valid[nt] ? v + bias_v[nt] : -FLT_MAX;
         }
+        float M = fmaxf(m[0], m[1]);
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+        float S = expf(m[0] - M) + expf(m[1] - M);
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) S += __shfl_xor(S, off, 64);
+        const float L = M + logf(S);
+        if ((lane & 31) == 0) {
+            const int64_t j2 = (t.w0 >> 1) + (wv & 1) * 8 + 4 * ax + 2 * h + (q & 1);
+            if (j0 < a.P[0] && j1 < a.P[1] && j2 < a.P[2])
+                a.y[((t.n * a.P[0] + j0) * a.P[1] + j1) * a.P[2] + j2] = L > 0.f ? L : 0.f;
+        }
+    }
 }
 
 }  // namespace
