@@ -135,7 +135,7 @@ __device__ __forceinline__ void stage_x(const Args& a, const Tile& t, int64_t ic
 #pragma unroll
     for (int q = 0; q < kIters; ++q) {
         const int it = threadIdx.x + q * kThreads;
-        if (q < kIters - 1 || it < kItems) *reinterpret_cast<f32x4*>(lx + it * 4) = v[q];
+        if (it < kItems) *reinterpret_cast<f32x4*>(lx + it * 4) = v[q];
     }
 }
 

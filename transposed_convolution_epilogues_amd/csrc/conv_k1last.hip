@@ -14,7 +14,8 @@
 // v_mfma_f32_32x32x2f32 the rows are output channels (the weights stay in
 // VGPRs for the whole kernel) and the columns are output positions.  One wave
 // owns one output row of 64 channels and walks it in blocks of 128 positions
-// (four N tiles).  The work is bound by the 2.6 GB of output stores, so the
+// (four N tiles); the four waves of a workgroup own four consecutive rows and
+// share the input they read through LDS.  The work is bound by the 2.6 GB of output stores, so the
 // column-to-position map is chosen for the store shape (see load_block); the
 // MFMA work runs underneath the stores.
 #include "c3d_internal.h"
@@ -26,6 +27,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int kMaxSteps = 16;  // K <= 32
+constexpr int kChunk = 512;    // output positions per workgroup (4 blocks of 128)
+constexpr int kMaxE = 12288;   // staged floats per workgroup (48 KB of LDS)
 
 struct K1Args {
     const float* x;
@@ -37,11 +40,10 @@ struct K1Args {
     int64_t O0, J;      // output rows and row length (O1*S2)
     int32_t K, k0n, k1n, d0, d1S2;
     int32_t ocb;        // blocks of 64 output channels
+    int32_t R, RL, E;   // staged input rows per workgroup, staged row length, staged floats
+    int32_t groups;     // row groups per (n, ocb): ceil(O0 / 4)
+    int32_t chunks;     // position chunks per row: ceil(J / kChunk)
 };
-
-__device__ __forceinline__ float ld(const float* base, uint32_t idx) {
-    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + (size_t)(idx * 4u));
-}
 
 // Block of 128 output positions.  N tile t's column c is position j0 + 4c + t,
 // so after the MFMAs a lane holds 4 consecutive positions of each of its 16
@@ -49,18 +51,6 @@ __device__ __forceinline__ float ld(const float* base, uint32_t idx) {
 // 0-31 then write 512 contiguous bytes of one channel row and lanes 32-63 of
 // another.  Measured on MI355X this store shape runs at ~6.3 TB/s, against
 // ~2.2 TB/s for one 4-byte column per lane.
-template <int kSteps>
-__device__ __forceinline__ void load_block(const float* xb, const uint32_t (&off)[kSteps], int64_t j0, int r,
-                                           int64_t J, float (&bx)[4][kSteps]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        int64_t j = j0 + 4 * r + t;
-        j = j < J ? j : J - 1;  // positions past the row end are computed but never stored
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) bx[t][s] = ld(xb, off[s] + (uint32_t)j);
-    }
-}
-
 template <bool kBias, bool kVec, bool kFull>
 __device__ __forceinline__ void store_block(float* yb, uint32_t ystride, const f32x16 (&acc)[2][4],
                                             const float (&brow)[2][16], int64_t j0, int r, int h, int64_t J,
@@ -87,25 +77,66 @@ __device__ __forceinline__ void store_block(float* yb, uint32_t ystride, const f
         }
 }
 
+// A workgroup owns 4 consecutive output rows (one per wave) and a chunk of
+// kChunk positions of them.  Everything it reads - R = 4 + (k0-1)d0 rows of
+// every input channel, RL = kChunk + (k1-1)d1*S2 positions each - is staged in
+// LDS once, before its first output store.  The loop over the chunk's blocks
+// then issues no global load: on this GPU loads and stores share one in-order
+// counter, so a load waited for after stores would also wait for those stores
+// to reach memory, and a wave that must drain its stores every block cannot
+// keep the HBM write queue full.  Box elements past the end of an input row or
+// below the last input row feed only outputs that are never stored, so their
+// loads are merely clamped into the image.
+__device__ __forceinline__ void stage(const K1Args& a, const float* xi, int64_t o0b, int64_t jc0, float* lds) {
+    constexpr int kBatch = 16;
+    const int32_t last = (int32_t)(a.Cin * a.S0 * a.S1S2 - 1);  // last element of this image
+    for (int e0 = 0; e0 < a.E; e0 += kBatch * kThreads) {
+        float v[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int e = e0 + q * kThreads + threadIdx.x;
+            const int ic = e / (a.R * a.RL);
+            const int rem = e - ic * (a.R * a.RL);
+            const int row = rem / a.RL;
+            const int col = rem - row * a.RL;
+            const int64_t g = (ic * a.S0 + o0b + row) * a.S1S2 + jc0 + col;
+            v[q] = xi[g < last ? g : last];
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int e = e0 + q * kThreads + threadIdx.x;
+            if (e < a.E) lds[e] = v[q];
+        }
+    }
+}
+
 template <int kSteps, bool kBias, bool kVec>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv_k1last_kernel(
     K1Args a) {
+    extern __shared__ float lds[];  // E floats
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, r = lane & 31;
-    // the wave index is uniform across the wave: keep the row bases in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + wave;
-    const int64_t rows = a.N * a.ocb * a.O0;
-    if (row >= rows) return;
-    const int64_t o0 = row % a.O0;
-    const int64_t ocb = (row / a.O0) % a.ocb;
-    const int64_t n = row / (a.O0 * a.ocb);
+    int64_t b = blockIdx.x;
+    const int64_t chunk = b % a.chunks;
+    b /= a.chunks;
+    const int64_t grp = b % a.groups;
+    b /= a.groups;
+    const int64_t ocb = b % a.ocb;
+    const int64_t n = b / a.ocb;
+    const int64_t o0b = 4 * grp;            // first output row of this workgroup
+    const int64_t o0 = o0b + wave;          // this wave's output row
+    const int64_t jc0 = chunk * kChunk;     // first position of this workgroup
+    const float* xi = a.x + n * a.Cin * a.S0 * a.S1S2;
+    stage(a, xi, o0b, jc0, lds);
+    __syncthreads();
+    if (o0 >= a.O0) return;  // uniform per wave; no barrier follows
 
-    // A operand (weights), kept for the whole row: lane holds W[oc][k] with
-    // oc = 64*ocb + 32*mt + r and k = 2s + h.  Padding rows k >= K get a zero
-    // weight and read a valid input element, so no load is predicated.
+    // A operand (weights): lane holds W[oc][k] with oc = 64*ocb + 32*mt + r and
+    // k = 2s + h.  Padding rows k >= K get a zero weight and read a valid
+    // staged element.
     float wa[2][kSteps];
-    uint32_t off[kSteps];
+    int loff[kSteps];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         const int k = 2 * s + h;
@@ -114,7 +145,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int k1 = kk % a.k1n;
         const int k0 = (kk / a.k1n) % a.k0n;
         const int ic = kk / (a.k1n * a.k0n);
-        off[s] = (uint32_t)((ic * a.S0 + k0 * a.d0) * a.S1S2 + k1 * a.d1S2);
+        loff[s] = (ic * a.R + wave + k0 * a.d0) * a.RL + k1 * a.d1S2 + 4 * r;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int64_t oc = 64 * ocb + 32 * mt + r;
@@ -131,14 +162,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             brow[mt][i] = (kBias && oc < a.Cout) ? a.bias[oc] : 0.f;
         }
     const bool all_oc = 64 * (ocb + 1) <= a.Cout;
-
-    const float* xb = a.x + (n * a.Cin * a.S0 + o0) * a.S1S2;
     float* yb = a.y + ((n * a.Cout + 64 * ocb) * a.O0 + o0) * a.J;
     const uint32_t ystride = (uint32_t)(a.O0 * a.J);  // between output channels
 
-    for (int64_t j0 = 0; j0 < a.J; j0 += 128) {
-        float bx[4][kSteps];
-        load_block<kSteps>(xb, off, j0, r, a.J, bx);
+    for (int jb = 0; jb < kChunk; jb += 128) {
+        const int64_t j0 = jc0 + jb;
+        if (j0 >= a.J) break;
         f32x16 acc[2][4];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -147,12 +176,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[mt][t][i] = 0.f;
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s)
+        for (int s = 0; s < kSteps; ++s) {
+            float bx[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) bx[t] = lds[loff[s] + jb + t];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(wa[mt][s], bx[t][s], acc[mt][t], 0, 0, 0);
+                    acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(wa[mt][s], bx[t], acc[mt][t], 0, 0, 0);
+        }
         if (all_oc && j0 + 128 <= a.J)
             store_block<kBias, kVec, true>(yb, ystride, acc, brow, j0, r, h, a.J, 0, 0);
         else
@@ -167,10 +200,13 @@ bool conv_k1last_supported(const Geom& g, const void*, const void*, const void*)
     for (int j = 0; j < 3; ++j)
         if (g.s[j] != 1 || g.p[j] != 0) return false;
     const int64_t K = g.Cin * g.k[0] * g.k[1];
-    // MFMA pays off with many output channels; K must fit the VGPR-resident weights
-    // 32-bit element offsets: within one image's input, and within 64 output channels
-    return K >= 2 && K <= 2 * kMaxSteps && g.Cout >= 16 && g.Cin * g.S[0] * g.S[1] * g.S[2] < (1ll << 30) &&
-           64 * g.O[0] * g.O[1] * g.S[2] < (1ll << 30);
+    const int64_t R = 4 + (int64_t)(g.k[0] - 1) * g.d[0];
+    const int64_t RL = kChunk + (int64_t)(g.k[1] - 1) * g.d[1] * g.S[2];
+    const int64_t E = g.Cin * R * RL;
+    // MFMA pays off with many output channels; K must fit the VGPR-resident
+    // weights, the staged box the LDS, and offsets 32 bits
+    return K >= 2 && K <= 2 * kMaxSteps && g.Cout >= 16 && E <= kMaxE &&
+           g.Cin * g.S[0] * g.S[1] * g.S[2] < (1ll << 30) && 64 * g.O[0] * g.O[1] * g.S[2] < (1ll << 30);
 }
 
 hipError_t launch_conv_k1last(const float* x, const float* w, const float* bias, float* y, const Geom& g,
@@ -193,21 +229,26 @@ hipError_t launch_conv_k1last(const float* x, const float* w, const float* bias,
     a.d0 = g.d[0];
     a.d1S2 = (int32_t)(g.d[1] * g.S[2]);
     a.ocb = (int32_t)ceil_div(g.Cout, 64);
-    const int64_t rows = g.N * a.ocb * g.O[0];
-    const int64_t blocks = ceil_div(rows, kThreads / 64);
+    a.R = 4 + (g.k[0] - 1) * g.d[0];
+    a.RL = kChunk + (g.k[1] - 1) * a.d1S2;
+    a.E = (int32_t)(g.Cin * a.R * a.RL);
+    a.groups = (int32_t)ceil_div(g.O[0], 4);
+    a.chunks = (int32_t)ceil_div(a.J, kChunk);
+    const int64_t blocks = g.N * a.ocb * (int64_t)a.groups * a.chunks;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const int steps = (a.K + 1) / 2;
     const bool vec = (a.J % 4 == 0) && ((uintptr_t)y % 16 == 0);
+    const size_t lds_bytes = (size_t)a.E * sizeof(float);
     const dim3 grid((unsigned)blocks), block(kThreads);
-#define C3D_K1_LAUNCH(S)                                                                               \
-    do {                                                                                               \
-        if (bias) {                                                                                    \
-            if (vec) hipLaunchKernelGGL((conv_k1last_kernel<S, true, true>), grid, block, 0, st, a);  \
-            else hipLaunchKernelGGL((conv_k1last_kernel<S, true, false>), grid, block, 0, st, a);     \
-        } else {                                                                                       \
-            if (vec) hipLaunchKernelGGL((conv_k1last_kernel<S, false, true>), grid, block, 0, st, a); \
-            else hipLaunchKernelGGL((conv_k1last_kernel<S, false, false>), grid, block, 0, st, a);    \
-        }                                                                                              \
+#define C3D_K1_LAUNCH(S)                                                                                 \
+    do {                                                                                                 \
+        if (bias) {                                                                                      \
+            if (vec) hipLaunchKernelGGL((conv_k1last_kernel<S, true, true>), grid, block, lds_bytes, st, a);  \
+            else hipLaunchKernelGGL((conv_k1last_kernel<S, true, false>), grid, block, lds_bytes, st, a);     \
+        } else {                                                                                         \
+            if (vec) hipLaunchKernelGGL((conv_k1last_kernel<S, false, true>), grid, block, lds_bytes, st, a); \
+            else hipLaunchKernelGGL((conv_k1last_kernel<S, false, false>), grid, block, lds_bytes, st, a);    \
+        }                                                                                                \
     } while (0)
     if (steps <= 8) C3D_K1_LAUNCH(8);
     else if (steps <= 14) C3D_K1_LAUNCH(14);
