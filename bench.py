@@ -34,12 +34,23 @@ FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 (MFMA and packed VALU)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 BENCH_KEYS = ("c2", "c3", "c4", "c5")
 # kernel that carries each workload (the roofline object names the dominant one)
+CSRC = "transposed_convolution_epilogues_amd/csrc/"
 KERNELS = {
-    "c2": ("conv_k1last", "transposed_convolution_epilogues_amd/csrc/conv_k1last.hip"),
-    "c3": ("convT_s2_sublattice", "transposed_convolution_epilogues_amd/csrc/convT_sublattice.hip"),
-    "c4": ("convT_bn_pool", "transposed_convolution_epilogues_amd/csrc/convT_bn_pool.hip"),
-    "c5": ("conv_pool_lse_mfma", "transposed_convolution_epilogues_amd/csrc/conv_pool_lse.hip"),
+    "c2": ("conv_k1last_kernel", [CSRC + "conv_k1last.hip"]),
+    "c3": ("conv333_store_kernel", [CSRC + "convT_sublattice.hip", CSRC + "conv333_mfma.h"]),
+    "c4": ("convT_bn_pool_phase1_kernel", [CSRC + "convT_bn_pool.hip"]),
+    "c5": ("conv_pool_lse_mfma_kernel", [CSRC + "conv_pool_lse.hip", CSRC + "conv333_mfma.h"]),
 }
+
+
+def source_hash(paths):
+    """SHA-256 prefix over a kernel's source files (traffic figures are only
+    reported for the source they were measured on)."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def valid_pairs(L_in, k, s, p, d, L_out):
@@ -173,7 +184,7 @@ def main():
 
     # roofline object for the dominant kernel (largest average duration)
     dom = max(per, key=lambda k: per[k]["ms_avg"])
-    kname, ksrc = KERNELS[dom]
+    kname, ksrcs = KERNELS[dom]
     bound = "mfma" if dom in ("c3", "c5") else ("hbm" if dom == "c2" else "alu")
     if bound == "hbm":
         achieved = per[dom]["algo_bytes"] / (per[dom]["ms_avg"] * 1e-3) / 1e9
@@ -182,12 +193,11 @@ def main():
         achieved = 2.0 * per[dom]["mac"] / (per[dom]["ms_avg"] * 1e-3) / 1e12
         peak, unit = (FP32_PEAK_TFLOPS if bound == "mfma" else FP32_PEAK_TFLOPS / 2), "TFLOP/s"
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"{kname}_traffic.json")
-    if os.path.exists(tfile) and os.path.exists(os.path.join(ROOT, ksrc)):
+    tfile = os.path.join(ROOT, "profiles", f"{kname}_{dom}_traffic.json")
+    if os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
-        src_hash = hashlib.sha256(open(os.path.join(ROOT, ksrc), "rb").read()).hexdigest()[:16]
-        if tr.get("source_sha256_16") == src_hash:
+        if tr.get("source_sha256_16") == source_hash(ksrcs):
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = dict(kernel=kname, workload=dom, bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
                     frac=round(achieved / peak, 4), traffic=traffic)
