@@ -19,15 +19,22 @@
 //                a lane holds rows {8a + 4*(lane/32) + b}: x = 8(a%2) + 4h + b,
 //                y = a/2, in both M tiles, i.e. four complete 2x2x2 windows, so
 //                a 2x2x2 max pool is lane-local.
-//   K loop     = input-channel chunks of 8; per chunk the input halo
-//                (TD+2)(TH+2)(TW+2) x 8 and the weights 27 x 8 x 64 are staged
-//                in LDS; per tap a lane fetches 4 K-steps of its A operand
-//                (4 consecutive channels of one voxel) and of its B operand
-//                (4 consecutive channels of one output channel) with one
-//                16-byte LDS read each.
+//   K loop     = input-channel chunks of 8, each split into three weight
+//                units of 9 taps (one kd plane).  The chunk's input halo
+//                (TD+2)(TH+2)(TW+2) x 8 sits in LDS; the units' weights
+//                9 x 8 x 64 are double-buffered in LDS.  While a unit is being
+//                computed the next unit's weights (and, during a chunk's last
+//                unit, the next chunk's halo) are already being loaded into
+//                registers, so their latency hides under ~9K cycles of MFMA
+//                work; they are written to LDS after the unit.  Per tap a
+//                lane fetches 4 K-steps of its A operand (4 consecutive
+//                channels of one voxel) and of its B operand (4 consecutive
+//                channels of one output channel) with one 16-byte LDS read
+//                each.
 //   K order    = within a chunk, K-step s and lane half h use channel
 //                4h + s; A and B agree on it, so the contraction is exact.
-// LDS: 26,112 B input + 55,728 B weights = 81,840 B -> two workgroups per CU.
+// LDS: 26,112 B halo + 2 x 18,576 B weights (the result staging of the store
+// epilogue reuses it and needs 65,792 B) -> two workgroups per CU.
 #pragma once
 
 #include <float.h>
@@ -50,8 +57,11 @@ constexpr int OCB = 64;                           // output channels per workgro
 constexpr int LDS_X = 2 * HPOS * 4;               // floats, layout [g][pos][4]
 constexpr int WTAP = 2 * 2 * 32 * 4 + 4;          // floats per tap, padded: staging writes
                                                   // of consecutive taps fall on distinct banks
-constexpr int LDS_W = 27 * WTAP;                  // floats, layout [tap][nt][h][n][s]
-constexpr int LDS_FLOATS = LDS_X + LDS_W;
+constexpr int UNIT_TAPS = 9;                      // taps per weight unit (one kd plane)
+constexpr int LDS_W = UNIT_TAPS * WTAP;           // floats per weight buffer, [tap][nt][h][n][s]
+constexpr int LDS_MAIN = LDS_X + 2 * LDS_W;
+constexpr int LDS_STAGE_OUT = OCB * (TD * TH * TW + 1);  // result staging of the store epilogue
+constexpr int LDS_FLOATS = LDS_MAIN > LDS_STAGE_OUT ? LDS_MAIN : LDS_STAGE_OUT;
 
 // How the B operand (weights) is read from global memory.
 enum WeightMode {
@@ -102,85 +112,114 @@ __device__ __forceinline__ Tile tile_of(const Args& a) {
     return t;
 }
 
-// Input halo chunk -> LDS [g][pos][4], channel ic0 + 4g + j at float j.
-// Loads are unconditional (out-of-range elements read a clamped, valid address
-// and are replaced by 0 with a select) and issued in batches, so a thread has
-// many loads in flight before its first LDS write.
-__device__ __forceinline__ void stage_x(const Args& a, const Tile& t, int64_t ic0, float* lx) {
-    constexpr int kItems = 2 * HPOS;
-    constexpr int kIters = (kItems + kThreads - 1) / kThreads;  // 7
-    const int64_t plane = a.S[0] * a.S[1] * a.S[2];
-    const float* xn = a.x + (t.n * a.Cin) * plane;
-    f32x4 v[kIters];
+// Input halo of one chunk, as two 4-channel groups: LDS layout [g][pos][4]
+// holds channels ic0 + 4g .. ic0 + 4g + 3 of halo position pos.  A thread
+// owns positions tid + 256q; the channel base pointers are wave-uniform, so a
+// thread keeps only its 4 position offsets.  Loads are unconditional
+// (out-of-range positions read a clamped, valid address and are replaced by 0
+// with a select).
+constexpr int X_POS_PER_THREAD = (HPOS + kThreads - 1) / kThreads;  // 4
+
+struct XRegs {
+    f32x4 v[2][X_POS_PER_THREAD];
+};
+
+struct XOffsets {
+    int32_t off[X_POS_PER_THREAD];  // spatial offset in the input plane, -1 outside
+};
+
+__device__ __forceinline__ XOffsets x_offsets(const Args& a, const Tile& t) {
+    XOffsets o;
 #pragma unroll
-    for (int q = 0; q < kIters; ++q) {
-        const int it = threadIdx.x + q * kThreads;
-        const int g = it / HPOS;
-        const int pos = it - g * HPOS;
+    for (int q = 0; q < X_POS_PER_THREAD; ++q) {
+        const int pos = threadIdx.x + q * kThreads;
         const int pw = pos % HW;
         const int ph = (pos / HW) % HH;
         const int pd = pos / (HW * HH);
         const int64_t gd = t.d0 - a.pad + pd, gh = t.h0 - a.pad + ph, gw = t.w0 - a.pad + pw;
-        const bool inb = it < kItems && gd >= 0 && gd < a.S[0] && gh >= 0 && gh < a.S[1] && gw >= 0 &&
+        const bool inb = pos < HPOS && gd >= 0 && gd < a.S[0] && gh >= 0 && gh < a.S[1] && gw >= 0 &&
                          gw < a.S[2];
-        const int64_t off = inb ? (gd * a.S[1] + gh) * a.S[2] + gw : 0;
+        o.off[q] = inb ? (int32_t)((gd * a.S[1] + gh) * a.S[2] + gw) : -1;
+    }
+    return o;
+}
+
+__device__ __forceinline__ void load_x(const Args& a, const Tile& t, const XOffsets& o, int64_t ic0,
+                                       XRegs& r) {
+    const int64_t plane = a.S[0] * a.S[1] * a.S[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t ic = ic0 + 4 * g + j;
-            const bool ok = inb && ic < a.Cin;
-            const float e = xn[ok ? ic * plane + off : 0];
-            v[q][j] = ok ? e : 0.f;
-        }
-    }
+            const bool icok = ic < a.Cin;
+            const float* xc = a.x + (t.n * a.Cin + (icok ? ic : 0)) * plane;  // wave-uniform
 #pragma unroll
-    for (int q = 0; q < kIters; ++q) {
-        const int it = threadIdx.x + q * kThreads;
-        if (it < kItems) *reinterpret_cast<f32x4*>(lx + it * 4) = v[q];
+            for (int q = 0; q < X_POS_PER_THREAD; ++q) {
+                const bool ok = icok && o.off[q] >= 0;
+                const float e = xc[ok ? o.off[q] : 0];
+                r.v[g][q][j] = ok ? e : 0.f;
+            }
+        }
+}
+
+__device__ __forceinline__ void store_x(const XRegs& r, float* lx) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int q = 0; q < X_POS_PER_THREAD; ++q) {
+            const int pos = threadIdx.x + q * kThreads;
+            if (pos < HPOS) *reinterpret_cast<f32x4*>(lx + (g * HPOS + pos) * 4) = r.v[g][q];
+        }
+}
+
+// One weight unit: the 9 taps (kd, *, *) of 8 input channels x 64 output
+// channels, LDS layout [tap % 9][nt][h][n][s] with oc = oc0 + 32nt + n and
+// ic = ic0 + 4h + s.  A thread owns the (oc, ic) pairs tid and tid + 256 and
+// reads each pair's 9 taps, which are consecutive in w (conv weights
+// w[oc][ic][tap]; transposed weights w[ic][oc][t] with tap = 26 - t, flipped).
+constexpr int W_PAIRS_PER_THREAD = ICC * OCB / kThreads;  // 2
+static_assert(ICC * OCB % kThreads == 0, "weight unit pairs");
+
+struct WRegs {
+    float v[W_PAIRS_PER_THREAD][UNIT_TAPS];
+};
+
+template <int kMode>
+__device__ __forceinline__ void load_w(const Args& a, const Tile& t, int64_t ic0, int kd, WRegs& r) {
+#pragma unroll
+    for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) {
+        const int p = threadIdx.x + q * kThreads;
+        const int oc = p >> 3, j = p & 7;
+        const int64_t goc = t.oc0 + oc, gic = ic0 + j;
+        const bool ok = goc < a.Cout && gic < a.Cin;
+        // first source element of this unit's 9-tap run
+        const int64_t first = kMode == kConvWeights ? (goc * a.Cin + gic) * 27 + kd * UNIT_TAPS
+                                                    : (gic * a.Cout + goc) * 27 + (18 - kd * UNIT_TAPS);
+        const float* src = a.w + (ok ? first : 0);
+#pragma unroll
+        for (int u = 0; u < UNIT_TAPS; ++u) {
+            const float v = src[u];
+            r.v[q][u] = ok ? v : 0.f;
+        }
     }
 }
 
-// Weight chunk -> LDS [tap][nt][h][n][s] with oc = oc0 + 32nt + n and
-// ic = ic0 + 4h + s.  Global reads follow the memory order of w; like
-// stage_x, loads are unconditional and batched.
 template <int kMode>
-__device__ __forceinline__ void stage_w(const Args& a, const Tile& t, int64_t ic0, float* lw) {
-    constexpr int kItems = 27 * ICC * OCB;       // 13824 = 54 per thread
-    constexpr int kBatch = 9;
-    static_assert(kItems % (kThreads * kBatch) == 0, "weight staging batches");
-    for (int q0 = 0; q0 < kItems / kThreads; q0 += kBatch) {
-        float v[kBatch];
-        int dst[kBatch];
+__device__ __forceinline__ void store_w(const WRegs& r, float* lw) {
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            const int e = threadIdx.x + (q0 + q) * kThreads;
-            int oc, j, tap;
-            int64_t src;
-            bool ok;
-            if (kMode == kConvWeights) {
-                oc = e / (ICC * 27);
-                const int rem = e - oc * (ICC * 27);
-                j = rem / 27;
-                tap = rem - j * 27;
-                const int64_t goc = t.oc0 + oc, gic = ic0 + j;
-                ok = goc < a.Cout && gic < a.Cin;
-                src = (goc * a.Cin + gic) * 27 + tap;
-            } else {
-                j = e / (OCB * 27);
-                const int rem = e - j * (OCB * 27);
-                oc = rem / 27;
-                const int tt = rem - oc * 27;
-                tap = 26 - tt;
-                const int64_t goc = t.oc0 + oc, gic = ic0 + j;
-                ok = goc < a.Cout && gic < a.Cin;
-                src = (gic * a.Cout + goc) * 27 + tt;
-            }
-            const float e2 = a.w[ok ? src : 0];
-            v[q] = ok ? e2 : 0.f;
-            const int nt = oc >> 5, n = oc & 31, h = j >> 2, s = j & 3;
-            dst[q] = tap * WTAP + ((nt * 2 + h) * 32 + n) * 4 + s;
+    for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) {
+        const int p = threadIdx.x + q * kThreads;
+        const int oc = p >> 3, j = p & 7;
+        const int nt = oc >> 5, n = oc & 31, h = j >> 2, s = j & 3;
+        float* dst = lw + ((nt * 2 + h) * 32 + n) * 4 + s;
+#pragma unroll
+        for (int u = 0; u < UNIT_TAPS; ++u) {
+            // conv: source tap kd*9 + u is unit tap u; transposed: source t = 18 - 9kd + u
+            // is tap 26 - t = 8 + 9kd - u, i.e. unit tap 8 - u
+            const int t9 = kMode == kConvWeights ? u : 8 - u;
+            dst[t9 * WTAP] = r.v[q][u];
         }
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) lw[dst[q]] = v[q];
     }
 }
 
@@ -188,7 +227,7 @@ __device__ __forceinline__ void stage_w(const Args& a, const Tile& t, int64_t ic
 template <int kMode>
 __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* lds, f32x16 (&acc)[2][2]) {
     float* lx = lds;
-    float* lw = lds + LDS_X;
+    float* lw0 = lds + LDS_X;
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int h = lane >> 5;
@@ -210,25 +249,40 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
             for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 
     const int64_t nchunks = ceil_div(a.Cin, ICC);
+    const XOffsets xo = x_offsets(a, t);
+    {
+        XRegs xr;
+        WRegs wr;
+        load_x(a, t, xo, 0, xr);
+        load_w<kMode>(a, t, 0, 0, wr);
+        store_x(xr, lx);
+        store_w<kMode>(wr, lw0);
+        __syncthreads();
+    }
+    int buf = 0;
     for (int64_t c = 0; c < nchunks; ++c) {
-        __syncthreads();
-        stage_x(a, t, c * ICC, lx);
-        stage_w<kMode>(a, t, c * ICC, lw);
-        __syncthreads();
-#pragma unroll
-        for (int kd = 0; kd < 3; ++kd)
+#pragma unroll 1
+        for (int kd = 0; kd < 3; ++kd) {
+            const bool last_unit = c == nchunks - 1 && kd == 2;
+            const int64_t nc = kd < 2 ? c : c + 1;  // chunk and kd plane of the next unit
+            const int nkd = kd < 2 ? kd + 1 : 0;
+            WRegs wr;
+            XRegs xr;
+            if (!last_unit) load_w<kMode>(a, t, nc * ICC, nkd, wr);
+            if (kd == 2 && !last_unit) load_x(a, t, xo, nc * ICC, xr);
+            const float* lw = lw0 + buf * LDS_W;
 #pragma unroll
             for (int kh = 0; kh < 3; ++kh)
 #pragma unroll
                 for (int kw = 0; kw < 3; ++kw) {
-                    const int tap = (kd * 3 + kh) * 3 + kw;
+                    const int t9 = kh * 3 + kw;
                     const int xoff = ((kd * HH + kh) * HW + kw) * 4;
                     f32x4 av[2], bv[2];
 #pragma unroll
                     for (int mt = 0; mt < 2; ++mt) av[mt] = *reinterpret_cast<const f32x4*>(lx + abase[mt] + xoff);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
-                        bv[nt] = *reinterpret_cast<const f32x4*>(lw + bbase + tap * WTAP + nt * 256);
+                        bv[nt] = *reinterpret_cast<const f32x4*>(lw + bbase + t9 * WTAP + nt * 256);
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -238,6 +292,17 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
                                 acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mt][s], bv[nt][s],
                                                                                    acc[mt][nt], 0, 0, 0);
                 }
+            if (last_unit) break;
+            if (kd == 2) {
+                __syncthreads();  // every wave is done with this chunk's halo
+                store_x(xr, lx);
+            }
+            // the other weight buffer was last read by the previous unit, which
+            // every wave finished before the previous barrier
+            store_w<kMode>(wr, lw0 + (buf ^ 1) * LDS_W);
+            __syncthreads();
+            buf ^= 1;
+        }
     }
 }
 

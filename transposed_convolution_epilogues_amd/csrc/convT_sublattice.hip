@@ -22,6 +22,7 @@ namespace {
 using namespace mfma333;
 
 constexpr int kStage = TD * TH * TW + 1;  // LDS floats per channel (padded)
+static_assert(OCB * kStage <= LDS_FLOATS, "result staging fits the kernel's LDS");
 
 // kLattice = 1: destination o = q (plain conv).  kLattice = 2: destination
 // o = 2q + 1 inside a destination grid of size Y (transposed conv).
