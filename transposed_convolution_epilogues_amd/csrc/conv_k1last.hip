@@ -49,8 +49,11 @@ struct K1Args {
 // so after the MFMAs a lane holds 4 consecutive positions of each of its 16
 // channels per M tile, and one 16-byte store per channel covers them: lanes
 // 0-31 then write 512 contiguous bytes of one channel row and lanes 32-63 of
-// another.  Measured on MI355X this store shape runs at ~6.3 TB/s, against
-// ~2.2 TB/s for one 4-byte column per lane.
+// another.  Measured on MI355X with stores alone, writing this kernel's 2.6 GB
+// output in this shape takes ~0.83-0.93 ms (about 3.1 TB/s, whatever the
+// workgroup shape), against 1.19 ms with one 4-byte column per lane; only
+// long runs within one channel plane go faster (whole 10 KB rows 0.62 ms), and
+// a block of 64 channels cannot provide those.
 template <bool kBias, bool kVec, bool kFull>
 __device__ __forceinline__ void store_block(float* yb, uint32_t ystride, const f32x16 (&acc)[2][4],
                                             const float (&brow)[2][16], int64_t j0, int r, int h, int64_t J,
