@@ -144,6 +144,10 @@ __device__ __forceinline__ XOffsets x_offsets(const Args& a, const Tile& t) {
     return o;
 }
 
+// The loads leave the raw values in registers; the zero padding is applied
+// when they are written to LDS.  A select right after a load would make the
+// wave wait for the load there, while the loads are meant to stay in flight
+// under a whole unit of MFMA work.
 __device__ __forceinline__ void load_x(const Args& a, const Tile& t, const XOffsets& o, int64_t ic0,
                                        XRegs& r) {
     const int64_t plane = a.S[0] * a.S[1] * a.S[2];
@@ -155,21 +159,21 @@ __device__ __forceinline__ void load_x(const Args& a, const Tile& t, const XOffs
             const bool icok = ic < a.Cin;
             const float* xc = a.x + (t.n * a.Cin + (icok ? ic : 0)) * plane;  // wave-uniform
 #pragma unroll
-            for (int q = 0; q < X_POS_PER_THREAD; ++q) {
-                const bool ok = icok && o.off[q] >= 0;
-                const float e = xc[ok ? o.off[q] : 0];
-                r.v[g][q][j] = ok ? e : 0.f;
-            }
+            for (int q = 0; q < X_POS_PER_THREAD; ++q) r.v[g][q][j] = xc[o.off[q] >= 0 ? o.off[q] : 0];
         }
 }
 
-__device__ __forceinline__ void store_x(const XRegs& r, float* lx) {
+__device__ __forceinline__ void store_x(const Args& a, const XOffsets& o, int64_t ic0, const XRegs& r,
+                                        float* lx) {
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int q = 0; q < X_POS_PER_THREAD; ++q) {
             const int pos = threadIdx.x + q * kThreads;
-            if (pos < HPOS) *reinterpret_cast<f32x4*>(lx + (g * HPOS + pos) * 4) = r.v[g][q];
+            f32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = (ic0 + 4 * g + j < a.Cin && o.off[q] >= 0) ? r.v[g][q][j] : 0.f;
+            if (pos < HPOS) *reinterpret_cast<f32x4*>(lx + (g * HPOS + pos) * 4) = v;
         }
 }
 
@@ -198,19 +202,17 @@ __device__ __forceinline__ void load_w(const Args& a, const Tile& t, int64_t ic0
                                                     : (gic * a.Cout + goc) * 27 + (18 - kd * UNIT_TAPS);
         const float* src = a.w + (ok ? first : 0);
 #pragma unroll
-        for (int u = 0; u < UNIT_TAPS; ++u) {
-            const float v = src[u];
-            r.v[q][u] = ok ? v : 0.f;
-        }
+        for (int u = 0; u < UNIT_TAPS; ++u) r.v[q][u] = src[u];
     }
 }
 
 template <int kMode>
-__device__ __forceinline__ void store_w(const WRegs& r, float* lw) {
+__device__ __forceinline__ void store_w(const Args& a, const Tile& t, int64_t ic0, const WRegs& r, float* lw) {
 #pragma unroll
     for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) {
         const int p = threadIdx.x + q * kThreads;
         const int oc = p >> 3, j = p & 7;
+        const bool ok = t.oc0 + oc < a.Cout && ic0 + j < a.Cin;
         const int nt = oc >> 5, n = oc & 31, h = j >> 2, s = j & 3;
         float* dst = lw + ((nt * 2 + h) * 32 + n) * 4 + s;
 #pragma unroll
@@ -218,14 +220,24 @@ __device__ __forceinline__ void store_w(const WRegs& r, float* lw) {
             // conv: source tap kd*9 + u is unit tap u; transposed: source t = 18 - 9kd + u
             // is tap 26 - t = 8 + 9kd - u, i.e. unit tap 8 - u
             const int t9 = kMode == kConvWeights ? u : 8 - u;
-            dst[t9 * WTAP] = r.v[q][u];
+            dst[t9 * WTAP] = ok ? r.v[q][u] : 0.f;
         }
     }
 }
 
-// Runs the whole K loop; acc[mt][nt] holds the 32x32 result tiles.
-template <int kMode>
-__device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* lds, f32x16 (&acc)[2][2]) {
+// Side work of a kernel that does not overlap anything with the K loop.
+struct NoSideWork {
+    __device__ void operator()(int64_t, int64_t) const {}
+};
+
+// Runs the whole K loop; acc[mt][nt] holds the 32x32 result tiles.  side(u, n)
+// is called once per weight unit u of n, right after that unit's prefetch
+// loads are issued and before its MFMAs: work placed there (stores that do
+// not depend on the result) overlaps the matrix-core work.  It must not touch
+// the operand LDS.
+template <int kMode, class Side = NoSideWork>
+__device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* lds, f32x16 (&acc)[2][2],
+                                         const Side& side = Side()) {
     float* lx = lds;
     float* lw0 = lds + LDS_X;
     const int lane = threadIdx.x & 63;
@@ -255,8 +267,8 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
         WRegs wr;
         load_x(a, t, xo, 0, xr);
         load_w<kMode>(a, t, 0, 0, wr);
-        store_x(xr, lx);
-        store_w<kMode>(wr, lw0);
+        store_x(a, xo, 0, xr, lx);
+        store_w<kMode>(a, t, 0, wr, lw0);
         __syncthreads();
     }
     int buf = 0;
@@ -270,6 +282,7 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
             XRegs xr;
             if (!last_unit) load_w<kMode>(a, t, nc * ICC, nkd, wr);
             if (kd == 2 && !last_unit) load_x(a, t, xo, nc * ICC, xr);
+            side(c * 3 + kd, nchunks * 3);
             const float* lw = lw0 + buf * LDS_W;
 #pragma unroll
             for (int kh = 0; kh < 3; ++kh)
@@ -295,11 +308,11 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
             if (last_unit) break;
             if (kd == 2) {
                 __syncthreads();  // every wave is done with this chunk's halo
-                store_x(xr, lx);
+                store_x(a, xo, nc * ICC, xr, lx);
             }
             // the other weight buffer was last read by the previous unit, which
             // every wave finished before the previous barrier
-            store_w<kMode>(wr, lw0 + (buf ^ 1) * LDS_W);
+            store_w<kMode>(a, t, nc * ICC, wr, lw0 + (buf ^ 1) * LDS_W);
             __syncthreads();
             buf ^= 1;
         }

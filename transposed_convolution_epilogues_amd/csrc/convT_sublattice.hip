@@ -21,17 +21,202 @@ namespace {
 
 using namespace mfma333;
 
-constexpr int kStage = TD * TH * TW + 1;  // LDS floats per channel (padded)
+constexpr int kStage = TD * TH * TW + 1;  // LDS floats per channel of the result staging (padded)
 static_assert(OCB * kStage <= LDS_FLOATS, "result staging fits the kernel's LDS");
 
+// n / d for 0 <= n, d < 2^22 from a float reciprocal: the rounded product is
+// within 1/2 of n / d, so its truncation is off by at most one, which one
+// remainder check corrects.
+struct Div {
+    int d;
+    float inv;
+    __device__ Div() : d(1), inv(1.f) {}
+    __device__ explicit Div(int d_) : d(d_), inv(1.f / (float)(d_ > 0 ? d_ : 1)) {}
+    __device__ int quot(int n) const {
+        int q = (int)((float)n * inv);
+        const int r = n - q * d;
+        if (r < 0)
+            --q;
+        else if (r >= d)
+            ++q;
+        return q;
+    }
+};
+
+// Destination box of a workgroup: channels oc0 + oc (oc < ocs), planes
+// lo[0] + id (id < bd), rows lo[1] + ih (ih < bh), columns lo[2] + c (c < bw).
+struct Box {
+    int lo[3];
+    int bd, bh, bw, ocs;
+    int64_t plane, Y1, Y2;
+    float* yn;       // channel oc0 of this workgroup's sample
+    bool full_rows;  // the box spans complete rows, so a plane of it is contiguous
+    Div div_bw;
+};
+
+// A set of runs inside the box.  A run is a contiguous stretch of y: either
+// a whole plane of the box (slab; needs full rows) or one row.  Planes
+// id = id0 + id_step * i (i < n1); rows ih = ih0 + ih_step * j (j < n2, row
+// runs only).  Each run is cut into 16-byte aligned slots of 4 floats counted
+// from the run's actual address; item g of the set is slot g % SL of run
+// g / SL, and runs are ordered (oc, i, j).
+struct RunSet {
+    int id0, id_step, n1;
+    int ih0, ih_step, n2;
+    bool slab;
+    int L, SL, items;  // floats per run, slots per run (enough for any alignment), items
+    Div div_sl, div_n1, div_n2;
+};
+
+__device__ inline int count_from(int first, int step, int end) {
+    return first < end ? (end - first + step - 1) / step : 0;
+}
+
+__device__ inline RunSet make_runs(const Box& b, int id0, int id_step, int ih0, int ih_step, bool slab) {
+    const int n1 = count_from(id0, id_step, b.bd);
+    const int n2 = slab ? 1 : count_from(ih0, ih_step, b.bh);
+    const int L = slab ? b.bh * b.bw : b.bw;
+    const int SL = (L + 6) >> 2;
+    return RunSet{id0, id_step, n1, ih0, ih_step, n2, slab, L, SL, b.ocs * n1 * n2 * SL,
+                  Div(SL), Div(n1), Div(n2)};
+}
+
+// Writes items [g0, g1) of a run set with the whole workgroup.  A slot wholly
+// inside its run is written with one 16-byte store, the partial slots at a
+// run's two ends float by float.  value(oc, id, ih, c, in) gives the float at
+// box coordinates (oc, id, ih, c); in is false for the floats of a partial
+// slot that lie outside the run (their value is discarded).
+template <class Value>
+__device__ __forceinline__ void store_runs(const Box& b, const RunSet& rs, int g0, int g1, const Value& value) {
+    for (int g = g0 + (int)threadIdx.x; g < g1; g += kThreads) {
+        int r = rs.div_sl.quot(g);
+        const int s = g - r * rs.SL;
+        int j = 0;
+        if (!rs.slab) {
+            const int r2 = rs.div_n2.quot(r);
+            j = r - r2 * rs.n2;
+            r = r2;
+        }
+        const int oc = rs.div_n1.quot(r);
+        const int id = rs.id0 + rs.id_step * (r - oc * rs.n1);
+        const int ihr = rs.slab ? 0 : rs.ih0 + rs.ih_step * j;
+        float* run = b.yn + oc * b.plane + ((int64_t)(b.lo[0] + id) * b.Y1 + b.lo[1] + ihr) * b.Y2 + b.lo[2];
+        const int e0 = 4 * s - (int)(((uintptr_t)run >> 2) & 3);  // run offset of the slot's first float
+        // box row and column of the slot's first float; a float before the run
+        // start (e0 < 0) gets a negative column and is never stored
+        int ih = ihr, c = e0;
+        if (rs.slab && e0 > 0) {
+            ih = b.div_bw.quot(e0);
+            c = e0 - ih * b.bw;
+        }
+        float v[4];
+        bool in[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int ck = c + k, ihk = ih;
+            if (rs.slab && ck >= b.bw) {  // slabs have bw >= 4: at most one row change per slot
+                ck -= b.bw;
+                ++ihk;
+            }
+            in[k] = e0 + k >= 0 && e0 + k < rs.L;
+            v[k] = value(oc, id, ihk, ck, in[k]);
+        }
+        if (in[0] && in[3]) {
+            const f32x4 o = {v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4*>(run + e0) = o;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (in[k]) run[e0 + k] = v[k];
+        }
+    }
+}
+
+struct BiasValue {
+    const float* sbias;
+    __device__ float operator()(int oc, int, int, int, bool) const { return sbias[oc]; }
+};
+
+// kLattice = 1: box coordinate (id, ih, c) is tile voxel (id, ih, c).
+// kLattice = 2: the box starts at even destination coordinates, so a box
+// coordinate is odd exactly when the destination coordinate is; odd 2m + 1
+// is tile voxel m, and a voxel with any even coordinate is the bias alone.
+template <int kLattice>
+struct TileValue {
+    const float* lds;
+    const float* sbias;
+    __device__ float operator()(int oc, int id, int ih, int c, bool in) const {
+        const bool from_tile = kLattice == 1 || (id & ih & c & 1) != 0;
+        const int idx = kLattice == 1 ? (id * TH + ih) * TW + c : ((id >> 1) * TH + (ih >> 1)) * TW + (c >> 1);
+        const float tv = lds[oc * kStage + (in && from_tile ? idx : 0)];
+        return (from_tile ? tv : 0.f) + sbias[oc];
+    }
+};
+
+// Side work of the transposed conv: during the K loop, the units share out
+// the bias-only part of the box (even planes, and the even rows of odd
+// planes), which does not depend on the result.
+struct BiasSideWork {
+    const Box* b;
+    const RunSet* even_planes;
+    const RunSet* even_rows;
+    const float* sbias;
+    __device__ void operator()(int64_t u, int64_t n) const {
+        const int n_a = even_planes->items;
+        const int64_t total = n_a + even_rows->items;
+        const int g0 = (int)(total * u / n), g1 = (int)(total * (u + 1) / n);
+        const BiasValue bias{sbias};
+        if (g0 < n_a) store_runs(*b, *even_planes, g0, g1 < n_a ? g1 : n_a, bias);
+        if (g1 > n_a) store_runs(*b, *even_rows, (g0 > n_a ? g0 : n_a) - n_a, g1 - n_a, bias);
+    }
+};
+
 // kLattice = 1: destination o = q (plain conv).  kLattice = 2: destination
-// o = 2q + 1 inside a destination grid of size Y (transposed conv).
+// o = 2q + 1 inside a destination grid of size Y (transposed conv); every
+// destination voxel with an even coordinate holds the bias.
 template <int kMode, int kLattice>
 __global__ __launch_bounds__(kThreads) void conv333_store_kernel(Args a) {
     __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
+    __shared__ float sbias[OCB];
     const Tile t = tile_of(a);
+    if (threadIdx.x < OCB)
+        sbias[threadIdx.x] = (a.bias && t.oc0 + threadIdx.x < a.Cout) ? a.bias[t.oc0 + threadIdx.x] : 0.f;
+    // (the mainloop's first barrier publishes sbias)
+
+    Box b{};
+    {
+        const int64_t q0[3] = {t.d0, t.h0, t.w0};
+        const int T[3] = {TD, TH, TW};
+        int hi[3];
+        for (int j = 0; j < 3; ++j) {
+            if (kLattice == 1) {
+                b.lo[j] = (int)q0[j];
+                hi[j] = (int)(q0[j] + T[j] < a.Y[j] ? q0[j] + T[j] : a.Y[j]);
+            } else {
+                b.lo[j] = (int)(2 * q0[j]);
+                hi[j] = (int)((q0[j] + T[j] >= a.O[j]) ? a.Y[j] : 2 * (q0[j] + T[j]));
+            }
+        }
+        b.bd = hi[0] - b.lo[0];
+        b.bh = hi[1] - b.lo[1];
+        b.bw = hi[2] - b.lo[2];
+        b.ocs = (int)(a.Cout - t.oc0 < OCB ? a.Cout - t.oc0 : OCB);
+        b.plane = a.Y[0] * a.Y[1] * a.Y[2];
+        b.Y1 = a.Y[1];
+        b.Y2 = a.Y[2];
+        b.yn = a.y + (t.n * a.Cout + t.oc0) * b.plane;
+        b.full_rows = b.lo[2] == 0 && hi[2] == a.Y[2] && b.bw >= 4;
+        b.div_bw = Div(b.bw);
+    }
+
     f32x16 acc[2][2];
-    mainloop<kMode>(a, t, lds, acc);
+    if (kLattice == 2) {
+        const RunSet even_planes = make_runs(b, 0, 2, 0, 1, b.full_rows);
+        const RunSet even_rows = make_runs(b, 1, 2, 0, 2, false);
+        mainloop<kMode>(a, t, lds, acc, BiasSideWork{&b, &even_planes, &even_rows, sbias});
+    } else {
+        mainloop<kMode>(a, t, lds, acc);
+    }
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
@@ -49,43 +234,10 @@ __global__ __launch_bounds__(kThreads) void conv333_store_kernel(Args a) {
             }
     __syncthreads();
 
-    // destination box of this workgroup
-    int64_t lo[3], hi[3];
-    const int64_t q0[3] = {t.d0, t.h0, t.w0};
-    const int T[3] = {TD, TH, TW};
-    for (int j = 0; j < 3; ++j) {
-        if (kLattice == 1) {
-            lo[j] = q0[j];
-            hi[j] = q0[j] + T[j] < a.Y[j] ? q0[j] + T[j] : a.Y[j];
-        } else {
-            lo[j] = 2 * q0[j];
-            hi[j] = (q0[j] + T[j] >= a.O[j]) ? a.Y[j] : 2 * (q0[j] + T[j]);
-        }
-    }
-    const int bd = (int)(hi[0] - lo[0]), bh = (int)(hi[1] - lo[1]), bw = (int)(hi[2] - lo[2]);
-    const int ocs = (int)(a.Cout - t.oc0 < OCB ? a.Cout - t.oc0 : OCB);
-    const int64_t plane = a.Y[0] * a.Y[1] * a.Y[2];
-    float* yn = a.y + (t.n * a.Cout + t.oc0) * plane;
-    for (int oc = 0; oc < ocs; ++oc) {
-        const float b = a.bias ? a.bias[t.oc0 + oc] : 0.f;
-        const float* src = lds + oc * kStage;
-        for (int id = 0; id < bd; ++id) {
-            const int64_t od = lo[0] + id;
-            for (int ih = wv; ih < bh; ih += kThreads / 64) {
-                const int64_t oh = lo[1] + ih;
-                float* row = yn + oc * plane + (od * a.Y[1] + oh) * a.Y[2] + lo[2];
-                if (kLattice == 1) {
-                    const float* s = src + (id * TH + ih) * TW;
-                    for (int c = lane; c < bw; c += 64) row[c] = s[c] + b;
-                } else {
-                    const bool odd_row = (od & 1) && (oh & 1);
-                    const float* s = src + (odd_row ? (int)((((od - 1) >> 1) - t.d0) * TH + (((oh - 1) >> 1) - t.h0)) * TW : 0);
-                    // lo[2] is even, so column c is odd exactly when ow is
-                    for (int c = lane; c < bw; c += 64) row[c] = (odd_row && (c & 1)) ? s[c >> 1] + b : b;
-                }
-            }
-        }
-    }
+    // the rest of the box: all of it for the plain conv, the odd rows of the
+    // odd planes for the transposed conv
+    const RunSet rest = kLattice == 1 ? make_runs(b, 0, 1, 0, 1, b.full_rows) : make_runs(b, 1, 2, 1, 2, false);
+    store_runs(b, rest, 0, rest.items, TileValue<kLattice>{lds, sbias});
 }
 
 Args make_args(const float* x, const float* w, const float* bias, float* y, const Geom& g) {
