@@ -7,18 +7,22 @@
 // output voxels, K = Cin x 27 taps, N = Cout):
 //   acc[voxel, oc] += sum_{ic, tap} X[ic, voxel + tap - pad] * W[oc, ic, tap]
 //
-// Work decomposition
-//   workgroup  = 256 threads (4 waves), output tile TD x TH x TW = 2 x 4 x 32
+// Work decomposition (kMT = tile depth, 2 or 4)
+//   workgroup  = 256 threads (4 waves), output tile TD x TH x TW = kMT x 4 x 32
 //                voxels x 64 output channels
-//   wave       = 2 (D) x 2 (H) x 16 (W) voxels x 64 channels = 2 x 2 MFMA tiles
-//                of 32 x 32 (M = voxels, N = channels), 64 accumulator VGPRs
+//   wave       = kMT (D) x 2 (H) x 16 (W) voxels x 64 channels = kMT x 2 MFMA
+//                tiles of 32 x 32 (M = voxels, N = channels), 32 kMT
+//                accumulator registers
 //   M tile     = 1 (D) x 2 (H) x 16 (W) voxels: row r holds x = r % 16,
-//                y = r / 16, and the wave's two M tiles are the two D planes.
+//                y = r / 16, and the wave's M tiles are its D planes.
 //                A-operand lanes 0-15 then read 16 consecutive voxels (256
 //                contiguous bytes of LDS, no bank conflict).  In the MFMA result
 //                a lane holds rows {8a + 4*(lane/32) + b}: x = 8(a%2) + 4h + b,
-//                y = a/2, in both M tiles, i.e. four complete 2x2x2 windows, so
-//                a 2x2x2 max pool is lane-local.
+//                y = a/2, in every M tile, so a pair of M tiles holds four
+//                complete 2x2x2 windows per lane and a 2x2x2 max pool is
+//                lane-local.  The deeper tile doubles the MFMA work between
+//                two barriers and cuts the halo overhead (6/4 instead of 4/2
+//                planes per output plane).
 //   K loop     = input-channel chunks of 8, each split into three weight
 //                units of 9 taps (one kd plane).  The chunk's input halo
 //                (TD+2)(TH+2)(TW+2) x 8 sits in LDS; the units' weights
@@ -33,8 +37,9 @@
 //                each.
 //   K order    = within a chunk, K-step s and lane half h use channel
 //                4h + s; A and B agree on it, so the contraction is exact.
-// LDS: 26,112 B halo + 2 x 18,576 B weights (the result staging of the store
-// epilogue reuses it and needs 65,792 B) -> two workgroups per CU.
+// LDS: halo 26,112 B (kMT = 2) or 39,168 B (kMT = 4) + 2 x 18,576 B weights
+// (the result staging of the kMT = 2 store epilogue reuses it and needs
+// 65,792 B) -> two workgroups per CU either way.
 #pragma once
 
 #include <float.h>
@@ -49,19 +54,25 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int TD = 2, TH = 4, TW = 32;           // output tile per workgroup
-constexpr int HD = TD + 2, HH = TH + 2, HW = TW + 2;
-constexpr int HPOS = HD * HH * HW;               // 816 halo positions
+constexpr int TH = 4, TW = 32;                   // output tile per workgroup (H, W)
+constexpr int HH = TH + 2, HW = TW + 2;
 constexpr int ICC = 8;                            // input channels per chunk
 constexpr int OCB = 64;                           // output channels per workgroup
-constexpr int LDS_X = 2 * HPOS * 4;               // floats, layout [g][pos][4]
 constexpr int WTAP = 2 * 2 * 32 * 4 + 4;          // floats per tap, padded: staging writes
                                                   // of consecutive taps fall on distinct banks
 constexpr int UNIT_TAPS = 9;                      // taps per weight unit (one kd plane)
 constexpr int LDS_W = UNIT_TAPS * WTAP;           // floats per weight buffer, [tap][nt][h][n][s]
-constexpr int LDS_MAIN = LDS_X + 2 * LDS_W;
-constexpr int LDS_STAGE_OUT = OCB * (TD * TH * TW + 1);  // result staging of the store epilogue
-constexpr int LDS_FLOATS = LDS_MAIN > LDS_STAGE_OUT ? LDS_MAIN : LDS_STAGE_OUT;
+
+// Sizes that depend on the tile depth kMT.
+template <int kMT>
+struct Geo {
+    static constexpr int TD = kMT;                        // output tile depth
+    static constexpr int HD = TD + 2;
+    static constexpr int HPOS = HD * HH * HW;             // halo positions: 816 or 1224
+    static constexpr int LDS_X = 2 * HPOS * 4;            // floats, layout [g][pos][4]
+    static constexpr int LDS_MAIN = LDS_X + 2 * LDS_W;    // floats of the K loop
+    static constexpr int XQ = (HPOS + kThreads - 1) / kThreads;  // halo positions per thread
+};
 
 // How the B operand (weights) is read from global memory.
 enum WeightMode {
@@ -93,6 +104,7 @@ struct Tile {
     int64_t oc0;
 };
 
+template <int kMT>
 __device__ __forceinline__ Tile tile_of(const Args& a) {
     const int64_t nb = (int64_t)gridDim.x;
     int64_t b = blockIdx.x;
@@ -106,7 +118,7 @@ __device__ __forceinline__ Tile tile_of(const Args& a) {
     b /= a.tiles[1];
     const int64_t td = b % a.tiles[0];
     t.n = b / a.tiles[0];
-    t.d0 = td * TD;
+    t.d0 = td * Geo<kMT>::TD;
     t.h0 = th * TH;
     t.w0 = tw * TW;
     return t;
@@ -115,23 +127,25 @@ __device__ __forceinline__ Tile tile_of(const Args& a) {
 // Input halo of one chunk, as two 4-channel groups: LDS layout [g][pos][4]
 // holds channels ic0 + 4g .. ic0 + 4g + 3 of halo position pos.  A thread
 // owns positions tid + 256q; the channel base pointers are wave-uniform, so a
-// thread keeps only its 4 position offsets.  Loads are unconditional
+// thread keeps only its position offsets.  Loads are unconditional
 // (out-of-range positions read a clamped, valid address and are replaced by 0
 // with a select).
-constexpr int X_POS_PER_THREAD = (HPOS + kThreads - 1) / kThreads;  // 4
-
+template <int kMT>
 struct XRegs {
-    f32x4 v[2][X_POS_PER_THREAD];
+    f32x4 v[2][Geo<kMT>::XQ];
 };
 
+template <int kMT>
 struct XOffsets {
-    int32_t off[X_POS_PER_THREAD];  // spatial offset in the input plane, -1 outside
+    int32_t off[Geo<kMT>::XQ];  // spatial offset in the input plane, -1 outside
 };
 
-__device__ __forceinline__ XOffsets x_offsets(const Args& a, const Tile& t) {
-    XOffsets o;
+template <int kMT>
+__device__ __forceinline__ XOffsets<kMT> x_offsets(const Args& a, const Tile& t) {
+    constexpr int HPOS = Geo<kMT>::HPOS;
+    XOffsets<kMT> o;
 #pragma unroll
-    for (int q = 0; q < X_POS_PER_THREAD; ++q) {
+    for (int q = 0; q < Geo<kMT>::XQ; ++q) {
         const int pos = threadIdx.x + q * kThreads;
         const int pw = pos % HW;
         const int ph = (pos / HW) % HH;
@@ -148,8 +162,9 @@ __device__ __forceinline__ XOffsets x_offsets(const Args& a, const Tile& t) {
 // when they are written to LDS.  A select right after a load would make the
 // wave wait for the load there, while the loads are meant to stay in flight
 // under a whole unit of MFMA work.
-__device__ __forceinline__ void load_x(const Args& a, const Tile& t, const XOffsets& o, int64_t ic0,
-                                       XRegs& r) {
+template <int kMT>
+__device__ __forceinline__ void load_x(const Args& a, const Tile& t, const XOffsets<kMT>& o, int64_t ic0,
+                                       XRegs<kMT>& r) {
     const int64_t plane = a.S[0] * a.S[1] * a.S[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
@@ -159,16 +174,18 @@ __device__ __forceinline__ void load_x(const Args& a, const Tile& t, const XOffs
             const bool icok = ic < a.Cin;
             const float* xc = a.x + (t.n * a.Cin + (icok ? ic : 0)) * plane;  // wave-uniform
 #pragma unroll
-            for (int q = 0; q < X_POS_PER_THREAD; ++q) r.v[g][q][j] = xc[o.off[q] >= 0 ? o.off[q] : 0];
+            for (int q = 0; q < Geo<kMT>::XQ; ++q) r.v[g][q][j] = xc[o.off[q] >= 0 ? o.off[q] : 0];
         }
 }
 
-__device__ __forceinline__ void store_x(const Args& a, const XOffsets& o, int64_t ic0, const XRegs& r,
+template <int kMT>
+__device__ __forceinline__ void store_x(const Args& a, const XOffsets<kMT>& o, int64_t ic0, const XRegs<kMT>& r,
                                         float* lx) {
+    constexpr int HPOS = Geo<kMT>::HPOS;
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int q = 0; q < X_POS_PER_THREAD; ++q) {
+        for (int q = 0; q < Geo<kMT>::XQ; ++q) {
             const int pos = threadIdx.x + q * kThreads;
             f32x4 v;
 #pragma unroll
@@ -235,35 +252,36 @@ struct NoSideWork {
 // loads are issued and before its MFMAs: work placed there (stores that do
 // not depend on the result) overlaps the matrix-core work.  It must not touch
 // the operand LDS.
-template <int kMode, class Side = NoSideWork>
-__device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* lds, f32x16 (&acc)[2][2],
+template <int kMode, int kMT, class Side = NoSideWork>
+__device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* lds, f32x16 (&acc)[kMT][2],
                                          const Side& side = Side()) {
+    constexpr int HPOS = Geo<kMT>::HPOS;
     float* lx = lds;
-    float* lw0 = lds + LDS_X;
+    float* lw0 = lds + Geo<kMT>::LDS_X;
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int h = lane >> 5;
     const int r = lane & 31;
     // this lane's A-operand voxel in each M tile (tile-relative), see header
     const int wx = (wv & 1) * 16, wy = (wv >> 1) * 2;
-    int abase[2];
+    int abase[kMT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < kMT; ++mt) {
         const int x = (r & 15) + wx, y = (r >> 4) + wy, z = mt;
         abase[mt] = (h * HPOS + (z * HH + y) * HW + x) * 4;
     }
     const int bbase = (h * 32 + r) * 4;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 
     const int64_t nchunks = ceil_div(a.Cin, ICC);
-    const XOffsets xo = x_offsets(a, t);
+    const XOffsets<kMT> xo = x_offsets<kMT>(a, t);
     {
-        XRegs xr;
+        XRegs<kMT> xr;
         WRegs wr;
         load_x(a, t, xo, 0, xr);
         load_w<kMode>(a, t, 0, 0, wr);
@@ -279,7 +297,7 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
             const int64_t nc = kd < 2 ? c : c + 1;  // chunk and kd plane of the next unit
             const int nkd = kd < 2 ? kd + 1 : 0;
             WRegs wr;
-            XRegs xr;
+            XRegs<kMT> xr;
             if (!last_unit) load_w<kMode>(a, t, nc * ICC, nkd, wr);
             if (kd == 2 && !last_unit) load_x(a, t, xo, nc * ICC, xr);
             side(c * 3 + kd, nchunks * 3);
@@ -290,16 +308,16 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
                 for (int kw = 0; kw < 3; ++kw) {
                     const int t9 = kh * 3 + kw;
                     const int xoff = ((kd * HH + kh) * HW + kw) * 4;
-                    f32x4 av[2], bv[2];
+                    f32x4 av[kMT], bv[2];
 #pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) av[mt] = *reinterpret_cast<const f32x4*>(lx + abase[mt] + xoff);
+                    for (int mt = 0; mt < kMT; ++mt) av[mt] = *reinterpret_cast<const f32x4*>(lx + abase[mt] + xoff);
 #pragma unroll
                     for (int nt = 0; nt < 2; ++nt)
                         bv[nt] = *reinterpret_cast<const f32x4*>(lw + bbase + t9 * WTAP + nt * 256);
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
 #pragma unroll
-                        for (int mt = 0; mt < 2; ++mt)
+                        for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
                             for (int nt = 0; nt < 2; ++nt)
                                 acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mt][s], bv[nt][s],

@@ -21,8 +21,10 @@ namespace {
 
 using namespace mfma333;
 
+constexpr int kMT = 2;                    // tile depth: the result staging below must fit in LDS
+constexpr int TD = Geo<kMT>::TD;
 constexpr int kStage = TD * TH * TW + 1;  // LDS floats per channel of the result staging (padded)
-static_assert(OCB * kStage <= LDS_FLOATS, "result staging fits the kernel's LDS");
+constexpr int kLdsFloats = Geo<kMT>::LDS_MAIN > OCB * kStage ? Geo<kMT>::LDS_MAIN : OCB * kStage;
 
 // n / d for 0 <= n, d < 2^22 from a float reciprocal: the rounded product is
 // within 1/2 of n / d, so its truncation is off by at most one, which one
@@ -176,9 +178,9 @@ struct BiasSideWork {
 // destination voxel with an even coordinate holds the bias.
 template <int kMode, int kLattice>
 __global__ __launch_bounds__(kThreads) void conv333_store_kernel(Args a) {
-    __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
+    __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
     __shared__ float sbias[OCB];
-    const Tile t = tile_of(a);
+    const Tile t = tile_of<kMT>(a);
     if (threadIdx.x < OCB)
         sbias[threadIdx.x] = (a.bias && t.oc0 + threadIdx.x < a.Cout) ? a.bias[t.oc0 + threadIdx.x] : 0.f;
     // (the mainloop's first barrier publishes sbias)
@@ -209,20 +211,20 @@ __global__ __launch_bounds__(kThreads) void conv333_store_kernel(Args a) {
         b.div_bw = Div(b.bw);
     }
 
-    f32x16 acc[2][2];
+    f32x16 acc[kMT][2];
     if (kLattice == 2) {
         const RunSet even_planes = make_runs(b, 0, 2, 0, 1, b.full_rows);
         const RunSet even_rows = make_runs(b, 1, 2, 0, 2, false);
-        mainloop<kMode>(a, t, lds, acc, BiasSideWork{&b, &even_planes, &even_rows, sbias});
+        mainloop<kMode, kMT>(a, t, lds, acc, BiasSideWork{&b, &even_planes, &even_rows, sbias});
     } else {
-        mainloop<kMode>(a, t, lds, acc);
+        mainloop<kMode, kMT>(a, t, lds, acc);
     }
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     __syncthreads();  // every wave is done reading the operand tiles
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll

@@ -21,16 +21,17 @@ namespace {
 
 using namespace mfma333;
 
-__global__ __launch_bounds__(kThreads) void conv_pool_lse_mfma_kernel(Args a) {
-    __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
-    const Tile t = tile_of(a);
-    f32x16 acc[2][2];
-    mainloop<kConvWeights>(a, t, lds, acc);
+constexpr int kMT = 4;  // tile depth: two pooled planes per tile
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv_pool_lse_mfma_kernel(Args a) {
+    __shared__ __attribute__((aligned(16))) float lds[Geo<kMT>::LDS_MAIN];
+    const Tile t = tile_of<kMT>(a);
+    f32x16 acc[kMT][2];
+    mainloop<kConvWeights, kMT>(a, t, lds, acc);
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int h = lane >> 5;
-    const int64_t j0 = t.d0 >> 1;
     const int64_t j1 = (t.h0 >> 1) + (wv >> 1);
     float bias_v[2];
     bool valid[2];
@@ -40,34 +41,39 @@ __global__ __launch_bounds__(kThreads) void conv_pool_lse_mfma_kernel(Args a) {
         valid[nt] = oc < a.Cout;
         bias_v[nt] = (a.bias && valid[nt]) ? a.bias[oc] : 0.f;
     }
-    // window q = 2*(a%2) + b/2 holds registers {a%2 + 2*ay, ...}: x = 8(a%2) + 4h + b,
-    // y = a/2 in {0,1}, z = mt in {0,1}; see acc_voxel in conv333_mfma.h
+    // pooled plane pd takes M tiles (D planes) 2pd and 2pd + 1.  Window
+    // q = 2*(a%2) + b/2 holds registers {a%2 + 2*ay, ...}: x = 8(a%2) + 4h + b,
+    // y = a/2 in {0,1}; see acc_voxel in conv333_mfma.h
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int ax = q >> 1, bx = (q & 1) * 2;
-        float m[2];
+    for (int pd = 0; pd < kMT / 2; ++pd) {
+        const int64_t j0 = (t.d0 >> 1) + pd;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            float v = -FLT_MAX;
+        for (int q = 0; q < 4; ++q) {
+            const int ax = q >> 1, bx = (q & 1) * 2;
+            float m[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int nt = 0; nt < 2; ++nt) {
+                float v = -FLT_MAX;
 #pragma unroll
-                for (int ay = 0; ay < 2; ++ay)
+                for (int mt = 2 * pd; mt < 2 * pd + 2; ++mt)
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) v = fmaxf(v, acc[mt][nt][(2 * ay + ax) * 4 + bx + u]);
-            m[nt] = valid[nt] ? v + bias_v[nt] : -FLT_MAX;
-        }
-        float M = fmaxf(m[0], m[1]);
+                    for (int ay = 0; ay < 2; ++ay)
 #pragma unroll
-        for (int off = 16; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-        float S = expf(m[0] - M) + expf(m[1] - M);
+                        for (int u = 0; u < 2; ++u) v = fmaxf(v, acc[mt][nt][(2 * ay + ax) * 4 + bx + u]);
+                m[nt] = valid[nt] ? v + bias_v[nt] : -FLT_MAX;
+            }
+            float M = fmaxf(m[0], m[1]);
 #pragma unroll
-        for (int off = 16; off > 0; off >>= 1) S += __shfl_xor(S, off, 64);
-        const float L = M + logf(S);
-        if ((lane & 31) == 0) {
-            const int64_t j2 = (t.w0 >> 1) + (wv & 1) * 8 + 4 * ax + 2 * h + (q & 1);
-            if (j0 < a.P[0] && j1 < a.P[1] && j2 < a.P[2])
-                a.y[((t.n * a.P[0] + j0) * a.P[1] + j1) * a.P[2] + j2] = L > 0.f ? L : 0.f;
+            for (int off = 16; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+            float S = expf(m[0] - M) + expf(m[1] - M);
+#pragma unroll
+            for (int off = 16; off > 0; off >>= 1) S += __shfl_xor(S, off, 64);
+            const float L = M + logf(S);
+            if ((lane & 31) == 0) {
+                const int64_t j2 = (t.w0 >> 1) + (wv & 1) * 8 + 4 * ax + 2 * h + (q & 1);
+                if (j0 < a.P[0] && j1 < a.P[1] && j2 < a.P[2])
+                    a.y[((t.n * a.P[0] + j0) * a.P[1] + j1) * a.P[2] + j2] = L > 0.f ? L : 0.f;
+            }
         }
     }
 }
@@ -100,7 +106,7 @@ hipError_t launch_conv_pool_lse_mfma(const float* x, const float* w, const float
     }
     a.pad = g.p[0];
     // only tiles holding at least one complete pooling window are needed
-    a.tiles[0] = (int32_t)ceil_div(2 * pg.P[0], TD);
+    a.tiles[0] = (int32_t)ceil_div(2 * pg.P[0], Geo<kMT>::TD);
     a.tiles[1] = (int32_t)ceil_div(2 * pg.P[1], TH);
     a.tiles[2] = (int32_t)ceil_div(2 * pg.P[2], TW);
     a.oc_blocks = 1;
