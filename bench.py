@@ -77,8 +77,8 @@ def work(wl, out_shape_conv):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=4.0, help="target oracle seconds per workload sample")
     ap.add_argument("--only", default=",".join(BENCH_KEYS), help="comma-separated subset (profiling runs)")
@@ -174,7 +174,10 @@ def main():
         avg = float(np.mean(ms))
         flop = 2.0 * r["mac"]
         total_flop += flop
+        p10, med, p90 = (float(v) for v in np.percentile(ms, [10, 50, 90]))
         per[key] = dict(op=r["wl"].op, ms_avg=round(avg, 5), ms_min=round(float(np.min(ms)), 5),
+                        ms_median=round(med, 5), ms_p10=round(p10, 5), ms_p90=round(p90, 5),
+                        tflops_median=round(flop / (med * 1e-3) / 1e12, 3),
                         tflops=round(flop / (avg * 1e-3) / 1e12, 3),
                         frac_fp32_peak=round(flop / (avg * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4),
                         hbm_gbs=round(r["bytes"] / (avg * 1e-3) / 1e9, 1),
