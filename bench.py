@@ -84,6 +84,9 @@ def main():
     ap.add_argument("--only", default=",".join(BENCH_KEYS), help="comma-separated subset (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--widen", action="store_true",
+                    help="instead of the step: time the transposed convs beyond the five configurations "
+                         "(per-output-phase MFMA path against the generic kernel) and print one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a design "
@@ -94,6 +97,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.widen:
+        widen(torch, args)
         return
 
     from transposed_convolution_epilogues_amd import binding as B
@@ -254,6 +260,64 @@ def calibrate_copy(torch):
     ms = e0.elapsed_time(e1) / reps
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms": round(ms, 4),
                       "gbs_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def widen(torch, args):
+    """Transposed convs beyond the five configurations: each through its
+    automatic kernel (the per-output-phase MFMA path), the c3 module also
+    through the general phase path instead of its sub-lattice kernel, and
+    each through the generic gather kernel for comparison."""
+    from transposed_convolution_epilogues_amd import binding as B
+    from transposed_convolution_epilogues_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.library()
+    cases = [(k, wl, 0) for k, wl in W.WIDEN.items()] + [("c3_phase", W.CONFIGS["c3"], 2)]
+    out = {}
+    for key, wl, variant in cases:
+        inp = W.make_inputs(wl)
+        x, w = torch.from_numpy(inp.x).to(dev), torch.from_numpy(inp.w).to(dev)
+        b = None if inp.b is None else torch.from_numpy(inp.b).to(dev)
+        p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+        oshape = B.conv_transpose3d_out_shape(wl.x_shape, wl.cout, p)
+        y = torch.empty(oshape, device=dev)
+        mac, xb, wb = work(wl, oshape)
+        nbytes = xb + wb + 4 * math.prod(oshape)
+        row = dict(workload=wl.description, mac=mac, algo_bytes=nbytes)
+        for label, v, reps in (("fast", variant, args.steps), ("generic", 1, 3)):
+            old = B.set_variant(v)
+            try:
+                row[label + "_algo"] = B.conv_transpose3d_algo(wl.x_shape, wl.cout, p)
+                fn = lambda: B.conv_transpose3d_fwd(x, w, b, wl.stride, wl.pad, wl.dilation, wl.output_pad,
+                                                    wl.groups, out=y)
+                for _ in range(2):
+                    fn()
+                torch.cuda.synchronize()
+                ms = []
+                stream = torch.cuda.current_stream()
+                for _ in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                    ms.append((e0, e1))
+                torch.cuda.synchronize()
+                t = float(np.median([a.elapsed_time(c) for a, c in ms]))
+            finally:
+                B.set_variant(old)
+            row[label + "_ms_median"] = round(t, 5)
+            row[label + "_tflops"] = round(2.0 * mac / (t * 1e-3) / 1e12, 3)
+        row["frac_fp32_peak"] = round(row["fast_tflops"] / FP32_PEAK_TFLOPS, 4)
+        row["hbm_gbs"] = round(nbytes / (row["fast_ms_median"] * 1e-3) / 1e9, 1)
+        row["frac_hbm_peak"] = round(row["hbm_gbs"] / HBM_PEAK_GBS, 4)
+        row["speedup_vs_generic"] = round(row["generic_ms_median"] / row["fast_ms_median"], 2)
+        out[key] = row
+        print(f"[bench --widen] {key}: {row}", file=sys.stderr, flush=True)
+        del x, w, b, y
+    print(json.dumps({"metric": "effective TFLOP/s (2*valid-tap MACs/time), transposed convs beyond the configs",
+                      "unit": "TFLOP/s", "dtype": "f32", "data": "synthetic", "steps": args.steps,
+                      "widen": out}), flush=True)
 
 
 def cpu_baseline(runs, seconds_per_workload):

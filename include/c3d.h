@@ -156,9 +156,33 @@ int conv_maxpool_lse_relu(const float* x, const int64_t x_shape[5], const float*
 const char* c3d_status_string(int status);
 
 /* Kernel-variant override for A/B tests: 0 = automatic (default), 1 = force
- * the generic direct kernels.  Returns the previous value.  Process-wide;
- * not for concurrent use with different settings. */
+ * the generic direct kernels, 2 = skip the shape-specialised kernels (the
+ * flattened-row conv for (k,k,1) kernels and the stride-2/dilation-2
+ * sub-lattice transposed conv) so that the general MFMA paths run where
+ * they apply.  Returns the previous value.  Process-wide; not for
+ * concurrent use with different settings. */
 int c3d_set_variant(int variant);
+
+/* Kernel a call would use (under the current variant), for tests and
+ * tuning; host-only, launches nothing. */
+enum {
+    C3D_ALGO_DIRECT = 0,     /* generic one-thread-per-output fp32 kernel              */
+    C3D_ALGO_K1LAST = 1,     /* conv3d, (k,k,1) kernel: flattened-row MFMA GEMM        */
+    C3D_ALGO_MFMA333 = 2,    /* conv3d, 3x3x3 stride 1: MFMA implicit GEMM             */
+    C3D_ALGO_SUBLATTICE = 3, /* conv_transpose3d, k3 s2 p1 d2: odd sub-lattice on MFMA */
+    C3D_ALGO_PHASE = 4       /* conv_transpose3d, strided: per-output-phase MFMA GEMM  */
+};
+
+/* Writes the C3D_ALGO_* code conv3d_fwd would use to *algo; returns the
+ * validation status conv3d_fwd would return (nothing is written on error). */
+int c3d_conv3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo);
+
+/* The same for conv_transpose3d_fwd.  The phase path ("Kimi-K2.6 l1_p77",
+ * the residue classes of o mod s, each a stride-1 correlation with its own
+ * taps) applies when every stride is at most 4, every residue class has at
+ * most 3 taps per dim whose input offsets span at most 3 positions, and
+ * Cin/groups >= 4, Cout/groups >= 8. */
+int c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo);
 
 #ifdef __cplusplus
 }

@@ -152,3 +152,46 @@ def test_binding_rejects_cpu_tensors():
     w = torch.zeros(8, 4, 3, 3, 3)
     with pytest.raises(TypeError):
         B.conv3d_fwd(x, w, None, 1, 1, out=torch.zeros(1, 8, 8, 8, 8))
+
+
+# ----------------------------------------------------------- kernel choice
+ALGO_CASES = [
+    # (op, x_shape, cout, kernel, stride, pad, dilation, output_pad, groups, variant, expected)
+    ("conv3d", (16, 3, 256, 256, 10), 64, (3, 3, 1), 1, 0, 1, 0, 1, 0, "k1last"),       # c2
+    ("conv3d", (1, 4, 8, 8, 8), 8, 3, 1, 1, 1, 0, 1, 0, "mfma333"),                     # c1
+    ("conv3d", (1, 2, 8, 8, 8), 8, 3, 1, 1, 1, 0, 1, 0, "direct"),                      # too few channels
+    ("conv3d", (1, 8, 8, 8, 8), 8, 3, 2, 1, 1, 0, 1, 0, "direct"),                      # strided
+    ("conv3d", (16, 3, 256, 256, 10), 64, (3, 3, 1), 1, 0, 1, 0, 1, 1, "direct"),       # forced generic
+    ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 0, "sublattice"),  # c3
+    ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 2, "phase"),       # c3, general path
+    ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 1, "direct"),
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 2, 1, 1, 1, 1, 0, "phase"),           # dense phases
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 4, 2, 1, 1, 0, 1, 0, "phase"),
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 3, 1, 1, 2, 2, 0, "phase"),           # s3, groups
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 1, 1, 1, 0, 1, 0, "phase"),           # stride 1
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 5, 1, 1, 0, 1, 0, "direct"),          # stride > 4
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 7, 2, 1, 1, 0, 1, 0, "direct"),          # 4 taps per residue
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 1, 1, 2, 0, 1, 0, "direct"),          # offsets span 4
+    ("conv_transpose3d", (2, 3, 8, 8, 8), 32, 3, 2, 1, 1, 0, 1, 0, "direct"),           # Cin/groups < 4
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 4, 3, 2, 1, 1, 0, 1, 0, "direct"),           # Cout/groups < 8
+]
+
+
+@pytest.mark.parametrize("case", ALGO_CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(ALGO_CASES)])
+def test_kernel_choice(case):
+    op, xs, cout, k, s, p, d, op_, g, variant, expected = case
+    params = B.make_params(k, s, p, d, op_, g)
+    old = B.set_variant(variant)
+    try:
+        got = (B.conv3d_algo if op == "conv3d" else B.conv_transpose3d_algo)(xs, cout, params)
+    finally:
+        B.set_variant(old)
+    assert got == expected
+
+
+def test_kernel_choice_rejects_invalid_arguments():
+    with pytest.raises(B.C3DError):
+        B.conv_transpose3d_algo((1, 4, 4, 4, 4), 8, B.make_params(3, 2, 1, 1, 2))  # output_pad >= stride
+    lib = B.library()
+    xs = (ctypes.c_int64 * 5)(1, 4, 4, 4, 4)
+    assert lib.c3d_conv3d_algo(xs, 8, ctypes.byref(B.make_params(3)), None) == 1  # C3D_ERR_NULL

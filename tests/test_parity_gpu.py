@@ -124,6 +124,88 @@ def test_random_small_shapes(op, variant):
         check_full(wl, inp, f"{op}#{i}")
 
 
+# ------------------------------------- transposed conv, per-phase MFMA path
+def _phase_cases(n, seed):
+    """Random transposed convs that take the per-phase MFMA kernel: strides
+    1..4, kernels 1..5, dilation 1..3, output padding, groups 1/2."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        groups = int(rng.choice([1, 2]))
+        wl = W.make("phase", "conv_transpose3d",
+                    (int(rng.integers(1, 3)), groups * int(rng.integers(4, 13))) +
+                    tuple(int(a) for a in rng.integers(1, 10, size=3)),
+                    groups * int(rng.integers(8, 41)), tuple(int(a) for a in rng.integers(1, 6, size=3)),
+                    tuple(int(a) for a in rng.integers(1, 5, size=3)), tuple(int(a) for a in rng.integers(0, 4, size=3)),
+                    tuple(int(a) for a in rng.integers(1, 4, size=3)), (0, 0, 0), groups, bool(rng.integers(0, 2)),
+                    seed=int(rng.integers(0, 2**31)))
+        wl = wl.with_(output_pad=tuple(int(rng.integers(0, max(si, di))) for si, di in zip(wl.stride, wl.dilation)))
+        if not _valid(wl):
+            continue
+        if B.conv_transpose3d_algo(wl.x_shape, wl.cout, B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation,
+                                                                      wl.output_pad, wl.groups)) != "phase":
+            continue
+        out.append(wl)
+    return out
+
+
+def test_convT_phase_random():
+    for i, wl in enumerate(_phase_cases(30, 71)):
+        print(f"[convT phase] case {i}: {wl}", flush=True)
+        check_full(wl, W.make_inputs(wl), f"convT phase #{i}")
+
+
+PHASE_MEDIUM = {
+    # dense phases (every residue has taps), ragged tiles in every dim
+    "k3s2p1d1_op1": W.make("pm", "conv_transpose3d", (2, 16, 5, 9, 37), 40, 3, 2, 1, 1, 1, seed=81),
+    "k4s2p1": W.make("pm", "conv_transpose3d", (1, 12, 4, 7, 33), 24, 4, 2, 1, seed=82),
+    "k3s3p1_op2_groups2": W.make("pm", "conv_transpose3d", (2, 16, 3, 5, 13), 32, 3, 3, 1, 1, 2, groups=2,
+                                 bias=True, seed=83),
+    "k3s1p1": W.make("pm", "conv_transpose3d", (1, 8, 4, 6, 40), 16, 3, 1, 1, bias=True, seed=84),
+    "mixed": W.make("pm", "conv_transpose3d", (1, 10, 5, 6, 20), 72, (3, 2, 5), (2, 1, 3), (1, 0, 2), (1, 2, 1),
+                    (1, 0, 0), bias=True, seed=85),
+    # the stride-2 dilation-2 module of the transposed-conv workload, reduced
+    "k3s2p1d2": W.CONFIGS["c3"].with_(x_shape=(2, 32, 5, 7, 19)),
+}
+
+
+@pytest.mark.parametrize("name", list(PHASE_MEDIUM))
+def test_convT_phase_medium(name):
+    """Per-phase MFMA path on multi-tile shapes; variant 2 makes the
+    stride-2 dilation-2 case take it instead of the sub-lattice kernel."""
+    wl = PHASE_MEDIUM[name]
+    old = B.set_variant(2)
+    try:
+        algo = B.conv_transpose3d_algo(wl.x_shape, wl.cout, B.make_params(wl.kernel, wl.stride, wl.pad,
+                                                                           wl.dilation, wl.output_pad, wl.groups))
+        assert algo == "phase", algo
+        print(f"[convT phase medium {name}] {wl}", flush=True)
+        check_full(wl, W.make_inputs(wl), name)
+    finally:
+        B.set_variant(old)
+
+
+@pytest.mark.parametrize("key", list(W.WIDEN))
+def test_convT_widen_full_size_sampled(key):
+    """The transposed convs `bench.py --widen` times, at full size through the
+    automatic kernel (the per-phase path), on sampled outputs."""
+    wl = W.WIDEN[key]
+    p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+    assert B.conv_transpose3d_algo(wl.x_shape, wl.cout, p) == "phase"
+    inp = W.make_inputs(wl)
+    print(f"[convT widen {key}] {wl}", flush=True)
+    y = run_gpu(wl, inp)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any().item()
+    flat = np.concatenate([_sample(y.numel(), 40_000, 91), np.arange(0, 300), y.numel() - 1 - np.arange(300)])
+    got = y.view(-1)[torch.from_numpy(flat).cuda()].cpu().numpy()
+    ref = O.conv_transpose3d_at(inp.x, inp.w, flat, inp.b, wl.stride, wl.pad, wl.dilation, wl.output_pad,
+                                wl.groups)
+    assert_close(f"widen {key} sampled", got, ref)
+    y2 = run_gpu(wl, inp)
+    assert torch.equal(y, y2)
+
+
 # ----------------------------------------------- medium shapes (many tiles)
 MEDIUM = {
     # the fast paths' shapes, reduced so the oracle finishes in seconds, with ragged tails

@@ -25,7 +25,9 @@ STATUS = {0: "C3D_OK", 1: "C3D_ERR_NULL", 2: "C3D_ERR_SHAPE", 3: "C3D_ERR_PARAM"
 EXPORTS = ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_bn_avgpool_out_shape",
            "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
            "convT_bn_avgpool_workspace_bytes", "convT_bn_avgpool", "conv_maxpool_lse_relu", "c3d_status_string",
-           "c3d_set_variant")
+           "c3d_set_variant", "c3d_conv3d_algo", "c3d_conv_transpose3d_algo")
+
+ALGO = {0: "direct", 1: "k1last", 2: "mfma333", 3: "sublattice", 4: "phase"}
 
 
 class C3DError(RuntimeError):
@@ -93,9 +95,13 @@ def _lib():
     lib.c3d_status_string.argtypes = [ctypes.c_int]
     lib.c3d_status_string.restype = ctypes.c_char_p
     lib.c3d_set_variant.argtypes = [ctypes.c_int]
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.c3d_conv3d_algo.argtypes = [i64p, i64, P, i32p]
+    lib.c3d_conv_transpose3d_algo.argtypes = [i64p, i64, P, i32p]
     for name in ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_bn_avgpool_out_shape",
                  "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
-                 "convT_bn_avgpool", "conv_maxpool_lse_relu", "c3d_set_variant"):
+                 "convT_bn_avgpool", "conv_maxpool_lse_relu", "c3d_set_variant", "c3d_conv3d_algo",
+                 "c3d_conv_transpose3d_algo"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -138,8 +144,25 @@ def _check(st: int, where: str):
 
 
 def set_variant(variant: int) -> int:
-    """0 = automatic kernel choice, 1 = force the generic direct kernels."""
+    """0 = automatic kernel choice, 1 = force the generic direct kernels,
+    2 = skip the shape-specialised kernels (general MFMA paths where they apply)."""
     return int(_lib().c3d_set_variant(int(variant)))
+
+
+def conv3d_algo(x_shape, cout: int, params: ConvParams) -> str:
+    """Name of the kernel conv3d_fwd would run for these arguments (host-only query)."""
+    v = ctypes.c_int32(-1)
+    _check(_lib().c3d_conv3d_algo(_shape5(x_shape), int(cout), ctypes.byref(params), ctypes.byref(v)),
+           "c3d_conv3d_algo")
+    return ALGO[v.value]
+
+
+def conv_transpose3d_algo(x_shape, cout: int, params: ConvParams) -> str:
+    """Name of the kernel conv_transpose3d_fwd would run for these arguments (host-only query)."""
+    v = ctypes.c_int32(-1)
+    _check(_lib().c3d_conv_transpose3d_algo(_shape5(x_shape), int(cout), ctypes.byref(params), ctypes.byref(v)),
+           "c3d_conv_transpose3d_algo")
+    return ALGO[v.value]
 
 
 def conv3d_out_shape(x_shape, cout: int, params: ConvParams) -> Tuple[int, ...]:

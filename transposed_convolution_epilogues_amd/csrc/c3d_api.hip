@@ -89,6 +89,26 @@ int resolve_pool(const Geom& g, int32_t pool, PoolGeom* pg) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? C3D_OK : C3D_ERR_HIP; }
 
+// Kernel choice (the C3D_ALGO_* codes of c3d.h).  Variant 1 forces the
+// generic kernels; variant 2 skips the shape-specialised ones (c2's
+// flattened-row conv, c3's sub-lattice transposed conv) so the general fast
+// paths can be compared with them.
+int conv3d_algo(const Geom& g) {
+    const int v = g_variant.load();
+    if (v == 1) return C3D_ALGO_DIRECT;
+    if (v == 0 && c3d::conv_k1last_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_K1LAST;
+    if (c3d::conv3x3x3_mfma_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_MFMA333;
+    return C3D_ALGO_DIRECT;
+}
+
+int convT_algo(const Geom& g) {
+    const int v = g_variant.load();
+    if (v == 1) return C3D_ALGO_DIRECT;
+    if (v == 0 && c3d::convT_s2_sublattice_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_SUBLATTICE;
+    if (c3d::convT_phase_mfma_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_PHASE;
+    return C3D_ALGO_DIRECT;
+}
+
 void write_shape(const Geom& g, int64_t ys[5]) {
     ys[0] = g.N;
     ys[1] = g.Cout;
@@ -173,12 +193,11 @@ int conv3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t
     int st = resolve(x_shape, cout, p, false, &g);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (g_variant.load() == 0) {
-        if (c3d::conv_k1last_supported(g, x, w, y)) return hip_status(c3d::launch_conv_k1last(x, w, bias, y, g, s));
-        if (c3d::conv3x3x3_mfma_supported(g, x, w, y))
-            return hip_status(c3d::launch_conv3x3x3_mfma(x, w, bias, y, g, s));
+    switch (conv3d_algo(g)) {
+        case C3D_ALGO_K1LAST: return hip_status(c3d::launch_conv_k1last(x, w, bias, y, g, s));
+        case C3D_ALGO_MFMA333: return hip_status(c3d::launch_conv3x3x3_mfma(x, w, bias, y, g, s));
+        default: return hip_status(c3d::launch_conv3d_direct(x, w, bias, y, g, s));
     }
-    return hip_status(c3d::launch_conv3d_direct(x, w, bias, y, g, s));
 }
 
 int conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
@@ -189,9 +208,29 @@ int conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const float* 
     int st = resolve(x_shape, cout, p, true, &g);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (g_variant.load() == 0 && c3d::convT_s2_sublattice_supported(g, x, w, y))
-        return hip_status(c3d::launch_convT_s2_sublattice(x, w, bias, y, g, s));
-    return hip_status(c3d::launch_convT_gather(x, w, bias, y, g, s));
+    switch (convT_algo(g)) {
+        case C3D_ALGO_SUBLATTICE: return hip_status(c3d::launch_convT_s2_sublattice(x, w, bias, y, g, s));
+        case C3D_ALGO_PHASE: return hip_status(c3d::launch_convT_phase_mfma(x, w, bias, y, g, s));
+        default: return hip_status(c3d::launch_convT_gather(x, w, bias, y, g, s));
+    }
+}
+
+int c3d_conv3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo) {
+    if (!algo) return C3D_ERR_NULL;
+    Geom g;
+    const int st = resolve(x_shape, cout, p, false, &g);
+    if (st) return st;
+    *algo = conv3d_algo(g);
+    return C3D_OK;
+}
+
+int c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo) {
+    if (!algo) return C3D_ERR_NULL;
+    Geom g;
+    const int st = resolve(x_shape, cout, p, true, &g);
+    if (st) return st;
+    *algo = convT_algo(g);
+    return C3D_OK;
 }
 
 size_t convT_bn_avgpool_workspace_bytes(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,

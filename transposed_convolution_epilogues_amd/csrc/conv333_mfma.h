@@ -86,9 +86,10 @@ struct Args {
     const float* bias;
     float* y;
     int64_t N, Cin, Cout;
+    int64_t xC;     // channels per sample of x (Cin, or more when x holds several groups)
     int64_t S[3];   // input dims
     int64_t O[3];   // conv output dims (stride 1)
-    int32_t pad;    // same padding on all dims
+    int32_t pad[3];  // halo origin = tile origin - pad, per dim
     int32_t tiles[3];  // tiles per dim (D, H, W)
     int32_t oc_blocks;
     int64_t P[3];   // pooled dims (fused pooling epilogue)
@@ -141,7 +142,7 @@ struct XOffsets {
 };
 
 template <int kMT>
-__device__ __forceinline__ XOffsets<kMT> x_offsets(const Args& a, const Tile& t) {
+__device__ __forceinline__ XOffsets<kMT> x_offsets(const Args& a, const Tile& t, const int32_t (&pad)[3]) {
     constexpr int HPOS = Geo<kMT>::HPOS;
     XOffsets<kMT> o;
 #pragma unroll
@@ -150,7 +151,7 @@ __device__ __forceinline__ XOffsets<kMT> x_offsets(const Args& a, const Tile& t)
         const int pw = pos % HW;
         const int ph = (pos / HW) % HH;
         const int pd = pos / (HW * HH);
-        const int64_t gd = t.d0 - a.pad + pd, gh = t.h0 - a.pad + ph, gw = t.w0 - a.pad + pw;
+        const int64_t gd = t.d0 - pad[0] + pd, gh = t.h0 - pad[1] + ph, gw = t.w0 - pad[2] + pw;
         const bool inb = pos < HPOS && gd >= 0 && gd < a.S[0] && gh >= 0 && gh < a.S[1] && gw >= 0 &&
                          gw < a.S[2];
         o.off[q] = inb ? (int32_t)((gd * a.S[1] + gh) * a.S[2] + gw) : -1;
@@ -172,7 +173,7 @@ __device__ __forceinline__ void load_x(const Args& a, const Tile& t, const XOffs
         for (int j = 0; j < 4; ++j) {
             const int64_t ic = ic0 + 4 * g + j;
             const bool icok = ic < a.Cin;
-            const float* xc = a.x + (t.n * a.Cin + (icok ? ic : 0)) * plane;  // wave-uniform
+            const float* xc = a.x + (t.n * a.xC + (icok ? ic : 0)) * plane;  // wave-uniform
 #pragma unroll
             for (int q = 0; q < Geo<kMT>::XQ; ++q) r.v[g][q][j] = xc[o.off[q] >= 0 ? o.off[q] : 0];
         }
@@ -279,7 +280,7 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
             for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 
     const int64_t nchunks = ceil_div(a.Cin, ICC);
-    const XOffsets<kMT> xo = x_offsets<kMT>(a, t);
+    const XOffsets<kMT> xo = x_offsets<kMT>(a, t, a.pad);
     {
         XRegs<kMT> xr;
         WRegs wr;
@@ -331,6 +332,152 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
             // the other weight buffer was last read by the previous unit, which
             // every wave finished before the previous barrier
             store_w<kMode>(a, t, nc * ICC, wr, lw0 + (buf ^ 1) * LDS_W);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tap-table variant of the K loop.  The taps are the product of three per-dim
+// lists (tap i of dim j: kernel index k[i], halo offset off[i] in 0..2, at
+// most 3 taps per dim), so a weight unit is one entry of the dim-0 list with
+// its n1 x n2 <= 9 taps, and the K loop runs (input-channel chunks) x n0
+// units.  Weights are read in the transposed layout w[ic][oc][kvol] with
+// kvol index (k0 * K1 + k1) * K2 + k2.  Used by the transposed-conv phase
+// kernel: each output phase of a strided transposed conv sees such a
+// product of per-dim tap lists.
+struct DimTaps {
+    int32_t n;       // taps in this dim (1..3)
+    int32_t k[3];    // kernel index of tap i
+    int32_t off[3];  // halo offset of tap i
+};
+
+struct TapSet {
+    DimTaps d[3];
+    int32_t K1, K2, Kvol;  // kernel extents of dims 1 and 2, kernel volume
+};
+
+__device__ __forceinline__ int32_t pick3(const int32_t (&v)[3], int i) {
+    return i == 0 ? v[0] : (i == 1 ? v[1] : v[2]);
+}
+
+// dims-1/2 part of unit slot u: weight index and halo offset (floats)
+struct SlotTaps {
+    int32_t wk[UNIT_TAPS];
+    int32_t xo[UNIT_TAPS];
+};
+
+__device__ __forceinline__ SlotTaps slot_taps(const TapSet& ts) {
+    SlotTaps st;
+    const int n2 = ts.d[2].n;
+#pragma unroll
+    for (int u = 0; u < UNIT_TAPS; ++u) {
+        const int i1 = n2 == 1 ? u : (n2 == 2 ? u >> 1 : u / 3);
+        const int i2 = u - i1 * n2;
+        st.wk[u] = pick3(ts.d[1].k, i1) * ts.K2 + pick3(ts.d[2].k, i2);
+        st.xo[u] = (pick3(ts.d[1].off, i1) * HW + pick3(ts.d[2].off, i2)) * 4;
+    }
+    return st;
+}
+
+__device__ __forceinline__ void load_w_taps(const Args& a, const Tile& t, const TapSet& ts, const SlotTaps& st,
+                                            int64_t ic0, int i0, WRegs& r) {
+    const int ntu = ts.d[1].n * ts.d[2].n;
+    const int wk0 = pick3(ts.d[0].k, i0) * ts.K1 * ts.K2;
+#pragma unroll
+    for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) {
+        const int p = threadIdx.x + q * kThreads;
+        const int oc = p >> 3, j = p & 7;
+        const int64_t goc = t.oc0 + oc, gic = ic0 + j;
+        const bool ok = goc < a.Cout && gic < a.Cin;
+        const float* src = a.w + (ok ? (gic * a.Cout + goc) * ts.Kvol + wk0 : 0);
+#pragma unroll
+        for (int u = 0; u < UNIT_TAPS; ++u) r.v[q][u] = u < ntu ? src[ok ? st.wk[u] : 0] : 0.f;
+    }
+}
+
+template <int kMT>
+__device__ __forceinline__ void mainloop_taps(const Args& a, const Tile& t, const TapSet& ts,
+                                              const int32_t (&pad)[3], float* lds, f32x16 (&acc)[kMT][2]) {
+    constexpr int HPOS = Geo<kMT>::HPOS;
+    float* lx = lds;
+    float* lw0 = lds + Geo<kMT>::LDS_X;
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int h = lane >> 5;
+    const int r = lane & 31;
+    const int wx = (wv & 1) * 16, wy = (wv >> 1) * 2;
+    int abase[kMT];
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+        const int x = (r & 15) + wx, y = (r >> 4) + wy, z = mt;
+        abase[mt] = (h * HPOS + (z * HH + y) * HW + x) * 4;
+    }
+    const int bbase = (h * 32 + r) * 4;
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
+
+    const int n0 = ts.d[0].n;
+    const int ntu = ts.d[1].n * ts.d[2].n;
+    const SlotTaps st = slot_taps(ts);
+    const int64_t nchunks = ceil_div(a.Cin, ICC);
+    const XOffsets<kMT> xo = x_offsets<kMT>(a, t, pad);
+    {
+        XRegs<kMT> xr;
+        WRegs wr;
+        load_x(a, t, xo, 0, xr);
+        load_w_taps(a, t, ts, st, 0, 0, wr);
+        store_x(a, xo, 0, xr, lx);
+        store_w<kConvWeights>(a, t, 0, wr, lw0);
+        __syncthreads();
+    }
+    int buf = 0;
+    for (int64_t c = 0; c < nchunks; ++c) {
+#pragma unroll 1
+        for (int i0 = 0; i0 < n0; ++i0) {
+            const bool chunk_end = i0 == n0 - 1;
+            const bool last_unit = c == nchunks - 1 && chunk_end;
+            const int64_t nc = chunk_end ? c + 1 : c;  // chunk and dim-0 tap of the next unit
+            const int ni0 = chunk_end ? 0 : i0 + 1;
+            WRegs wr;
+            XRegs<kMT> xr;
+            if (!last_unit) load_w_taps(a, t, ts, st, nc * ICC, ni0, wr);
+            if (chunk_end && !last_unit) load_x(a, t, xo, nc * ICC, xr);
+            const float* lw = lw0 + buf * LDS_W;
+            const int xo0 = pick3(ts.d[0].off, i0) * HH * HW * 4;
+#pragma unroll
+            for (int u = 0; u < UNIT_TAPS; ++u) {
+                if (u < ntu) {
+                    const int xoff = xo0 + st.xo[u];
+                    f32x4 av[kMT], bv[2];
+#pragma unroll
+                    for (int mt = 0; mt < kMT; ++mt) av[mt] = *reinterpret_cast<const f32x4*>(lx + abase[mt] + xoff);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        bv[nt] = *reinterpret_cast<const f32x4*>(lw + bbase + u * WTAP + nt * 256);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+#pragma unroll
+                        for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                            for (int nt = 0; nt < 2; ++nt)
+                                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mt][s], bv[nt][s],
+                                                                                   acc[mt][nt], 0, 0, 0);
+                }
+            }
+            if (last_unit) break;
+            if (chunk_end) {
+                __syncthreads();  // every wave is done with this chunk's halo
+                store_x(a, xo, nc * ICC, xr, lx);
+            }
+            // the other weight buffer was last read by the previous unit, which
+            // every wave finished before the previous barrier
+            store_w<kConvWeights>(a, t, nc * ICC, wr, lw0 + (buf ^ 1) * LDS_W);
             __syncthreads();
             buf ^= 1;
         }

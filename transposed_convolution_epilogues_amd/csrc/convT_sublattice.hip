@@ -250,6 +250,7 @@ Args make_args(const float* x, const float* w, const float* bias, float* y, cons
     a.y = y;
     a.N = g.N;
     a.Cin = g.Cin;
+    a.xC = g.Cin;
     a.Cout = g.Cout;
     for (int j = 0; j < 3; ++j) a.S[j] = g.S[j];
     a.oc_blocks = (int32_t)ceil_div(g.Cout, OCB);
@@ -269,7 +270,7 @@ bool conv3x3x3_mfma_supported(const Geom& g, const void*, const void*, const voi
 hipError_t launch_conv3x3x3_mfma(const float* x, const float* w, const float* bias, float* y, const Geom& g,
                                  hipStream_t st) {
     Args a = make_args(x, w, bias, y, g);
-    a.pad = g.p[0];
+    for (int j = 0; j < 3; ++j) a.pad[j] = g.p[0];
     for (int j = 0; j < 3; ++j) {
         a.O[j] = g.O[j];
         a.Y[j] = g.O[j];
@@ -293,7 +294,7 @@ bool convT_s2_sublattice_supported(const Geom& g, const void*, const void*, cons
 hipError_t launch_convT_s2_sublattice(const float* x, const float* w, const float* bias, float* y, const Geom& g,
                                       hipStream_t st) {
     Args a = make_args(x, w, bias, y, g);
-    a.pad = 1;
+    for (int j = 0; j < 3; ++j) a.pad[j] = 1;
     for (int j = 0; j < 3; ++j) {
         a.O[j] = g.S[j];  // sub-lattice grid = input grid
         a.Y[j] = g.O[j];  // destination = the transposed-conv output

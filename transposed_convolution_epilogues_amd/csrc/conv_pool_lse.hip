@@ -98,13 +98,14 @@ hipError_t launch_conv_pool_lse_mfma(const float* x, const float* w, const float
     a.y = y;
     a.N = g.N;
     a.Cin = g.Cin;
+    a.xC = g.Cin;
     a.Cout = g.Cout;
     for (int j = 0; j < 3; ++j) {
         a.S[j] = g.S[j];
         a.O[j] = g.O[j];
         a.P[j] = pg.P[j];
     }
-    a.pad = g.p[0];
+    for (int j = 0; j < 3; ++j) a.pad[j] = g.p[0];
     // only tiles holding at least one complete pooling window are needed
     a.tiles[0] = (int32_t)ceil_div(2 * pg.P[0], Geo<kMT>::TD);
     a.tiles[1] = (int32_t)ceil_div(2 * pg.P[1], TH);

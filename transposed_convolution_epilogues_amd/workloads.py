@@ -112,6 +112,20 @@ CONFIGS = {
 }
 
 
+# Transposed convs beyond the five configurations, for the per-output-phase
+# MFMA path (timed by `bench.py --widen`; reduced copies are parity cases).
+WIDEN = {
+    "t1": make("t1", "conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 1, 1, bias=True, seed=101,
+               description="ConvTranspose3d 32->64 k3 s2 p1 output_padding 1 (x2 upsampling) on "
+                           "x[16,32,16,32,32] -> [16,64,32,64,64]"),
+    "t2": make("t2", "conv_transpose3d", (8, 64, 16, 32, 32), 32, 4, 2, 1, bias=True, seed=102,
+               description="ConvTranspose3d 64->32 k4 s2 p1 on x[8,64,16,32,32] -> [8,32,32,64,64]"),
+    "t3": make("t3", "conv_transpose3d", (8, 32, 8, 16, 16), 64, 3, 3, 1, 1, 2, groups=2, bias=True, seed=103,
+               description="ConvTranspose3d 32->64 groups 2 k3 s3 p1 output_padding 2 on x[8,32,8,16,16] "
+                           "-> [8,64,24,48,48]"),
+}
+
+
 @dataclasses.dataclass
 class Inputs:
     x: np.ndarray
