@@ -62,6 +62,9 @@ def load(path: str = LIB):
         "oracle_relu": ([_f64p, i64], None),
         "oracle_convT_bn_avgpool": ([_f32p, _i64p, _f32p, i64, P, _f32p, _f32p, _f32p, ctypes.c_double,
                                      ctypes.c_int32, _f64p, _f64p, _f64p], None),
+        "oracle_convT_bn_eval_avgpool": ([_f32p, _i64p, _f32p, i64, P, _f32p, _f32p, _f32p, _f32p, _f32p,
+                                          ctypes.c_double, ctypes.c_int32, _f64p], None),
+        "oracle_bn_running_update": ([i64, ctypes.c_double, i64, _f64p, _f64p, _f64p, _f64p], None),
         "oracle_conv_maxpool_lse_relu": ([_f32p, _i64p, _f32p, i64, P, _f32p, ctypes.c_int32, _f64p], None),
         "oracle_conv_maxpool_lse_relu_at": ([_f32p, _i64p, _f32p, i64, P, _f32p, ctypes.c_int32, _i64p,
                                              i64, _f64p], None),
@@ -259,6 +262,41 @@ def convT_bn_avgpool(x, w, bias, gamma, beta, eps=1e-5, pool=4, stride=(2, 2, 2)
                                   _params(k, stride, pad, dilation, output_pad, groups), bp, gp, bep,
                                   float(eps), int(pool), out.ctypes.data, mean.ctypes.data, var.ctypes.data)
     return out, mean, var
+
+
+def convT_bn_eval_avgpool(x, w, bias, gamma, beta, running_mean, running_var, eps=1e-5, pool=4,
+                          stride=(2, 2, 2), pad=(1, 1, 1), dilation=(1, 1, 1), output_pad=(0, 0, 0), groups=1):
+    """The ConvT -> BatchNorm3d -> AvgPool module with BN in eval mode ([p72]):
+    BN normalises with the running statistics.  Returns out (float64)."""
+    x, xp = _f32(x)
+    w, wp = _f32(w)
+    b, bp = _f32(bias)
+    g, gp = _f32(gamma)
+    be, bep = _f32(beta)
+    rm, rmp = _f32(running_mean)
+    rv, rvp = _f32(running_var)
+    k = w.shape[2:]
+    cout = w.shape[1] * groups
+    ys = convT_out_shape(x.shape, cout, k, stride, pad, dilation, output_pad)
+    P = tuple(pool_out_len(ys[2 + j], pool) for j in range(3))
+    out = np.empty((x.shape[0], cout) + P, np.float64)
+    lib().oracle_convT_bn_eval_avgpool(xp, _shape(x.shape), wp, cout,
+                                       _params(k, stride, pad, dilation, output_pad, groups), bp, gp, bep, rmp, rvp,
+                                       float(eps), int(pool), out.ctypes.data)
+    return out
+
+
+def bn_running_update(running_mean, running_var, batch_mean, batch_var_biased, count, momentum=0.1):
+    """Running statistics after one training-mode forward ([p72]'s momentum;
+    the running variance tracks the unbiased batch variance).  Returns new
+    (running_mean, running_var) in float64."""
+    bm = np.ascontiguousarray(batch_mean, np.float64)
+    bv = np.ascontiguousarray(batch_var_biased, np.float64)
+    rm = np.array(running_mean, np.float64)
+    rv = np.array(running_var, np.float64)
+    lib().oracle_bn_running_update(len(rm), float(momentum), int(count), bm.ctypes.data, bv.ctypes.data,
+                                   rm.ctypes.data, rv.ctypes.data)
+    return rm, rv
 
 
 def conv_maxpool_lse_relu(x, w, bias, pool=2, stride=(1, 1, 1), pad=(1, 1, 1), dilation=(1, 1, 1), groups=1):

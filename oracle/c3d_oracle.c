@@ -426,6 +426,53 @@ void oracle_convT_bn_avgpool(const float* x, const int64_t xs[5], const float* w
     free(pooled);
 }
 
+/* The same module with BatchNorm3d in eval mode ([p72], the eval-mode
+ * kernel the page ships: BN normalises with the running statistics, an
+ * affine map per channel).  In the module's order: t = convT(x, w, bias),
+ * then u = gamma_c (t - running_mean_c) / sqrt(running_var_c + eps) + beta_c
+ * on every element, then the average pool.  out is [N, Cout, P0, P1, P2]. */
+void oracle_convT_bn_eval_avgpool(const float* x, const int64_t xs[5], const float* w, int64_t cout,
+                                  const oracle_params* P, const float* bias, const float* gamma,
+                                  const float* beta, const float* running_mean, const float* running_var,
+                                  double eps, int32_t pool, double* out) {
+    int64_t ys[5];
+    convT_dims(xs, cout, P, ys);
+    const int64_t N = xs[0];
+    const int64_t S[3] = {ys[2], ys[3], ys[4]};
+    const int64_t plane = S[0] * S[1] * S[2];
+    const int64_t P0 = oracle_pool_out_len(S[0], pool), P1 = oracle_pool_out_len(S[1], pool),
+                  P2 = oracle_pool_out_len(S[2], pool);
+    const int64_t pplane = P0 * P1 * P2;
+    double* y = (double*)malloc(sizeof(double) * (size_t)(N * plane));
+    double* pooled = (double*)malloc(sizeof(double) * (size_t)(N * (pplane > 0 ? pplane : 1)));
+    for (int64_t c = 0; c < cout; ++c) {
+        oracle_conv_transpose3d_channels(x, xs, w, cout, P, bias, c, c + 1, y);
+        const double rm = running_mean[c], rs = sqrt((double)running_var[c] + eps);
+        for (int64_t e = 0; e < N * plane; ++e) y[e] = (double)gamma[c] * (y[e] - rm) / rs + (double)beta[c];
+        oracle_avgpool3d(y, N, S, pool, pooled);
+        for (int64_t n = 0; n < N; ++n)
+            memcpy(out + (n * cout + c) * pplane, pooled + n * pplane, sizeof(double) * (size_t)pplane);
+    }
+    free(y);
+    free(pooled);
+}
+
+/* Running statistics after one training-mode forward (BatchNorm3d, [p72]'s
+ * momentum 0.1 and its training/eval distinction): with count = elements per
+ * channel,
+ *   running_mean <- (1 - m) running_mean + m * batch_mean
+ *   running_var  <- (1 - m) running_var  + m * batch_var * count / (count - 1)
+ * i.e. the running variance tracks the unbiased batch variance while the
+ * normalisation itself uses the biased one. */
+void oracle_bn_running_update(int64_t C, double momentum, int64_t count, const double* batch_mean,
+                              const double* batch_var_biased, double* running_mean, double* running_var) {
+    for (int64_t c = 0; c < C; ++c) {
+        const double unbiased = batch_var_biased[c] * (double)count / (double)(count - 1);
+        running_mean[c] = (1.0 - momentum) * running_mean[c] + momentum * batch_mean[c];
+        running_var[c] = (1.0 - momentum) * running_var[c] + momentum * unbiased;
+    }
+}
+
 /* Conv3d -> MaxPool3d(pool) -> logsumexp over channels (keepdim) -> ReLU
  * ([p43], the module definition).  Processed one pooled row j0 at a time
  * (the conv rows [pool*j0, pool*j0 + pool) of every channel, then the three

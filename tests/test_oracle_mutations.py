@@ -40,6 +40,14 @@ MUTATIONS = [
     ("lse_no_shift_inside_exp", "s += exp(in[(n * C + c) * plane + t] - m);",
      "s += exp(in[(n * C + c) * plane + t]);", 0),
     ("relu_inverted", "if (!(v[t] > 0.0)) v[t] = 0.0;", "if (v[t] > 0.0) v[t] = 0.0;", 0),
+    ("running_var_biased", "batch_var_biased[c] * (double)count / (double)(count - 1);",
+     "batch_var_biased[c];", 0),
+    ("running_momentum_swapped", "running_mean[c] = (1.0 - momentum) * running_mean[c] + momentum * batch_mean[c];",
+     "running_mean[c] = momentum * running_mean[c] + (1.0 - momentum) * batch_mean[c];", 0),
+    ("eval_running_mean_dropped", "(double)gamma[c] * (y[e] - rm) / rs + (double)beta[c];",
+     "(double)gamma[c] * y[e] / rs + (double)beta[c];", 0),
+    ("eval_eps_dropped", "const double rm = running_mean[c], rs = sqrt((double)running_var[c] + eps);",
+     "const double rm = running_mean[c], rs = sqrt((double)running_var[c]);", 0),
     ("fused_pool_rows_shifted", "oracle_conv3d_rows(x, xs, w, cout, P, bias, j0 * pool, j0 * pool + pool, y);",
      "oracle_conv3d_rows(x, xs, w, cout, P, bias, j0 * pool / 2, j0 * pool / 2 + pool, y);", 0),
 ]
@@ -66,6 +74,10 @@ def _pins():
         out.append(lambda s=s: P.test_convT_gather_equals_scatter(s))
         out.append(lambda s=s: P.test_adjoint_identity(s))
     out.append(lambda: P.test_convT_bn_avgpool_matches_torch_module(dict(x_shape=(4, 3, 8, 8, 8), cout=16, pool=4)))
+    out.append(lambda: P.test_convT_bn_eval_avgpool_matches_torch_module(P.EVAL_CASES[0]))
+    out.append(P.test_convT_bn_eval_with_batch_statistics_equals_training_mode)
+    out.append(lambda: P.test_bn_running_update_matches_torch_module(0.1))
+    out.append(P.test_bn_running_update_closed_forms)
     out.append(lambda: P.test_conv_maxpool_lse_relu_matches_torch_module(dict(x_shape=(2, 4, 8, 8, 8), cout=8)))
     return out
 

@@ -433,6 +433,77 @@ def test_convT_bn_avgpool_matches_torch_module(case):
     np.testing.assert_allclose(var, vt, rtol=1e-11)
 
 
+# --------------------------------------------- eval mode, running statistics
+EVAL_CASES = [
+    dict(x_shape=(3, 3, 8, 8, 8), cout=16, pool=4),
+    dict(x_shape=(2, 2, 7, 9, 8), cout=5, pool=2, kernel=(3, 2, 3), stride=(2, 3, 2), pad=(1, 0, 1)),
+    dict(x_shape=(2, 4, 6, 6, 6), cout=4, pool=3, groups=2, dilation=(2, 1, 1), output_pad=(1, 0, 0)),
+]
+
+
+@pytest.mark.parametrize("case", EVAL_CASES)
+def test_convT_bn_eval_avgpool_matches_torch_module(case):
+    """Eval-mode BatchNorm3d ([p72]'s shipped variant) against PyTorch's
+    batch_norm with running statistics, in float64, then the pool."""
+    wl = W.CONFIGS["c4"].with_(**case)
+    inp = W.make_inputs(wl)
+    rm, rv = W.make_running_stats(wl.cout, 7)
+    out = O.convT_bn_eval_avgpool(inp.x, inp.w, inp.b, inp.gamma, inp.beta, rm, rv, wl.eps, wl.pool, wl.stride,
+                                  wl.pad, wl.dilation, wl.output_pad, wl.groups)
+    y = F.conv_transpose3d(t64(inp.x), t64(inp.w), t64(inp.b), wl.stride, wl.pad, wl.output_pad, wl.groups,
+                           wl.dilation)
+    z = F.batch_norm(y, t64(rm), t64(rv), t64(inp.gamma), t64(inp.beta), training=False, eps=wl.eps)
+    ref = F.avg_pool3d(z, wl.pool).numpy()
+    assert out.shape == ref.shape
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-11)
+
+
+def test_convT_bn_eval_with_batch_statistics_equals_training_mode():
+    """Eval mode fed the batch's own mean and biased variance normalises exactly
+    as training mode does (up to the float32 cast of the statistics)."""
+    wl = W.CONFIGS["c4"].with_(x_shape=(3, 3, 8, 8, 8))
+    inp = W.make_inputs(wl)
+    out_t, mean, var = O.run_workload(wl, inp)
+    out_e = O.convT_bn_eval_avgpool(inp.x, inp.w, inp.b, inp.gamma, inp.beta, mean.astype(np.float32),
+                                    var.astype(np.float32), wl.eps, wl.pool, wl.stride, wl.pad, wl.dilation,
+                                    wl.output_pad, wl.groups)
+    np.testing.assert_allclose(out_e, out_t, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("momentum", [0.1, 0.3])
+def test_bn_running_update_matches_torch_module(momentum):
+    """One training-mode forward of torch.nn.BatchNorm3d (float64) updates the
+    running statistics exactly as the oracle does: the unbiased batch
+    variance, blended with the momentum ([p72]'s 0.1)."""
+    wl = W.CONFIGS["c4"].with_(x_shape=(2, 3, 6, 7, 5), cout=6)
+    inp = W.make_inputs(wl)
+    rm, rv = W.make_running_stats(wl.cout, 11)
+    _, mean, var = O.run_workload(wl, inp)
+    y = F.conv_transpose3d(t64(inp.x), t64(inp.w), t64(inp.b), wl.stride, wl.pad, wl.output_pad, wl.groups,
+                           wl.dilation)
+    bn = torch.nn.BatchNorm3d(wl.cout, eps=wl.eps, momentum=momentum, dtype=torch.float64)
+    with torch.no_grad():
+        bn.running_mean.copy_(t64(rm))
+        bn.running_var.copy_(t64(rv))
+    bn.train()
+    bn(y)
+    count = y.numel() // wl.cout
+    nrm, nrv = O.bn_running_update(rm, rv, mean, var, count, momentum)
+    np.testing.assert_allclose(nrm, bn.running_mean.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(nrv, bn.running_var.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_bn_running_update_closed_forms():
+    rng = np.random.default_rng(5)
+    rm, rv = rng.uniform(-1, 1, 4), rng.uniform(0.5, 2, 4)
+    bm, bv = rng.uniform(-1, 1, 4), rng.uniform(0.1, 3, 4)
+    a, b = O.bn_running_update(rm, rv, bm, bv, 10, 0.0)   # momentum 0: unchanged
+    assert np.array_equal(a, rm) and np.array_equal(b, rv)
+    a, b = O.bn_running_update(rm, rv, bm, bv, 10, 1.0)   # momentum 1: the batch's own statistics
+    np.testing.assert_allclose(a, bm, rtol=1e-15)
+    np.testing.assert_allclose(b, bv * 10 / 9, rtol=1e-15)
+
+
 def test_convT_bn_avgpool_bias_cancels_and_gamma_zero():
     wl = W.CONFIGS["c4"].with_(x_shape=(3, 3, 8, 8, 8))
     inp = W.make_inputs(wl)

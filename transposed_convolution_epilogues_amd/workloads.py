@@ -167,6 +167,16 @@ def make_inputs(wl: Workload, seed: Optional[int] = None,
     return Inputs(x=x, w=w, b=b, gamma=gamma, beta=beta)
 
 
+def make_running_stats(cout: int, seed: int) -> Tuple[np.ndarray, np.ndarray]:
+    """BatchNorm running statistics for eval-mode tests: mean ~ U[-0.25, 0.25],
+    variance ~ U[0.5, 2.0], drawn in float64 with their own seed and cast to
+    float32."""
+    rng = np.random.default_rng(seed)
+    rm = _uniform(rng, -0.25, 0.25, (cout,))
+    rv = _uniform(rng, 0.5, 2.0, (cout,))
+    return rm, rv
+
+
 def random_small_workload(op: str, rng: np.random.Generator, max_spatial: int = 9,
                           allow_groups: bool = True) -> Workload:
     """A random small module for sweep tests: stride 1..3, pad 0..2,
