@@ -85,8 +85,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--widen", action="store_true",
-                    help="instead of the step: time the transposed convs beyond the five configurations "
-                         "(per-output-phase MFMA path against the generic kernel) and print one JSON line")
+                    help="instead of the step: time the work beyond the five configurations (general "
+                         "transposed convs, eval-mode / running-statistics BatchNorm) against the generic kernels "
+                         "and print one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a design "
@@ -263,34 +264,53 @@ def calibrate_copy(torch):
 
 
 def widen(torch, args):
-    """Transposed convs beyond the five configurations: each through its
-    automatic kernel (the per-output-phase MFMA path), the c3 module also
-    through the general phase path instead of its sub-lattice kernel, and
-    each through the generic gather kernel for comparison."""
+    """Work beyond the five configurations, each timed through its automatic
+    kernel and through the generic kernels for comparison:
+      - transposed convs on the per-output-phase MFMA path, and the c3 module
+        through that general path instead of its sub-lattice kernel;
+      - the c4 module with BatchNorm in eval mode (running statistics), and in
+        training mode with the running-statistics update."""
     from transposed_convolution_epilogues_amd import binding as B
     from transposed_convolution_epilogues_amd import workloads as W
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B.library()
-    cases = [(k, wl, 0) for k, wl in W.WIDEN.items()] + [("c3_phase", W.CONFIGS["c3"], 2)]
+    c4 = W.CONFIGS["c4"]
+    cases = ([(k, wl, 0, "convT") for k, wl in W.WIDEN.items()] + [("c3_phase", W.CONFIGS["c3"], 2, "convT")] +
+             [("c4_eval", c4, 0, "bn_eval"), ("c4_train_running", c4, 0, "bn_running")])
     out = {}
-    for key, wl, variant in cases:
+    for key, wl, variant, kind in cases:
         inp = W.make_inputs(wl)
-        x, w = torch.from_numpy(inp.x).to(dev), torch.from_numpy(inp.w).to(dev)
-        b = None if inp.b is None else torch.from_numpy(inp.b).to(dev)
+        t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        x, w, b = t(inp.x), t(inp.w), t(inp.b)
         p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
-        oshape = B.conv_transpose3d_out_shape(wl.x_shape, wl.cout, p)
-        y = torch.empty(oshape, device=dev)
-        mac, xb, wb = work(wl, oshape)
-        nbytes = xb + wb + 4 * math.prod(oshape)
-        row = dict(workload=wl.description, mac=mac, algo_bytes=nbytes)
+        conv_shape = B.conv_transpose3d_out_shape(wl.x_shape, wl.cout, p)
+        mac, xb, wb = work(wl, conv_shape)
+        kw = dict(stride=wl.stride, pad=wl.pad, dilation=wl.dilation, output_pad=wl.output_pad, groups=wl.groups)
+        if kind == "convT":
+            y = torch.empty(conv_shape, device=dev)
+            fn = lambda: B.conv_transpose3d_fwd(x, w, b, out=y, **kw)
+            algo = lambda: B.conv_transpose3d_algo(wl.x_shape, wl.cout, p)
+        else:
+            y = torch.empty(B.convT_bn_avgpool_out_shape(wl.x_shape, wl.cout, p, wl.pool), device=dev)
+            gm, bt = t(inp.gamma), t(inp.beta)
+            rm0, rv0 = W.make_running_stats(wl.cout, 5)
+            rm, rv = t(rm0), t(rv0)
+            ws = torch.empty(B.convT_bn_avgpool_workspace_bytes(wl.x_shape, wl.cout, p, wl.pool), dtype=torch.uint8,
+                             device=dev)
+            train = kind == "bn_running"
+            fn = lambda: B.convT_bn_avgpool(x, w, b, gm, bt, wl.eps, wl.pool, out=y, workspace=ws, training=train,
+                                            running_mean=rm, running_var=rv, **kw)
+            algo = lambda: "fused (phase 1" + (" + phase 2)" if train else " with the BN affine)")
+        nbytes = xb + wb + 4 * y.numel()
+        row = dict(workload=wl.description + {"convT": "", "bn_eval": "; BN in eval mode",
+                                              "bn_running": "; training mode + running-statistics update"}[kind],
+                   mac=mac, algo_bytes=nbytes)
         for label, v, reps in (("fast", variant, args.steps), ("generic", 1, 3)):
             old = B.set_variant(v)
             try:
-                row[label + "_algo"] = B.conv_transpose3d_algo(wl.x_shape, wl.cout, p)
-                fn = lambda: B.conv_transpose3d_fwd(x, w, b, wl.stride, wl.pad, wl.dilation, wl.output_pad,
-                                                    wl.groups, out=y)
+                row[label + "_algo"] = algo() if v != 1 else "generic"
                 for _ in range(2):
                     fn()
                 torch.cuda.synchronize()
@@ -303,11 +323,11 @@ def widen(torch, args):
                     e1.record(stream)
                     ms.append((e0, e1))
                 torch.cuda.synchronize()
-                t = float(np.median([a.elapsed_time(c) for a, c in ms]))
+                tm = float(np.median([a.elapsed_time(c) for a, c in ms]))
             finally:
                 B.set_variant(old)
-            row[label + "_ms_median"] = round(t, 5)
-            row[label + "_tflops"] = round(2.0 * mac / (t * 1e-3) / 1e12, 3)
+            row[label + "_ms_median"] = round(tm, 5)
+            row[label + "_tflops"] = round(2.0 * mac / (tm * 1e-3) / 1e12, 3)
         row["frac_fp32_peak"] = round(row["fast_tflops"] / FP32_PEAK_TFLOPS, 4)
         row["hbm_gbs"] = round(nbytes / (row["fast_ms_median"] * 1e-3) / 1e9, 1)
         row["frac_hbm_peak"] = round(row["hbm_gbs"] / HBM_PEAK_GBS, 4)
@@ -315,9 +335,9 @@ def widen(torch, args):
         out[key] = row
         print(f"[bench --widen] {key}: {row}", file=sys.stderr, flush=True)
         del x, w, b, y
-    print(json.dumps({"metric": "effective TFLOP/s (2*valid-tap MACs/time), transposed convs beyond the configs",
-                      "unit": "TFLOP/s", "dtype": "f32", "data": "synthetic", "steps": args.steps,
-                      "widen": out}), flush=True)
+    print(json.dumps({"metric": "effective TFLOP/s (2*MACs/time; valid-tap MACs for transposed convs), work beyond "
+                                "the five configurations", "unit": "TFLOP/s", "dtype": "f32", "data": "synthetic",
+                      "steps": args.steps, "widen": out}), flush=True)
 
 
 def cpu_baseline(runs, seconds_per_workload):

@@ -141,6 +141,34 @@ int convT_bn_avgpool(const float* x, const int64_t x_shape[5], const float* w, i
                      float eps, int32_t pool, float* y, void* ws, size_t ws_bytes, float* batch_mean,
                      float* batch_var, void* stream);
 
+/* convT_bn_avgpool with the module's running statistics and its eval mode
+ * ("Kimi-K2.6 l2_p72": the eval-mode variant the page ships, which folds
+ * BatchNorm into the transposed conv and normalises with the running
+ * statistics, and BatchNorm3d's momentum of 0.1).
+ *   training != 0: as convT_bn_avgpool; if running_mean and running_var are
+ *     given (both or neither), they are then updated in place:
+ *       running_mean <- (1 - momentum) running_mean + momentum * batch mean
+ *       running_var  <- (1 - momentum) running_var
+ *                       + momentum * batch var * count / (count - 1)
+ *     with count = N*O0*O1*O2 elements per channel (the running variance
+ *     tracks the unbiased batch variance, as BatchNorm3d does).  Requires
+ *     0 <= momentum <= 1 (C3D_ERR_PARAM) and count >= 2 (C3D_ERR_SHAPE).
+ *   training == 0 (eval): running_mean and running_var are required and
+ *     read; one kernel writes
+ *       y[n,c,j] = gamma_c * (avg_{u in [0,pool)^3} t[n,c,pool*j+u] - running_mean_c)
+ *                  / sqrt(running_var_c + eps) + beta_c
+ *     with t = conv_transpose3d(x, w, conv_bias) (the map is applied after
+ *     the pool, which it commutes with).  ws, ws_bytes, batch_mean and
+ *     batch_var are ignored (ws may be NULL).
+ *   running_mean, running_var [Cout] or NULL (device, read; written in
+ *     training mode)
+ * Calls that update the same running buffers must not overlap. */
+int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+                        const c3d_conv_params* p, const float* conv_bias, const float* gamma, const float* beta,
+                        float eps, int32_t pool, int32_t training, float momentum, float* running_mean,
+                        float* running_var, float* y, void* ws, size_t ws_bytes, float* batch_mean,
+                        float* batch_var, void* stream);
+
 /* Conv3d -> MaxPool3d(pool, stride pool) -> logsumexp over channels
  * (keepdim) -> ReLU ("Kimi-K2.6 l2_p43": the module, floor-mode pooling and
  * the max-shifted logsumexp):

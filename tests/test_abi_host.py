@@ -138,6 +138,35 @@ def test_fused_op_errors_are_reported_before_launch():
                                      2, vp(12288), None) == 2
 
 
+def test_bn_running_stats_and_eval_errors_are_reported_before_launch():
+    lib = B.library()
+    vp = ctypes.c_void_p
+    p = _p(3, 2, 1)
+    xs = B._shape5((2, 3, 8, 8, 8))
+    ws_need = lib.convT_bn_avgpool_workspace_bytes(xs, 16, ctypes.byref(p), 4)
+    ok = dict(x=vp(4096), w=vp(8192), b=None, g=vp(12288), be=vp(16384), y=vp(20480), ws=vp(24576),
+              rm=vp(28672), rv=vp(32768))
+
+    def call(training=1, momentum=0.1, eps=1e-5, shape=xs, params=p, **kw):
+        a = dict(ok, **kw)
+        return lib.convT_bn_avgpool_ex(a["x"], shape, a["w"], 16, ctypes.byref(params), a["b"], a["g"], a["be"],
+                                       eps, 4 if shape is xs else 1, training, momentum, a["rm"], a["rv"], a["y"],
+                                       a["ws"], ws_need, None, None, None)
+
+    assert call(training=0, rm=None, rv=None) == 1       # eval mode needs the running statistics
+    assert call(training=0, rv=None) == 1
+    assert call(rm=None) == 1                             # both or neither
+    assert call(momentum=1.5) == 3
+    assert call(momentum=-0.1) == 3
+    assert call(momentum=float("nan")) == 3
+    assert call(training=0, eps=0.0) == 3
+    assert call(training=0, g=None) == 1
+    assert call(training=0, rm=vp(28674)) == 7            # misaligned running mean
+    assert call(ws=None) == 4                             # training still needs the workspace
+    # one element per channel: no unbiased variance for the running update
+    assert call(shape=B._shape5((1, 3, 1, 1, 1)), params=_p(1, 1, 0)) == 2
+
+
 def test_status_strings():
     lib = B.library()
     for code in range(8):

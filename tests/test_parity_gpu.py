@@ -317,6 +317,68 @@ def test_c5_full_size_sampled():
     assert torch.equal(y, y2)
 
 
+# ------------------------------------ BatchNorm: eval mode, running statistics
+BN_EVAL = {
+    "c4_reduced": W.CONFIGS["c4"].with_(x_shape=(3, 3, 14, 13, 18)),
+    "c4_cin1_cout5": W.CONFIGS["c4"].with_(x_shape=(2, 1, 6, 9, 8), cout=5),
+    "generic_pool2_groups": W.CONFIGS["c4"].with_(x_shape=(2, 4, 5, 6, 7), cout=6, pool=2, groups=2,
+                                                  kernel=(3, 2, 3), stride=(2, 1, 2), output_pad=(1, 0, 0)),
+}
+
+
+def _bn_eval_gpu(wl, inp, rm, rv):
+    return B.convT_bn_avgpool(dev(inp.x), dev(inp.w), dev(inp.b), dev(inp.gamma), dev(inp.beta), wl.eps, wl.pool,
+                              wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups,
+                              out=poisoned(O.output_shape(wl)), training=False, running_mean=dev(rm),
+                              running_var=dev(rv))
+
+
+@pytest.mark.parametrize("name", list(BN_EVAL))
+def test_bn_eval_mode(name, variant):
+    wl = BN_EVAL[name]
+    inp = W.make_inputs(wl)
+    rm, rv = W.make_running_stats(wl.cout, 17)
+    print(f"[bn eval {name} v{variant}] {wl}", flush=True)
+    y = _bn_eval_gpu(wl, inp, rm, rv)
+    torch.cuda.synchronize()
+    ref = O.convT_bn_eval_avgpool(inp.x, inp.w, inp.b, inp.gamma, inp.beta, rm, rv, wl.eps, wl.pool, wl.stride,
+                                  wl.pad, wl.dilation, wl.output_pad, wl.groups)
+    assert_close(f"bn eval {name}", y.cpu().numpy(), ref)
+
+
+def test_bn_eval_mode_c4_full_size():
+    wl = W.CONFIGS["c4"]
+    inp = W.make_inputs(wl)
+    rm, rv = W.make_running_stats(wl.cout, 19)
+    y = _bn_eval_gpu(wl, inp, rm, rv)
+    torch.cuda.synchronize()
+    ref = O.convT_bn_eval_avgpool(inp.x, inp.w, inp.b, inp.gamma, inp.beta, rm, rv, wl.eps, wl.pool, wl.stride,
+                                  wl.pad, wl.dilation, wl.output_pad, wl.groups)
+    assert_close("bn eval c4", y.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("name", ["c4_reduced", "generic_pool2_groups"])
+def test_bn_running_statistics_update(name, variant):
+    wl = BN_EVAL[name]
+    inp = W.make_inputs(wl)
+    rm0, rv0 = W.make_running_stats(wl.cout, 23)
+    rm, rv = dev(rm0), dev(rv0)
+    kw = dict(stride=wl.stride, pad=wl.pad, dilation=wl.dilation, output_pad=wl.output_pad, groups=wl.groups)
+    args = (dev(inp.x), dev(inp.w), dev(inp.b), dev(inp.gamma), dev(inp.beta), wl.eps, wl.pool)
+    y = B.convT_bn_avgpool(*args, out=poisoned(O.output_shape(wl)), running_mean=rm, running_var=rv,
+                           momentum=0.1, **kw)
+    y_plain = B.convT_bn_avgpool(*args, out=poisoned(O.output_shape(wl)), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_plain)  # the update does not change the output
+    out, mean, var = O.run_workload(wl, inp)
+    assert_close(f"bn running out {name}", y.cpu().numpy(), out)
+    cshape = O.convT_out_shape(wl.x_shape, wl.cout, wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad)
+    count = cshape[0] * cshape[2] * cshape[3] * cshape[4]
+    erm, erv = O.bn_running_update(rm0, rv0, mean, var, count, 0.1)
+    assert_close(f"running mean {name}", rm.cpu().numpy(), erm)
+    assert_close(f"running var {name}", rv.cpu().numpy(), erv)
+
+
 # ----------------------------------------------------------- edge cases
 EDGE = {
     "conv_1x1x1_single": W.make("e", "conv3d", (1, 1, 1, 1, 1), 1, 1, bias=True, seed=7),

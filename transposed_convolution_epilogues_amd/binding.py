@@ -24,7 +24,8 @@ STATUS = {0: "C3D_OK", 1: "C3D_ERR_NULL", 2: "C3D_ERR_SHAPE", 3: "C3D_ERR_PARAM"
 
 EXPORTS = ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_bn_avgpool_out_shape",
            "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
-           "convT_bn_avgpool_workspace_bytes", "convT_bn_avgpool", "conv_maxpool_lse_relu", "c3d_status_string",
+           "convT_bn_avgpool_workspace_bytes", "convT_bn_avgpool", "convT_bn_avgpool_ex", "conv_maxpool_lse_relu",
+           "c3d_status_string",
            "c3d_set_variant", "c3d_conv3d_algo", "c3d_conv_transpose3d_algo")
 
 ALGO = {0: "direct", 1: "k1last", 2: "mfma333", 3: "sublattice", 4: "phase"}
@@ -91,6 +92,8 @@ def _lib():
     lib.convT_bn_avgpool_workspace_bytes.restype = ctypes.c_size_t
     lib.convT_bn_avgpool.argtypes = [vp, i64p, vp, i64, P, vp, vp, vp, ctypes.c_float, ctypes.c_int32, vp, vp,
                                      ctypes.c_size_t, vp, vp, vp]
+    lib.convT_bn_avgpool_ex.argtypes = [vp, i64p, vp, i64, P, vp, vp, vp, ctypes.c_float, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp]
     lib.conv_maxpool_lse_relu.argtypes = [vp, i64p, vp, i64, P, vp, ctypes.c_int32, vp, vp]
     lib.c3d_status_string.argtypes = [ctypes.c_int]
     lib.c3d_status_string.restype = ctypes.c_char_p
@@ -100,7 +103,8 @@ def _lib():
     lib.c3d_conv_transpose3d_algo.argtypes = [i64p, i64, P, i32p]
     for name in ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_bn_avgpool_out_shape",
                  "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
-                 "convT_bn_avgpool", "conv_maxpool_lse_relu", "c3d_set_variant", "c3d_conv3d_algo",
+                 "convT_bn_avgpool", "convT_bn_avgpool_ex", "conv_maxpool_lse_relu", "c3d_set_variant",
+                 "c3d_conv3d_algo",
                  "c3d_conv_transpose3d_algo"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
@@ -236,23 +240,37 @@ def convT_bn_avgpool(x: torch.Tensor, w: torch.Tensor, conv_bias: Optional[torch
                      dilation: Int3 = 1, output_pad: Int3 = 0, groups: int = 1,
                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                      batch_mean: Optional[torch.Tensor] = None, batch_var: Optional[torch.Tensor] = None,
-                     stream=None) -> torch.Tensor:
-    """ConvTranspose3d -> BatchNorm3d (batch statistics) -> AvgPool3d(pool)."""
+                     stream=None, training: bool = True, momentum: float = 0.1,
+                     running_mean: Optional[torch.Tensor] = None,
+                     running_var: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ConvTranspose3d -> BatchNorm3d -> AvgPool3d(pool).  Training mode
+    normalises with the batch statistics and, when running_mean/running_var
+    are given, updates them in place; eval mode (training=False) normalises
+    with them."""
     params = make_params(tuple(w.shape[2:]), stride, pad, dilation, output_pad, groups)
     cout = int(w.shape[1]) * int(groups)
     ys = convT_bn_avgpool_out_shape(x.shape, cout, params, pool)
     if out is None:
         out = torch.empty(ys, dtype=torch.float32, device=x.device)
-    nbytes = convT_bn_avgpool_workspace_bytes(x.shape, cout, params, pool)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=x.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr())
-    _check(_lib().convT_bn_avgpool(_dev(x, "x"), _shape5(x.shape), _dev(w, "w"), cout, ctypes.byref(params),
-                                   _dev(conv_bias, "conv_bias", False), _dev(gamma, "gamma"), _dev(beta, "beta"),
-                                   float(eps), int(pool), _dev(out, "out"), ws_ptr,
-                                   workspace.numel() * workspace.element_size(),
-                                   _dev(batch_mean, "batch_mean", False), _dev(batch_var, "batch_var", False),
-                                   _stream(stream)), "convT_bn_avgpool")
+    plain = training and running_mean is None and running_var is None
+    if training:
+        nbytes = convT_bn_avgpool_workspace_bytes(x.shape, cout, params, pool)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=x.device)
+        ws_ptr, ws_bytes = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    else:
+        ws_ptr, ws_bytes = None, 0
+    head = (_dev(x, "x"), _shape5(x.shape), _dev(w, "w"), cout, ctypes.byref(params),
+            _dev(conv_bias, "conv_bias", False), _dev(gamma, "gamma"), _dev(beta, "beta"), float(eps), int(pool))
+    tail = (ws_ptr, ws_bytes, _dev(batch_mean, "batch_mean", False), _dev(batch_var, "batch_var", False),
+            _stream(stream))
+    if plain:
+        _check(_lib().convT_bn_avgpool(*head, _dev(out, "out"), *tail), "convT_bn_avgpool")
+    else:
+        _check(_lib().convT_bn_avgpool_ex(*head, int(bool(training)), float(momentum),
+                                          _dev(running_mean, "running_mean", False),
+                                          _dev(running_var, "running_var", False), _dev(out, "out"), *tail),
+               "convT_bn_avgpool_ex")
     return out
 
 

@@ -242,35 +242,56 @@ size_t convT_bn_avgpool_workspace_bytes(const int64_t x_shape[5], int64_t cout, 
     return c3d::convT_bn_pool_partials(pg, 0) * (size_t)g.Cout * 2 * sizeof(double);
 }
 
-int convT_bn_avgpool(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
-                     const c3d_conv_params* p, const float* conv_bias, const float* gamma, const float* beta,
-                     float eps, int32_t pool, float* y, void* ws, size_t ws_bytes, float* batch_mean,
-                     float* batch_var, void* stream) {
+int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+                        const c3d_conv_params* p, const float* conv_bias, const float* gamma, const float* beta,
+                        float eps, int32_t pool, int32_t training, float momentum, float* running_mean,
+                        float* running_var, float* y, void* ws, size_t ws_bytes, float* batch_mean,
+                        float* batch_var, void* stream) {
     if (!x || !w || !y || !gamma || !beta) return C3D_ERR_NULL;
+    const bool update = running_mean || running_var;
+    if (update && !(running_mean && running_var)) return C3D_ERR_NULL;  // both or neither
+    if (!training && !update) return C3D_ERR_NULL;                      // eval mode reads them
     if (!aligned4(x) || !aligned4(w) || !aligned4(y) || !aligned4(conv_bias) || !aligned4(gamma) ||
-        !aligned4(beta) || !aligned4(batch_mean) || !aligned4(batch_var))
+        !aligned4(beta) || !aligned4(batch_mean) || !aligned4(batch_var) || !aligned4(running_mean) ||
+        !aligned4(running_var))
         return C3D_ERR_ALIGN;
     if (!(eps > 0.f) || !isfinite(eps)) return C3D_ERR_PARAM;
+    if (training && update && !(momentum >= 0.f && momentum <= 1.f)) return C3D_ERR_PARAM;
     Geom g;
     PoolGeom pg;
     int st = resolve(x_shape, cout, p, true, &g);
     if (st) return st;
     st = resolve_pool(g, pool, &pg);
     if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const bool fast = g_variant.load() != 1 && c3d::convT_bn_pool_fast_supported(pg, x);
+    if (!training) {
+        // eval mode: one pass, the BN affine with the running statistics applied to the pooled values
+        const c3d::BnEval ev{gamma, beta, running_mean, running_var, conv_bias, eps};
+        return hip_status(fast ? c3d::launch_convT_bn_pool_phase1_fast(x, w, y, nullptr, pg, ev, s)
+                               : c3d::launch_convT_bn_pool_phase1_direct(x, w, y, nullptr, pg, ev, s));
+    }
+    if (update && g.N * g.O[0] * g.O[1] * g.O[2] < 2) return C3D_ERR_SHAPE;  // no unbiased variance
     const size_t parts = c3d::convT_bn_pool_partials(pg, 0);
     const size_t need = parts * (size_t)g.Cout * 2 * sizeof(double);
     if (!ws || ws_bytes < need) return C3D_ERR_WORKSPACE;
     if (((uintptr_t)ws & 7u) != 0) return C3D_ERR_ALIGN;
-    hipStream_t s = (hipStream_t)stream;
     double* part = (double*)ws;
-    hipError_t e;
-    if (g_variant.load() == 0 && c3d::convT_bn_pool_fast_supported(pg, x))
-        e = c3d::launch_convT_bn_pool_phase1_fast(x, w, y, part, pg, s);
-    else
-        e = c3d::launch_convT_bn_pool_phase1_direct(x, w, y, part, pg, s);
+    const c3d::BnEval none{nullptr, nullptr, nullptr, nullptr, nullptr, 0.f};
+    const hipError_t e = fast ? c3d::launch_convT_bn_pool_phase1_fast(x, w, y, part, pg, none, s)
+                              : c3d::launch_convT_bn_pool_phase1_direct(x, w, y, part, pg, none, s);
     if (e != hipSuccess) return C3D_ERR_HIP;
+    const c3d::BnRunning run{update ? running_mean : nullptr, update ? running_var : nullptr, momentum};
     return hip_status(c3d::launch_bn_pool_phase2(y, part, (int64_t)parts, conv_bias, gamma, beta, eps, batch_mean,
-                                                 batch_var, pg, s));
+                                                 batch_var, run, pg, s));
+}
+
+int convT_bn_avgpool(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+                     const c3d_conv_params* p, const float* conv_bias, const float* gamma, const float* beta,
+                     float eps, int32_t pool, float* y, void* ws, size_t ws_bytes, float* batch_mean,
+                     float* batch_var, void* stream) {
+    return convT_bn_avgpool_ex(x, x_shape, w, cout, p, conv_bias, gamma, beta, eps, pool, 1, 0.f, nullptr, nullptr,
+                               y, ws, ws_bytes, batch_mean, batch_var, stream);
 }
 
 int conv_maxpool_lse_relu(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,

@@ -35,13 +35,43 @@ hipError_t launch_conv_pool_lse_relu_direct(const float* x, const float* w, cons
 
 // convT_bn_avgpool: phase 1 writes pre-normalisation pooled means into y and
 // per-block (sum, sum of squares) partials in float64 into ws; phase 2 merges
-// the partials per channel and applies the affine map in place.
+// the partials per channel and applies the affine map in place (and blends
+// the batch statistics into the running ones when asked).
+//
+// Eval-mode BatchNorm: when gamma is set, phase 1 writes the final output
+// gamma_c (avg + bias_c - mean_c) / sqrt(var_c + eps) + beta_c with the
+// running statistics (the BN affine commutes with the linear average pool)
+// and computes no partials; ws is not used and phase 2 does not run.
+struct BnEval {
+    const float* gamma;
+    const float* beta;
+    const float* mean;
+    const float* var;
+    const float* bias;
+    float eps;
+};
+
+// scale and shift of the eval-mode map for channel c
+__device__ inline void bn_eval_affine(const BnEval& ev, int64_t c, float& sc, float& sh) {
+    const double s = (double)ev.gamma[c] / sqrt((double)ev.var[c] + (double)ev.eps);
+    sc = (float)s;
+    sh = (float)((double)ev.beta[c] + ((ev.bias ? (double)ev.bias[c] : 0.0) - (double)ev.mean[c]) * s);
+}
+
+// Running-statistics update of phase 2 (training mode): with m = momentum,
+// mean <- (1 - m) mean + m * batch mean, var <- (1 - m) var + m * unbiased batch var.
+struct BnRunning {
+    float* mean;
+    float* var;
+    float momentum;
+};
+
 size_t convT_bn_pool_partials(const PoolGeom& pg, int fast);
 hipError_t launch_convT_bn_pool_phase1_direct(const float* x, const float* w, float* y, double* ws,
-                                              const PoolGeom& pg, hipStream_t st);
+                                              const PoolGeom& pg, const BnEval& ev, hipStream_t st);
 hipError_t launch_bn_pool_phase2(float* y, const double* ws, int64_t parts_per_channel, const float* conv_bias,
                                  const float* gamma, const float* beta, float eps, float* mean_out,
-                                 float* var_out, const PoolGeom& pg, hipStream_t st);
+                                 float* var_out, const BnRunning& run, const PoolGeom& pg, hipStream_t st);
 
 // ------------------------------------------------------------- fast paths
 // Each returns hipErrorNotSupported (without launching) when the geometry is
@@ -63,7 +93,7 @@ hipError_t launch_conv_k1last(const float* x, const float* w, const float* bias,
                               hipStream_t st);
 bool convT_bn_pool_fast_supported(const PoolGeom& pg, const void* x);
 hipError_t launch_convT_bn_pool_phase1_fast(const float* x, const float* w, float* y, double* ws,
-                                            const PoolGeom& pg, hipStream_t st);
+                                            const PoolGeom& pg, const BnEval& ev, hipStream_t st);
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

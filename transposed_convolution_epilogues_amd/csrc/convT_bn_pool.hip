@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kThreads) void convT_bn_pool_phase1_kernel(const fl
                                                                         const float* __restrict__ w,
                                                                         float* __restrict__ y,
                                                                         double* __restrict__ ws, PoolGeom pg,
-                                                                        int64_t blocks_per_plane) {
+                                                                        int64_t blocks_per_plane, BnEval ev) {
     __shared__ double red[kThreads / 64][2];
     const Geom& g = pg.g;
     const int64_t cells = pg.C[0] * pg.C[1] * pg.C[2];
@@ -111,8 +111,14 @@ __global__ __launch_bounds__(kThreads) void convT_bn_pool_phase1_kernel(const fl
                         sq = fma((double)t, (double)t, sq);
                     }
                 }
-        if (full)
-            y[(n * g.Cout + oc) * pplane + (c0 * pg.P[1] + c1) * pg.P[2] + c2] = win * (1.f / 64.f);
+        float* yo = y + (n * g.Cout + oc) * pplane + (c0 * pg.P[1] + c1) * pg.P[2] + c2;
+        if (ev.gamma) {  // eval mode (workgroup-uniform): final output, no statistics
+            float sc, sh;
+            bn_eval_affine(ev, oc, sc, sh);
+            if (full) *yo = fmaf(win * (1.f / 64.f), sc, sh);
+            continue;
+        }
+        if (full) *yo = win * (1.f / 64.f);
         // block partial of (sum, sum of squares) for this channel
         double s1 = wave_sum_d((double)win);
         double s2 = wave_sum_d(sq);
@@ -144,17 +150,17 @@ bool convT_bn_pool_fast_supported(const PoolGeom& pg, const void*) {
 }
 
 hipError_t launch_convT_bn_pool_phase1_fast(const float* x, const float* w, float* y, double* ws,
-                                            const PoolGeom& pg, hipStream_t st) {
+                                            const PoolGeom& pg, const BnEval& ev, hipStream_t st) {
     const int64_t cells = pg.C[0] * pg.C[1] * pg.C[2];
     const int64_t bpp = ceil_div(cells, kThreads);
     const int64_t blocks = pg.g.N * bpp;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks), block(kThreads);
     switch (pg.g.Cin) {
-        case 1: hipLaunchKernelGGL(convT_bn_pool_phase1_kernel<1>, grid, block, 0, st, x, w, y, ws, pg, bpp); break;
-        case 2: hipLaunchKernelGGL(convT_bn_pool_phase1_kernel<2>, grid, block, 0, st, x, w, y, ws, pg, bpp); break;
-        case 3: hipLaunchKernelGGL(convT_bn_pool_phase1_kernel<3>, grid, block, 0, st, x, w, y, ws, pg, bpp); break;
-        default: hipLaunchKernelGGL(convT_bn_pool_phase1_kernel<4>, grid, block, 0, st, x, w, y, ws, pg, bpp); break;
+        case 1: hipLaunchKernelGGL(convT_bn_pool_phase1_kernel<1>, grid, block, 0, st, x, w, y, ws, pg, bpp, ev); break;
+        case 2: hipLaunchKernelGGL(convT_bn_pool_phase1_kernel<2>, grid, block, 0, st, x, w, y, ws, pg, bpp, ev); break;
+        case 3: hipLaunchKernelGGL(convT_bn_pool_phase1_kernel<3>, grid, block, 0, st, x, w, y, ws, pg, bpp, ev); break;
+        default: hipLaunchKernelGGL(convT_bn_pool_phase1_kernel<4>, grid, block, 0, st, x, w, y, ws, pg, bpp, ev); break;
     }
     return hipGetLastError();
 }

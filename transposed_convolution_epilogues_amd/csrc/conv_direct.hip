@@ -194,7 +194,8 @@ __global__ __launch_bounds__(kBlock) void convT_bn_pool_phase1_direct_kernel(con
                                                                              const float* __restrict__ w,
                                                                              float* __restrict__ y,
                                                                              double* __restrict__ ws,
-                                                                             PoolGeom pg, int64_t blocks_per_plane) {
+                                                                             PoolGeom pg, int64_t blocks_per_plane,
+                                                                             BnEval ev) {
     const Geom& g = pg.g;
     const int pool = pg.pool;
     const int64_t b = blockIdx.x;
@@ -226,9 +227,16 @@ __global__ __launch_bounds__(kBlock) void convT_bn_pool_phase1_direct_kernel(con
         }
         if (c0 < pg.P[0] && c1 < pg.P[1] && c2 < pg.P[2]) {
             const float inv = 1.f / (float)(pool * pool * pool);
-            y[((n * g.Cout + c) * pg.P[0] + c0) * pg.P[1] * pg.P[2] + c1 * pg.P[2] + c2] = win * inv;
+            float v = win * inv;
+            if (ev.gamma) {  // eval mode: the final output
+                float sc, sh;
+                bn_eval_affine(ev, c, sc, sh);
+                v = fmaf(v, sc, sh);
+            }
+            y[((n * g.Cout + c) * pg.P[0] + c0) * pg.P[1] * pg.P[2] + c1 * pg.P[2] + c2] = v;
         }
     }
+    if (ev.gamma) return;  // workgroup-uniform: eval mode keeps no statistics
     block_sum2(s1, s2);
     if (threadIdx.x == 0) {
         const int64_t part = c * (g.N * blocks_per_plane) + n * blocks_per_plane + (b % blocks_per_plane);
@@ -246,8 +254,9 @@ __global__ __launch_bounds__(kBlock) void bn_pool_phase2_kernel(float* __restric
                                                                 const float* __restrict__ gamma,
                                                                 const float* __restrict__ beta, float eps,
                                                                 float* __restrict__ mean_out,
-                                                                float* __restrict__ var_out, PoolGeom pg,
-                                                                int64_t blocks_per_channel, int64_t count) {
+                                                                float* __restrict__ var_out, BnRunning run,
+                                                                PoolGeom pg, int64_t blocks_per_channel,
+                                                                int64_t count) {
     __shared__ float s_scale, s_shift;
     const Geom& g = pg.g;
     const int64_t c = blockIdx.x / blocks_per_channel;
@@ -267,8 +276,14 @@ __global__ __launch_bounds__(kBlock) void bn_pool_phase2_kernel(float* __restric
         s_scale = (float)sc;
         s_shift = (float)((double)beta[c] - mean * sc);
         if (q == 0) {
-            if (mean_out) mean_out[c] = (float)(mean + (conv_bias ? (double)conv_bias[c] : 0.0));
+            const double true_mean = mean + (conv_bias ? (double)conv_bias[c] : 0.0);
+            if (mean_out) mean_out[c] = (float)true_mean;
             if (var_out) var_out[c] = (float)var;
+            if (run.mean) {  // count > 1 is checked on the host
+                const double m = (double)run.momentum;
+                run.mean[c] = (float)((1.0 - m) * (double)run.mean[c] + m * true_mean);
+                run.var[c] = (float)((1.0 - m) * (double)run.var[c] + m * var * (double)count / (double)(count - 1));
+            }
         }
     }
     __syncthreads();
@@ -323,25 +338,25 @@ size_t convT_bn_pool_partials(const PoolGeom& pg, int fast) {
 }
 
 hipError_t launch_convT_bn_pool_phase1_direct(const float* x, const float* w, float* y, double* ws,
-                                              const PoolGeom& pg, hipStream_t st) {
+                                              const PoolGeom& pg, const BnEval& ev, hipStream_t st) {
     const int64_t cells = pg.C[0] * pg.C[1] * pg.C[2];
     const int64_t bpp = ceil_div(cells, kBlock);
     const int64_t blocks = pg.g.Cout * pg.g.N * bpp;
     hipLaunchKernelGGL(convT_bn_pool_phase1_direct_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, x, w, y,
-                       ws, pg, bpp);
+                       ws, pg, bpp, ev);
     return hipGetLastError();
 }
 
 hipError_t launch_bn_pool_phase2(float* y, const double* ws, int64_t parts_per_channel, const float* conv_bias,
                                  const float* gamma, const float* beta, float eps, float* mean_out,
-                                 float* var_out, const PoolGeom& pg, hipStream_t st) {
+                                 float* var_out, const BnRunning& run, const PoolGeom& pg, hipStream_t st) {
     const int64_t pp = pg.P[0] * pg.P[1] * pg.P[2];
     const int64_t per_channel = pg.g.N * pp;
     int64_t bpc = ceil_div(per_channel, 4 * kBlock);
     if (bpc < 1) bpc = 1;
     const int64_t count = pg.g.N * pg.g.O[0] * pg.g.O[1] * pg.g.O[2];
     hipLaunchKernelGGL(bn_pool_phase2_kernel, dim3((unsigned)(bpc * pg.g.Cout)), dim3(kBlock), 0, st, y, ws,
-                       parts_per_channel, conv_bias, gamma, beta, eps, mean_out, var_out, pg, bpc, count);
+                       parts_per_channel, conv_bias, gamma, beta, eps, mean_out, var_out, run, pg, bpc, count);
     return hipGetLastError();
 }
 
