@@ -268,8 +268,9 @@ def widen(torch, args):
     kernel and through the generic kernels for comparison:
       - transposed convs on the per-output-phase MFMA path, and the c3 module
         through that general path instead of its sub-lattice kernel;
-      - the c4 module with BatchNorm in eval mode (running statistics), and in
-        training mode with the running-statistics update."""
+      - the c4 module with BatchNorm in eval mode (running statistics), in
+        training mode with the running-statistics update, and through its
+        swapped-sums algorithm."""
     from transposed_convolution_epilogues_amd import binding as B
     from transposed_convolution_epilogues_amd import workloads as W
 
@@ -278,7 +279,8 @@ def widen(torch, args):
     B.library()
     c4 = W.CONFIGS["c4"]
     cases = ([(k, wl, 0, "convT") for k, wl in W.WIDEN.items()] + [("c3_phase", W.CONFIGS["c3"], 2, "convT")] +
-             [("c4_eval", c4, 0, "bn_eval"), ("c4_train_running", c4, 0, "bn_running")])
+             [("c4_eval", c4, 0, "bn_eval"), ("c4_train_running", c4, 0, "bn_running"),
+              ("c4_swapped_sums", c4, 3, "bn_swap")])
     out = {}
     for key, wl, variant, kind in cases:
         inp = W.make_inputs(wl)
@@ -299,13 +301,17 @@ def widen(torch, args):
             rm, rv = t(rm0), t(rv0)
             ws = torch.empty(B.convT_bn_avgpool_workspace_bytes(wl.x_shape, wl.cout, p, wl.pool), dtype=torch.uint8,
                              device=dev)
-            train = kind == "bn_running"
-            fn = lambda: B.convT_bn_avgpool(x, w, b, gm, bt, wl.eps, wl.pool, out=y, workspace=ws, training=train,
-                                            running_mean=rm, running_var=rv, **kw)
-            algo = lambda: "fused (phase 1" + (" + phase 2)" if train else " with the BN affine)")
+            if kind == "bn_swap":  # the module's second algorithm, batch statistics only
+                fn = lambda: B.convT_bn_avgpool(x, w, b, gm, bt, wl.eps, wl.pool, out=y, workspace=ws, **kw)
+            else:
+                train = kind == "bn_running"
+                fn = lambda: B.convT_bn_avgpool(x, w, b, gm, bt, wl.eps, wl.pool, out=y, workspace=ws,
+                                                training=train, running_mean=rm, running_var=rv, **kw)
+            algo = lambda: B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool)
         nbytes = xb + wb + 4 * y.numel()
         row = dict(workload=wl.description + {"convT": "", "bn_eval": "; BN in eval mode",
-                                              "bn_running": "; training mode + running-statistics update"}[kind],
+                                              "bn_running": "; training mode + running-statistics update",
+                                              "bn_swap": "; swapped-sums algorithm"}[kind],
                    mac=mac, algo_bytes=nbytes)
         for label, v, reps in (("fast", variant, args.steps), ("generic", 1, 3)):
             old = B.set_variant(v)

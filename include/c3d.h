@@ -114,7 +114,10 @@ int conv3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t
 int conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
                          const c3d_conv_params* p, const float* bias, float* y, void* stream);
 
-/* Bytes of device workspace convT_bn_avgpool needs for these arguments. */
+/* Bytes of device workspace convT_bn_avgpool (and convT_bn_avgpool_ex in
+ * training mode) needs for these arguments, whichever kernel
+ * c3d_set_variant selects (the largest of their needs); 0 for invalid
+ * arguments. */
 size_t convT_bn_avgpool_workspace_bytes(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
                                         int32_t pool);
 
@@ -187,8 +190,10 @@ const char* c3d_status_string(int status);
  * the generic direct kernels, 2 = skip the shape-specialised kernels (the
  * flattened-row conv for (k,k,1) kernels and the stride-2/dilation-2
  * sub-lattice transposed conv) so that the general MFMA paths run where
- * they apply.  Returns the previous value.  Process-wide; not for
- * concurrent use with different settings. */
+ * they apply, 3 = as 0 but with the swapped-sums algorithm for
+ * convT_bn_avgpool where it applies (see c3d_convT_bn_avgpool_algo).
+ * Returns the previous value.  Process-wide; not for concurrent use with
+ * different settings. */
 int c3d_set_variant(int variant);
 
 /* Kernel a call would use (under the current variant), for tests and
@@ -198,7 +203,9 @@ enum {
     C3D_ALGO_K1LAST = 1,     /* conv3d, (k,k,1) kernel: flattened-row MFMA GEMM        */
     C3D_ALGO_MFMA333 = 2,    /* conv3d, 3x3x3 stride 1: MFMA implicit GEMM             */
     C3D_ALGO_SUBLATTICE = 3, /* conv_transpose3d, k3 s2 p1 d2: odd sub-lattice on MFMA */
-    C3D_ALGO_PHASE = 4       /* conv_transpose3d, strided: per-output-phase MFMA GEMM  */
+    C3D_ALGO_PHASE = 4,      /* conv_transpose3d, strided: per-output-phase MFMA GEMM  */
+    C3D_ALGO_BN_CELLS = 5,   /* convT_bn_avgpool, k3 s2 p1 pool 4: a thread per 4^3 cell */
+    C3D_ALGO_BN_SWAP = 6     /* convT_bn_avgpool, k3 s2 p1 pool 4: swapped sums        */
 };
 
 /* Writes the C3D_ALGO_* code conv3d_fwd would use to *algo; returns the
@@ -211,6 +218,17 @@ int c3d_conv3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_param
  * most 3 taps per dim whose input offsets span at most 3 positions, and
  * Cin/groups >= 4, Cout/groups >= 8. */
 int c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo);
+
+/* The same for convT_bn_avgpool and convT_bn_avgpool_ex.  The swapped-sums
+ * path ("Kimi-K2.6 l2_p72", the proposal to swap the pooled sum and the conv
+ * sum) takes the page's module (kernel 3, stride 2, padding 1, dilation 1,
+ * no output padding, pool 4, groups 1) with Cin <= 3 and Cout <= 32: pooled
+ * sums from 3x3x3 summed weights, batch statistics from lag correlations of
+ * the input.  It is the second algorithm for the module, selected by
+ * variant 3; the default is the one-thread-per-cell kernel (C3D_ALGO_BN_CELLS),
+ * which measures faster on MI355X. */
+int c3d_convT_bn_avgpool_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t pool,
+                              int32_t* algo);
 
 #ifdef __cplusplus
 }

@@ -129,7 +129,7 @@ def test_fused_op_errors_are_reported_before_launch():
     assert call(pool=0) == 3
     assert call(pool=16) == 2  # ConvT output 15 < pool
     assert call(ws=None) == 4
-    assert call(ws_bytes=ws_need - 1) == 4
+    assert call(ws_bytes=8) == 4  # the query covers every kernel choice; any path needs more than this
     assert call(ws=vp(24580)) == 7  # workspace must be 8-byte aligned
     pc = _p(3, 1, 1)
     assert lib.conv_maxpool_lse_relu(vp(4096), B._shape5((1, 4, 8, 8, 8)), vp(8192), 8, ctypes.byref(pc), None,
@@ -213,6 +213,30 @@ def test_kernel_choice(case):
     old = B.set_variant(variant)
     try:
         got = (B.conv3d_algo if op == "conv3d" else B.conv_transpose3d_algo)(xs, cout, params)
+    finally:
+        B.set_variant(old)
+    assert got == expected
+
+
+BN_ALGO_CASES = [
+    # (x_shape, cout, kernel, stride, pad, pool, variant, expected)
+    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 0, "bn_cells"),   # c4
+    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 3, "bn_swap"),
+    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 2, "bn_cells"),
+    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 1, "direct"),
+    ((2, 4, 8, 8, 8), 16, 3, 2, 1, 4, 3, "bn_cells"),      # Cin 4: outside the swapped-sums path
+    ((2, 3, 8, 8, 8), 40, 3, 2, 1, 4, 3, "bn_cells"),      # Cout 40: outside it too
+    ((2, 3, 8, 8, 8), 16, 3, 2, 1, 2, 3, "direct"),        # pool 2
+    ((2, 3, 8, 8, 8), 16, 3, 1, 1, 4, 0, "direct"),        # stride 1
+]
+
+
+@pytest.mark.parametrize("case", BN_ALGO_CASES, ids=[f"bn-{i}" for i in range(len(BN_ALGO_CASES))])
+def test_bn_kernel_choice(case):
+    xs, cout, k, s, p, pool, variant, expected = case
+    old = B.set_variant(variant)
+    try:
+        got = B.convT_bn_avgpool_algo(xs, cout, B.make_params(k, s, p), pool)
     finally:
         B.set_variant(old)
     assert got == expected

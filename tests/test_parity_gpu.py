@@ -38,6 +38,14 @@ def variant(request):
     B.set_variant(old)
 
 
+@pytest.fixture(params=[0, 1, 3], ids=["auto", "generic", "swapped_sums"])
+def bn_variant(request):
+    """Kernel choices of the c4 module: per-cell (default), generic, swapped sums."""
+    old = B.set_variant(request.param)
+    yield request.param
+    B.set_variant(old)
+
+
 def dev(a):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
@@ -292,13 +300,43 @@ def test_c3_full_size_sampled_and_checkerboard():
     assert torch.equal(y, y2)
 
 
-def test_c4_full_size():
-    wl = W.CONFIGS["c4"]
-    inp = W.make_inputs(wl)
-    y = check_full(wl, inp, "c4")
-    # repeat (the workspace is reused) and compare bit for bit
-    y2 = run_gpu(wl, inp)
-    assert torch.equal(y, y2)
+@pytest.mark.parametrize("v", [0, 3], ids=["per_cell", "swapped_sums"])
+def test_c4_full_size(v):
+    old = B.set_variant(v)
+    try:
+        wl = W.CONFIGS["c4"]
+        p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+        assert B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool) == {0: "bn_cells", 3: "bn_swap"}[v]
+        inp = W.make_inputs(wl)
+        y = check_full(wl, inp, "c4")
+        # repeat (the workspace is reused) and compare bit for bit
+        y2 = run_gpu(wl, inp)
+        assert torch.equal(y, y2)
+    finally:
+        B.set_variant(old)
+
+
+SWAP_MEDIUM = {
+    # the swapped-sums path on ragged shapes and every supported channel count
+    "c4_reduced": W.CONFIGS["c4"].with_(x_shape=(3, 3, 14, 13, 18)),
+    "cin1_cout5": W.CONFIGS["c4"].with_(x_shape=(2, 1, 6, 9, 8), cout=5),
+    "cin2_cout32": W.CONFIGS["c4"].with_(x_shape=(2, 2, 5, 7, 11), cout=32),
+    "exact_windows": W.CONFIGS["c4"].with_(x_shape=(2, 3, 16, 16, 16)),
+    "tiny": W.CONFIGS["c4"].with_(x_shape=(1, 3, 3, 3, 4), cout=7),
+}
+
+
+@pytest.mark.parametrize("name", list(SWAP_MEDIUM))
+def test_c4_swapped_sums_medium(name):
+    wl = SWAP_MEDIUM[name]
+    old = B.set_variant(3)
+    try:
+        p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+        assert B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool) == "bn_swap"
+        print(f"[c4 swapped sums {name}] {wl}", flush=True)
+        check_full(wl, W.make_inputs(wl), name)
+    finally:
+        B.set_variant(old)
 
 
 def test_c5_full_size_sampled():
@@ -334,7 +372,8 @@ def _bn_eval_gpu(wl, inp, rm, rv):
 
 
 @pytest.mark.parametrize("name", list(BN_EVAL))
-def test_bn_eval_mode(name, variant):
+def test_bn_eval_mode(name, bn_variant):
+    variant = bn_variant
     wl = BN_EVAL[name]
     inp = W.make_inputs(wl)
     rm, rv = W.make_running_stats(wl.cout, 17)
@@ -358,7 +397,7 @@ def test_bn_eval_mode_c4_full_size():
 
 
 @pytest.mark.parametrize("name", ["c4_reduced", "generic_pool2_groups"])
-def test_bn_running_statistics_update(name, variant):
+def test_bn_running_statistics_update(name, bn_variant):
     wl = BN_EVAL[name]
     inp = W.make_inputs(wl)
     rm0, rv0 = W.make_running_stats(wl.cout, 23)

@@ -26,9 +26,9 @@ EXPORTS = ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_
            "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
            "convT_bn_avgpool_workspace_bytes", "convT_bn_avgpool", "convT_bn_avgpool_ex", "conv_maxpool_lse_relu",
            "c3d_status_string",
-           "c3d_set_variant", "c3d_conv3d_algo", "c3d_conv_transpose3d_algo")
+           "c3d_set_variant", "c3d_conv3d_algo", "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo")
 
-ALGO = {0: "direct", 1: "k1last", 2: "mfma333", 3: "sublattice", 4: "phase"}
+ALGO = {0: "direct", 1: "k1last", 2: "mfma333", 3: "sublattice", 4: "phase", 5: "bn_cells", 6: "bn_swap"}
 
 
 class C3DError(RuntimeError):
@@ -101,11 +101,12 @@ def _lib():
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.c3d_conv3d_algo.argtypes = [i64p, i64, P, i32p]
     lib.c3d_conv_transpose3d_algo.argtypes = [i64p, i64, P, i32p]
+    lib.c3d_convT_bn_avgpool_algo.argtypes = [i64p, i64, P, ctypes.c_int32, i32p]
     for name in ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_bn_avgpool_out_shape",
                  "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
                  "convT_bn_avgpool", "convT_bn_avgpool_ex", "conv_maxpool_lse_relu", "c3d_set_variant",
                  "c3d_conv3d_algo",
-                 "c3d_conv_transpose3d_algo"):
+                 "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -149,7 +150,8 @@ def _check(st: int, where: str):
 
 def set_variant(variant: int) -> int:
     """0 = automatic kernel choice, 1 = force the generic direct kernels,
-    2 = skip the shape-specialised kernels (general MFMA paths where they apply)."""
+    2 = skip the shape-specialised kernels (general MFMA paths where they apply),
+    3 = automatic, but the swapped-sums algorithm for convT_bn_avgpool where it applies."""
     return int(_lib().c3d_set_variant(int(variant)))
 
 
@@ -158,6 +160,14 @@ def conv3d_algo(x_shape, cout: int, params: ConvParams) -> str:
     v = ctypes.c_int32(-1)
     _check(_lib().c3d_conv3d_algo(_shape5(x_shape), int(cout), ctypes.byref(params), ctypes.byref(v)),
            "c3d_conv3d_algo")
+    return ALGO[v.value]
+
+
+def convT_bn_avgpool_algo(x_shape, cout: int, params: ConvParams, pool: int) -> str:
+    """Name of the kernel convT_bn_avgpool(_ex) would run for these arguments (host-only query)."""
+    v = ctypes.c_int32(-1)
+    _check(_lib().c3d_convT_bn_avgpool_algo(_shape5(x_shape), int(cout), ctypes.byref(params), int(pool),
+                                            ctypes.byref(v)), "c3d_convT_bn_avgpool_algo")
     return ALGO[v.value]
 
 

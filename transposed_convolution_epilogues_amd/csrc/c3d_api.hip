@@ -96,15 +96,27 @@ int hip_status(hipError_t e) { return e == hipSuccess ? C3D_OK : C3D_ERR_HIP; }
 int conv3d_algo(const Geom& g) {
     const int v = g_variant.load();
     if (v == 1) return C3D_ALGO_DIRECT;
-    if (v == 0 && c3d::conv_k1last_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_K1LAST;
+    if ((v == 0 || v == 3) && c3d::conv_k1last_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_K1LAST;
     if (c3d::conv3x3x3_mfma_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_MFMA333;
+    return C3D_ALGO_DIRECT;
+}
+
+// c4 module: one thread per 4x4x4 cell (variants 0 and 2), the swapped sums
+// (variant 3; measured slower on MI355X, kept as the second algorithm),
+// generic (variant 1)
+int bn_algo(const PoolGeom& pg) {
+    const int v = g_variant.load();
+    if (v == 1) return C3D_ALGO_DIRECT;
+    if (v == 3 && c3d::convT_bn_swap_supported(pg, nullptr)) return C3D_ALGO_BN_SWAP;
+    if (c3d::convT_bn_pool_fast_supported(pg, nullptr)) return C3D_ALGO_BN_CELLS;
     return C3D_ALGO_DIRECT;
 }
 
 int convT_algo(const Geom& g) {
     const int v = g_variant.load();
     if (v == 1) return C3D_ALGO_DIRECT;
-    if (v == 0 && c3d::convT_s2_sublattice_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_SUBLATTICE;
+    if ((v == 0 || v == 3) && c3d::convT_s2_sublattice_supported(g, nullptr, nullptr, nullptr))
+        return C3D_ALGO_SUBLATTICE;
     if (c3d::convT_phase_mfma_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_PHASE;
     return C3D_ALGO_DIRECT;
 }
@@ -224,6 +236,19 @@ int c3d_conv3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_param
     return C3D_OK;
 }
 
+int c3d_convT_bn_avgpool_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t pool,
+                              int32_t* algo) {
+    if (!algo) return C3D_ERR_NULL;
+    Geom g;
+    PoolGeom pg;
+    int st = resolve(x_shape, cout, p, true, &g);
+    if (st) return st;
+    st = resolve_pool(g, pool, &pg);
+    if (st) return st;
+    *algo = bn_algo(pg);
+    return C3D_OK;
+}
+
 int c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo) {
     if (!algo) return C3D_ERR_NULL;
     Geom g;
@@ -238,8 +263,12 @@ size_t convT_bn_avgpool_workspace_bytes(const int64_t x_shape[5], int64_t cout, 
     Geom g;
     PoolGeom pg;
     if (resolve(x_shape, cout, p, true, &g) || resolve_pool(g, pool, &pg)) return 0;
-    // two float64 partials (sum, sum of squares) per phase-1 block and channel
-    return c3d::convT_bn_pool_partials(pg, 0) * (size_t)g.Cout * 2 * sizeof(double);
+    // two float64 partials (sum, sum of squares) per phase-1 block and channel,
+    // or the swapped-sums path's partials, whichever is larger (the kernel
+    // choice can change with c3d_set_variant)
+    const size_t direct = c3d::convT_bn_pool_partials(pg, 0) * (size_t)g.Cout * 2 * sizeof(double);
+    const size_t swap = c3d::convT_bn_swap_supported(pg, nullptr) ? c3d::convT_bn_swap_workspace_bytes(pg) : 0;
+    return direct > swap ? direct : swap;
 }
 
 int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
@@ -264,25 +293,37 @@ int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w
     st = resolve_pool(g, pool, &pg);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    const bool fast = g_variant.load() != 1 && c3d::convT_bn_pool_fast_supported(pg, x);
+    const int algo = bn_algo(pg);
     if (!training) {
         // eval mode: one pass, the BN affine with the running statistics applied to the pooled values
         const c3d::BnEval ev{gamma, beta, running_mean, running_var, conv_bias, eps};
-        return hip_status(fast ? c3d::launch_convT_bn_pool_phase1_fast(x, w, y, nullptr, pg, ev, s)
-                               : c3d::launch_convT_bn_pool_phase1_direct(x, w, y, nullptr, pg, ev, s));
+        switch (algo) {
+            case C3D_ALGO_BN_SWAP: return hip_status(c3d::launch_convT_bn_swap(x, w, y, nullptr, pg, ev, nullptr, s));
+            case C3D_ALGO_BN_CELLS: return hip_status(c3d::launch_convT_bn_pool_phase1_fast(x, w, y, nullptr, pg, ev, s));
+            default: return hip_status(c3d::launch_convT_bn_pool_phase1_direct(x, w, y, nullptr, pg, ev, s));
+        }
     }
     if (update && g.N * g.O[0] * g.O[1] * g.O[2] < 2) return C3D_ERR_SHAPE;  // no unbiased variance
     const size_t parts = c3d::convT_bn_pool_partials(pg, 0);
-    const size_t need = parts * (size_t)g.Cout * 2 * sizeof(double);
+    const size_t need = algo == C3D_ALGO_BN_SWAP ? c3d::convT_bn_swap_workspace_bytes(pg)
+                                                 : parts * (size_t)g.Cout * 2 * sizeof(double);
     if (!ws || ws_bytes < need) return C3D_ERR_WORKSPACE;
     if (((uintptr_t)ws & 7u) != 0) return C3D_ERR_ALIGN;
     double* part = (double*)ws;
+    int64_t nparts = (int64_t)parts;
     const c3d::BnEval none{nullptr, nullptr, nullptr, nullptr, nullptr, 0.f};
-    const hipError_t e = fast ? c3d::launch_convT_bn_pool_phase1_fast(x, w, y, part, pg, none, s)
-                              : c3d::launch_convT_bn_pool_phase1_direct(x, w, y, part, pg, none, s);
+    hipError_t e;
+    if (algo == C3D_ALGO_BN_SWAP) {
+        e = c3d::launch_convT_bn_swap(x, w, y, part, pg, none, &part, s);  // part -> the per-channel finals
+        nparts = 1;
+    } else if (algo == C3D_ALGO_BN_CELLS) {
+        e = c3d::launch_convT_bn_pool_phase1_fast(x, w, y, part, pg, none, s);
+    } else {
+        e = c3d::launch_convT_bn_pool_phase1_direct(x, w, y, part, pg, none, s);
+    }
     if (e != hipSuccess) return C3D_ERR_HIP;
     const c3d::BnRunning run{update ? running_mean : nullptr, update ? running_var : nullptr, momentum};
-    return hip_status(c3d::launch_bn_pool_phase2(y, part, (int64_t)parts, conv_bias, gamma, beta, eps, batch_mean,
+    return hip_status(c3d::launch_bn_pool_phase2(y, part, nparts, conv_bias, gamma, beta, eps, batch_mean,
                                                  batch_var, run, pg, s));
 }
 
@@ -305,7 +346,7 @@ int conv_maxpool_lse_relu(const float* x, const int64_t x_shape[5], const float*
     st = resolve_pool(g, pool, &pg);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (g_variant.load() == 0 && c3d::conv_pool_lse_mfma_supported(pg, x, w))
+    if (g_variant.load() != 1 && c3d::conv_pool_lse_mfma_supported(pg, x, w))
         return hip_status(c3d::launch_conv_pool_lse_mfma(x, w, bias, y, pg, s));
     return hip_status(c3d::launch_conv_pool_lse_relu_direct(x, w, bias, y, pg, s));
 }

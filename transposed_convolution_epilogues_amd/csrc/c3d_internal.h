@@ -91,6 +91,15 @@ hipError_t launch_convT_phase_mfma(const float* x, const float* w, const float* 
 bool conv_k1last_supported(const Geom& g, const void* x, const void* w, const void* y);
 hipError_t launch_conv_k1last(const float* x, const float* w, const float* bias, float* y, const Geom& g,
                               hipStream_t st);
+// The page's module (k3 s2 p1, pool 4, Cin <= 3, Cout <= 32) with the sums
+// swapped: pooled sums from summed weights, batch statistics from lag
+// correlations of the input.  Training mode leaves one (sum, sum of squares)
+// part per channel at *stats_out (inside ws) for phase 2; eval mode (ev set)
+// writes the final output and uses no workspace.
+bool convT_bn_swap_supported(const PoolGeom& pg, const void* x);
+size_t convT_bn_swap_workspace_bytes(const PoolGeom& pg);
+hipError_t launch_convT_bn_swap(const float* x, const float* w, float* y, double* ws, const PoolGeom& pg,
+                                const BnEval& ev, double** stats_out, hipStream_t st);
 bool convT_bn_pool_fast_supported(const PoolGeom& pg, const void* x);
 hipError_t launch_convT_bn_pool_phase1_fast(const float* x, const float* w, float* y, double* ws,
                                             const PoolGeom& pg, const BnEval& ev, hipStream_t st);

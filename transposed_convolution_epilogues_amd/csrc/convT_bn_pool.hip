@@ -26,6 +26,7 @@ namespace c3d {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kRedChannels = 16;  // channels whose wave partials wait in LDS for one block reduction
 
 __device__ __forceinline__ double wave_sum_d(double v) {
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void convT_bn_pool_phase1_kernel(const fl
                                                                         float* __restrict__ y,
                                                                         double* __restrict__ ws, PoolGeom pg,
                                                                         int64_t blocks_per_plane, BnEval ev) {
-    __shared__ double red[kThreads / 64][2];
+    __shared__ double red[kRedChannels][kThreads / 64][2];
     const Geom& g = pg.g;
     const int64_t cells = pg.C[0] * pg.C[1] * pg.C[2];
     const int64_t n = blockIdx.x / blocks_per_plane;
@@ -119,24 +120,28 @@ __global__ __launch_bounds__(kThreads) void convT_bn_pool_phase1_kernel(const fl
             continue;
         }
         if (full) *yo = win * (1.f / 64.f);
-        // block partial of (sum, sum of squares) for this channel
-        double s1 = wave_sum_d((double)win);
-        double s2 = wave_sum_d(sq);
+        // wave partial of (sum, sum of squares) for this channel; the block
+        // reduction over waves waits until every channel is done
+        const double s1 = wave_sum_d((double)win);
+        const double s2 = wave_sum_d(sq);
         if (lane == 0) {
-            red[wv][0] = s1;
-            red[wv][1] = s2;
+            red[oc % kRedChannels][wv][0] = s1;
+            red[oc % kRedChannels][wv][1] = s2;
         }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            for (int i = 1; i < kThreads / 64; ++i) {
-                s1 += red[i][0];
-                s2 += red[i][1];
+        if (oc % kRedChannels == kRedChannels - 1 || oc == (int)g.Cout - 1) {
+            // flush a group of kRedChannels channels (workgroup-uniform)
+            __syncthreads();
+            const int base = oc - oc % kRedChannels;
+            const int cnt = oc - base + 1;
+            if (threadIdx.x < 2 * cnt) {
+                const int c = threadIdx.x >> 1, k = threadIdx.x & 1;
+                double v = 0.0;
+                for (int i = 0; i < kThreads / 64; ++i) v += red[c][i][k];
+                const int64_t part = (int64_t)(base + c) * parts + n * blocks_per_plane + bip;
+                ws[2 * part + k] = v;
             }
-            const int64_t part = (int64_t)oc * parts + n * blocks_per_plane + bip;
-            ws[2 * part] = s1;
-            ws[2 * part + 1] = s2;
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
