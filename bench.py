@@ -266,8 +266,9 @@ def calibrate_copy(torch):
 def widen(torch, args):
     """Work beyond the five configurations, each timed through its automatic
     kernel and through the generic kernels for comparison:
-      - transposed convs on the per-output-phase MFMA path, and the c3 module
-        through that general path instead of its sub-lattice kernel;
+      - transposed convs on the per-output-phase MFMA path, the c3 module
+        through that general path instead of its sub-lattice kernel, and both
+        through the LDS-scatter algorithm;
       - the c4 module with BatchNorm in eval mode (running statistics), in
         training mode with the running-statistics update, and through its
         swapped-sums algorithm."""
@@ -279,6 +280,7 @@ def widen(torch, args):
     B.library()
     c4 = W.CONFIGS["c4"]
     cases = ([(k, wl, 0, "convT") for k, wl in W.WIDEN.items()] + [("c3_phase", W.CONFIGS["c3"], 2, "convT")] +
+             [("t1_scatter", W.WIDEN["t1"], 4, "convT"), ("c3_scatter", W.CONFIGS["c3"], 4, "convT")] +
              [("c4_eval", c4, 0, "bn_eval"), ("c4_train_running", c4, 0, "bn_running"),
               ("c4_swapped_sums", c4, 3, "bn_swap")])
     out = {}

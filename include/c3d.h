@@ -191,7 +191,11 @@ const char* c3d_status_string(int status);
  * flattened-row conv for (k,k,1) kernels and the stride-2/dilation-2
  * sub-lattice transposed conv) so that the general MFMA paths run where
  * they apply, 3 = as 0 but with the swapped-sums algorithm for
- * convT_bn_avgpool where it applies (see c3d_convT_bn_avgpool_algo).
+ * convT_bn_avgpool where it applies (see c3d_convT_bn_avgpool_algo), 4 = as
+ * 0 but conv_transpose3d_fwd scatters into an LDS output tile
+ * (C3D_ALGO_SCATTER: "Kimi-K2.6 l1_p77", the scatter form, which needs no
+ * atomics within one tap offset because the input-to-output map is
+ * injective there; LDS-bound, the second algorithm to compare against).
  * Returns the previous value.  Process-wide; not for concurrent use with
  * different settings. */
 int c3d_set_variant(int variant);
@@ -205,7 +209,8 @@ enum {
     C3D_ALGO_SUBLATTICE = 3, /* conv_transpose3d, k3 s2 p1 d2: odd sub-lattice on MFMA */
     C3D_ALGO_PHASE = 4,      /* conv_transpose3d, strided: per-output-phase MFMA GEMM  */
     C3D_ALGO_BN_CELLS = 5,   /* convT_bn_avgpool, k3 s2 p1 pool 4: a thread per 4^3 cell */
-    C3D_ALGO_BN_SWAP = 6     /* convT_bn_avgpool, k3 s2 p1 pool 4: swapped sums        */
+    C3D_ALGO_BN_SWAP = 6,    /* convT_bn_avgpool, k3 s2 p1 pool 4: swapped sums        */
+    C3D_ALGO_SCATTER = 7     /* conv_transpose3d: scatter into an LDS output tile      */
 };
 
 /* Writes the C3D_ALGO_* code conv3d_fwd would use to *algo; returns the

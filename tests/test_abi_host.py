@@ -203,6 +203,9 @@ ALGO_CASES = [
     ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 1, 1, 2, 0, 1, 0, "direct"),          # offsets span 4
     ("conv_transpose3d", (2, 3, 8, 8, 8), 32, 3, 2, 1, 1, 0, 1, 0, "direct"),           # Cin/groups < 4
     ("conv_transpose3d", (2, 16, 8, 8, 8), 4, 3, 2, 1, 1, 0, 1, 0, "direct"),           # Cout/groups < 8
+    ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 4, "scatter"),     # variant 4
+    ("conv_transpose3d", (2, 3, 8, 8, 8), 4, 3, 5, 1, 1, 0, 1, 4, "scatter"),
+    ("conv3d", (16, 3, 256, 256, 10), 64, (3, 3, 1), 1, 0, 1, 0, 1, 4, "k1last"),       # conv unaffected
 ]
 
 

@@ -214,6 +214,31 @@ def test_convT_widen_full_size_sampled(key):
     assert torch.equal(y, y2)
 
 
+# ------------------------------ transposed conv, LDS scatter (second algorithm)
+def test_convT_scatter_random():
+    cases = _random_cases("conv_transpose3d", 20, 12) + _phase_cases(10, 13)  # drawn under the default variant
+    old = B.set_variant(4)
+    try:
+        for i, wl in enumerate(cases):
+            p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+            assert B.conv_transpose3d_algo(wl.x_shape, wl.cout, p) == "scatter"
+            print(f"[convT scatter] case {i}: {wl}", flush=True)
+            check_full(wl, W.make_inputs(wl), f"convT scatter #{i}")
+    finally:
+        B.set_variant(old)
+
+
+@pytest.mark.parametrize("name", list(PHASE_MEDIUM) + ["convT_s2p1d2_cout80", "convT_s2p1d2_bias"])
+def test_convT_scatter_medium(name):
+    wl = PHASE_MEDIUM.get(name) or MEDIUM[name]
+    old = B.set_variant(4)
+    try:
+        print(f"[convT scatter medium {name}] {wl}", flush=True)
+        check_full(wl, W.make_inputs(wl), name)
+    finally:
+        B.set_variant(old)
+
+
 # ----------------------------------------------- medium shapes (many tiles)
 MEDIUM = {
     # the fast paths' shapes, reduced so the oracle finishes in seconds, with ragged tails

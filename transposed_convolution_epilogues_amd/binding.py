@@ -28,7 +28,8 @@ EXPORTS = ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_
            "c3d_status_string",
            "c3d_set_variant", "c3d_conv3d_algo", "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo")
 
-ALGO = {0: "direct", 1: "k1last", 2: "mfma333", 3: "sublattice", 4: "phase", 5: "bn_cells", 6: "bn_swap"}
+ALGO = {0: "direct", 1: "k1last", 2: "mfma333", 3: "sublattice", 4: "phase", 5: "bn_cells", 6: "bn_swap",
+        7: "scatter"}
 
 
 class C3DError(RuntimeError):
@@ -151,7 +152,8 @@ def _check(st: int, where: str):
 def set_variant(variant: int) -> int:
     """0 = automatic kernel choice, 1 = force the generic direct kernels,
     2 = skip the shape-specialised kernels (general MFMA paths where they apply),
-    3 = automatic, but the swapped-sums algorithm for convT_bn_avgpool where it applies."""
+    3 = automatic, but the swapped-sums algorithm for convT_bn_avgpool where it applies,
+    4 = automatic, but conv_transpose3d_fwd scatters into an LDS output tile."""
     return int(_lib().c3d_set_variant(int(variant)))
 
 

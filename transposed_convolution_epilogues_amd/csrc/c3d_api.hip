@@ -92,11 +92,13 @@ int hip_status(hipError_t e) { return e == hipSuccess ? C3D_OK : C3D_ERR_HIP; }
 // Kernel choice (the C3D_ALGO_* codes of c3d.h).  Variant 1 forces the
 // generic kernels; variant 2 skips the shape-specialised ones (c2's
 // flattened-row conv, c3's sub-lattice transposed conv) so the general fast
-// paths can be compared with them.
+// paths can be compared with them; variants 3 and 4 select the second
+// algorithms of the c4 module (swapped sums) and of the transposed conv
+// (LDS scatter).
 int conv3d_algo(const Geom& g) {
     const int v = g_variant.load();
     if (v == 1) return C3D_ALGO_DIRECT;
-    if ((v == 0 || v == 3) && c3d::conv_k1last_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_K1LAST;
+    if (v != 2 && c3d::conv_k1last_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_K1LAST;
     if (c3d::conv3x3x3_mfma_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_MFMA333;
     return C3D_ALGO_DIRECT;
 }
@@ -115,7 +117,8 @@ int bn_algo(const PoolGeom& pg) {
 int convT_algo(const Geom& g) {
     const int v = g_variant.load();
     if (v == 1) return C3D_ALGO_DIRECT;
-    if ((v == 0 || v == 3) && c3d::convT_s2_sublattice_supported(g, nullptr, nullptr, nullptr))
+    if (v == 4 && c3d::convT_scatter_supported(g)) return C3D_ALGO_SCATTER;
+    if (v != 2 && c3d::convT_s2_sublattice_supported(g, nullptr, nullptr, nullptr))
         return C3D_ALGO_SUBLATTICE;
     if (c3d::convT_phase_mfma_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_PHASE;
     return C3D_ALGO_DIRECT;
@@ -223,6 +226,7 @@ int conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const float* 
     switch (convT_algo(g)) {
         case C3D_ALGO_SUBLATTICE: return hip_status(c3d::launch_convT_s2_sublattice(x, w, bias, y, g, s));
         case C3D_ALGO_PHASE: return hip_status(c3d::launch_convT_phase_mfma(x, w, bias, y, g, s));
+        case C3D_ALGO_SCATTER: return hip_status(c3d::launch_convT_scatter(x, w, bias, y, g, s));
         default: return hip_status(c3d::launch_convT_gather(x, w, bias, y, g, s));
     }
 }
