@@ -193,6 +193,7 @@ ALGO_CASES = [
     ("conv3d", (16, 3, 256, 256, 10), 64, (3, 3, 1), 1, 0, 1, 0, 1, 1, "direct"),       # forced generic
     ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 0, "sublattice"),  # c3
     ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 2, "phase"),       # c3, general path
+    ("conv_transpose3d", (1, 8, 4, 4, 4), 1025, 3, 2, 1, 2, 0, 1, 0, "phase"),          # bias table limit
     ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 1, "direct"),
     ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 2, 1, 1, 1, 1, 0, "phase"),           # dense phases
     ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 4, 2, 1, 1, 0, 1, 0, "phase"),

@@ -257,6 +257,7 @@ MEDIUM = {
     "conv3d_k333_pad2": W.CONFIGS["c1"].with_(x_shape=(1, 9, 3, 5, 33), cout=16, pad=2),
     "convT_s2p1d2_cout80": W.CONFIGS["c3"].with_(x_shape=(1, 8, 3, 5, 6), cout=80),
     "convT_s2p1d2_bias": W.CONFIGS["c3"].with_(x_shape=(2, 5, 3, 4, 33), cout=16, bias=True),
+    "convT_s2p1d2_bias_cout72": W.CONFIGS["c3"].with_(x_shape=(3, 6, 3, 3, 5), cout=72, bias=True),
     "conv3d_k331_bias_dil": W.CONFIGS["c2"].with_(x_shape=(1, 2, 9, 12, 5), cout=20, dilation=(2, 2, 1),
                                                   bias=True),
     "convT_bn_pool_cin1_cout5": W.CONFIGS["c4"].with_(x_shape=(2, 1, 6, 9, 8), cout=5),

@@ -10,10 +10,16 @@
 // sub-lattice is a stride-1, pad-1 conv3d of x with the flipped,
 // channel-transposed weights Wf[oc][ic][k'] = W[ic][oc][2 - k'] over a grid of
 // the input's own size (the valid-residue decomposition the page arrives at,
-// with one non-empty residue per dim).  Each workgroup computes its
-// sub-lattice tile and then writes its whole box of output rows, odd positions
-// from the tile and everything else as the bias, so each output element is
-// written once with coalesced stores.
+// with one non-empty residue per dim).
+//
+// Every output element is written once.  The even planes of the output hold
+// only the bias and do not depend on any tile, so they are shared out over the
+// whole grid, not by tile: during K-loop unit u, workgroup b writes chunk
+// u * gridDim + b of the even planes taken in memory order.  The workgroups
+// resident at one time then write adjacent chunks, a compact write front that
+// HBM absorbs far faster than every workgroup writing its own scattered box.
+// After the K loop a workgroup writes the odd planes of its box as whole
+// slabs, odd positions from the tile and the rest as the bias.
 #include "conv333_mfma.h"
 
 namespace c3d {
@@ -25,6 +31,7 @@ constexpr int kMT = 2;                    // tile depth: the result staging belo
 constexpr int TD = Geo<kMT>::TD;
 constexpr int kStage = TD * TH * TW + 1;  // LDS floats per channel of the result staging (padded)
 constexpr int kLdsFloats = Geo<kMT>::LDS_MAIN > OCB * kStage ? Geo<kMT>::LDS_MAIN : OCB * kStage;
+constexpr int kMaxBiasLds = 1024;  // output channels whose bias the even-plane pass keeps in LDS
 
 // n / d for 0 <= n, d < 2^22 from a float reciprocal: the rounded product is
 // within 1/2 of n / d, so its truncation is off by at most one, which one
@@ -134,11 +141,6 @@ __device__ __forceinline__ void store_runs(const Box& b, const RunSet& rs, int g
     }
 }
 
-struct BiasValue {
-    const float* sbias;
-    __device__ float operator()(int oc, int, int, int, bool) const { return sbias[oc]; }
-};
-
 // kLattice = 1: box coordinate (id, ih, c) is tile voxel (id, ih, c).
 // kLattice = 2: the box starts at even destination coordinates, so a box
 // coordinate is odd exactly when the destination coordinate is; odd 2m + 1
@@ -155,21 +157,52 @@ struct TileValue {
     }
 };
 
-// Side work of the transposed conv: during the K loop, the units share out
-// the bias-only part of the box (even planes, and the even rows of odd
-// planes), which does not depend on the result.
-struct BiasSideWork {
-    const Box* b;
-    const RunSet* even_planes;
-    const RunSet* even_rows;
-    const float* sbias;
+// Side work of the transposed conv: the even planes of the whole output,
+// which hold only the bias.  They are taken as runs of P = Y1 * Y2 floats
+// (plane 2j of sample-channel nc), each cut into SL 16-byte aligned slots
+// counted from the run's address.  The total is split into n * gridDim chunks
+// of near-equal size; unit u of workgroup b writes chunk u * gridDim + b.
+struct EvenPlanes {
+    float* y;
+    const float* bias;  // LDS copy of all Cout biases, or null for none
+    int64_t P, vol;     // floats per plane and per (sample, channel) volume
+    int64_t total;      // slots over all even planes
+    int nEven, SL, Cout;
     __device__ void operator()(int64_t u, int64_t n) const {
-        const int n_a = even_planes->items;
-        const int64_t total = n_a + even_rows->items;
-        const int g0 = (int)(total * u / n), g1 = (int)(total * (u + 1) / n);
-        const BiasValue bias{sbias};
-        if (g0 < n_a) store_runs(*b, *even_planes, g0, g1 < n_a ? g1 : n_a, bias);
-        if (g1 > n_a) store_runs(*b, *even_rows, (g0 > n_a ? g0 : n_a) - n_a, g1 - n_a, bias);
+        const int64_t nch = n * (int64_t)gridDim.x, chunk = u * (int64_t)gridDim.x + blockIdx.x;
+        const int64_t q = total / nch, rem = total - q * nch;
+        const int64_t g0 = chunk * q + (chunk < rem ? chunk : rem);
+        const int cnt = (int)(q + (chunk < rem ? 1 : 0));
+        const int64_t r0 = g0 / SL;
+        const int s0 = (int)(g0 - r0 * SL);
+        const int64_t nc0 = r0 / nEven;
+        const int j0 = (int)(r0 - nc0 * nEven);
+        const int c0 = (int)(nc0 % Cout);
+        const Div div_sl(SL), div_ne(nEven), div_c(Cout);
+        for (int l = threadIdx.x; l < cnt; l += kThreads) {
+            const int sl = s0 + l;  // < SL + cnt < 2^22 (checked on the host)
+            const int dr = div_sl.quot(sl);
+            const int s = sl - dr * SL;
+            const int jj = j0 + dr;
+            const int dnc = div_ne.quot(jj);
+            const int j = jj - dnc * nEven;
+            const int64_t nc = nc0 + dnc;
+            float* run = y + nc * vol + (int64_t)(2 * j) * P;
+            const int e0 = 4 * s - (int)(((uintptr_t)run >> 2) & 3);
+            float v = 0.f;
+            if (bias) {
+                const int cc = c0 + dnc;
+                v = bias[cc - div_c.quot(cc) * Cout];
+            }
+            if (e0 >= 0 && e0 + 3 < P) {
+                const f32x4 o = {v, v, v, v};
+                *reinterpret_cast<f32x4*>(run + e0) = o;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (e0 + k >= 0 && e0 + k < P) run[e0 + k] = v;
+            }
+        }
     }
 };
 
@@ -180,10 +213,13 @@ template <int kMode, int kLattice>
 __global__ __launch_bounds__(kThreads) void conv333_store_kernel(Args a) {
     __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
     __shared__ float sbias[OCB];
+    __shared__ float all_bias[kLattice == 2 ? kMaxBiasLds : 1];
     const Tile t = tile_of<kMT>(a);
     if (threadIdx.x < OCB)
         sbias[threadIdx.x] = (a.bias && t.oc0 + threadIdx.x < a.Cout) ? a.bias[t.oc0 + threadIdx.x] : 0.f;
-    // (the mainloop's first barrier publishes sbias)
+    if (kLattice == 2 && a.bias)
+        for (int c = threadIdx.x; c < a.Cout; c += kThreads) all_bias[c] = a.bias[c];
+    // (the mainloop's first barrier publishes sbias and all_bias)
 
     Box b{};
     {
@@ -213,9 +249,16 @@ __global__ __launch_bounds__(kThreads) void conv333_store_kernel(Args a) {
 
     f32x16 acc[kMT][2];
     if (kLattice == 2) {
-        const RunSet even_planes = make_runs(b, 0, 2, 0, 1, b.full_rows);
-        const RunSet even_rows = make_runs(b, 1, 2, 0, 2, false);
-        mainloop<kMode, kMT>(a, t, lds, acc, BiasSideWork{&b, &even_planes, &even_rows, sbias});
+        EvenPlanes ep;
+        ep.y = a.y;
+        ep.bias = a.bias ? all_bias : nullptr;
+        ep.P = a.Y[1] * a.Y[2];
+        ep.vol = a.Y[0] * ep.P;
+        ep.nEven = (int)((a.Y[0] + 1) / 2);
+        ep.SL = (int)((ep.P + 6) >> 2);
+        ep.total = a.N * a.Cout * ep.nEven * ep.SL;
+        ep.Cout = (int)a.Cout;
+        mainloop<kMode, kMT>(a, t, lds, acc, ep);
     } else {
         mainloop<kMode, kMT>(a, t, lds, acc);
     }
@@ -236,9 +279,9 @@ __global__ __launch_bounds__(kThreads) void conv333_store_kernel(Args a) {
             }
     __syncthreads();
 
-    // the rest of the box: all of it for the plain conv, the odd rows of the
-    // odd planes for the transposed conv
-    const RunSet rest = kLattice == 1 ? make_runs(b, 0, 1, 0, 1, b.full_rows) : make_runs(b, 1, 2, 1, 2, false);
+    // the rest of the box: all of it for the plain conv, its odd planes for
+    // the transposed conv
+    const RunSet rest = make_runs(b, kLattice == 1 ? 0 : 1, kLattice, 0, 1, b.full_rows);
     store_runs(b, rest, 0, rest.items, TileValue<kLattice>{lds, sbias});
 }
 
@@ -287,8 +330,15 @@ hipError_t launch_conv3x3x3_mfma(const float* x, const float* w, const float* bi
 bool convT_s2_sublattice_supported(const Geom& g, const void*, const void*, const void*) {
     for (int j = 0; j < 3; ++j)
         if (g.k[j] != 3 || g.s[j] != 2 || g.d[j] != 2 || g.p[j] != 1 || g.O[j] != 2 * g.S[j] + 1) return false;
-    return g.groups == 1 && mfma333::fits_int32_tiles(g.O[0]) && mfma333::fits_int32_tiles(g.O[1]) &&
-           mfma333::fits_int32_tiles(g.O[2]);
+    if (g.groups != 1 || g.Cout > kMaxBiasLds || !mfma333::fits_int32_tiles(g.O[0]) ||
+        !mfma333::fits_int32_tiles(g.O[1]) || !mfma333::fits_int32_tiles(g.O[2]))
+        return false;
+    // the even-plane pass decodes slot indices below 2^22 with float reciprocals
+    const int64_t P = g.O[1] * g.O[2], SL = (P + 6) >> 2;
+    const int64_t units = 3 * ceil_div(g.Cin, ICC);
+    const int64_t grid = g.N * ceil_div(g.S[0], TD) * ceil_div(g.S[1], TH) * ceil_div(g.S[2], TW) * ceil_div(g.Cout, OCB);
+    const int64_t per_chunk = g.N * g.Cout * ((g.O[0] + 1) / 2) * SL / (units * grid) + 1;
+    return SL + per_chunk < (1 << 22) && g.Cout + per_chunk < (1 << 22);
 }
 
 hipError_t launch_convT_s2_sublattice(const float* x, const float* w, const float* bias, float* y, const Geom& g,
