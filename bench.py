@@ -38,7 +38,7 @@ CSRC = "transposed_convolution_epilogues_amd/csrc/"
 KERNELS = {
     "c2": ("conv_k1last_kernel", [CSRC + "conv_k1last.hip"]),
     "c3": ("conv333_store_kernel", [CSRC + "convT_sublattice.hip", CSRC + "conv333_mfma.h"]),
-    "c4": ("convT_bn_pool_phase1_kernel", [CSRC + "convT_bn_pool.hip"]),
+    "c4": ("convT_bn_pool_mfma_kernel", [CSRC + "convT_bn_pool_mfma.hip"]),
     "c5": ("conv_pool_lse_mfma_kernel", [CSRC + "conv_pool_lse.hip", CSRC + "conv333_mfma.h"]),
 }
 

@@ -195,7 +195,9 @@ const char* c3d_status_string(int status);
  * 0 but conv_transpose3d_fwd scatters into an LDS output tile
  * (C3D_ALGO_SCATTER: "Kimi-K2.6 l1_p77", the scatter form, which needs no
  * atomics within one tap offset because the input-to-output map is
- * injective there; LDS-bound, the second algorithm to compare against).
+ * injective there; LDS-bound, the second algorithm to compare against),
+ * 5 = as 0 but convT_bn_avgpool uses its one-thread-per-cell fp32 kernel
+ * (C3D_ALGO_BN_CELLS) instead of the matrix-core one.
  * Returns the previous value.  Process-wide; not for concurrent use with
  * different settings. */
 int c3d_set_variant(int variant);
@@ -210,7 +212,8 @@ enum {
     C3D_ALGO_PHASE = 4,      /* conv_transpose3d, strided: per-output-phase MFMA GEMM  */
     C3D_ALGO_BN_CELLS = 5,   /* convT_bn_avgpool, k3 s2 p1 pool 4: a thread per 4^3 cell */
     C3D_ALGO_BN_SWAP = 6,    /* convT_bn_avgpool, k3 s2 p1 pool 4: swapped sums        */
-    C3D_ALGO_SCATTER = 7     /* conv_transpose3d: scatter into an LDS output tile      */
+    C3D_ALGO_SCATTER = 7,    /* conv_transpose3d: scatter into an LDS output tile      */
+    C3D_ALGO_BN_MFMA = 8     /* convT_bn_avgpool, k3 s2 p1 pool 4: output phases on MFMA */
 };
 
 /* Writes the C3D_ALGO_* code conv3d_fwd would use to *algo; returns the
@@ -230,8 +233,11 @@ int c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_
  * no output padding, pool 4, groups 1) with Cin <= 3 and Cout <= 32: pooled
  * sums from 3x3x3 summed weights, batch statistics from lag correlations of
  * the input.  It is the second algorithm for the module, selected by
- * variant 3; the default is the one-thread-per-cell kernel (C3D_ALGO_BN_CELLS),
- * which measures faster on MI355X. */
+ * variant 3.  The default for Cin <= 4 and Cout <= 16 is C3D_ALGO_BN_MFMA
+ * (the 8 output-phase classes of [p72]'s parity tables, each a GEMM over
+ * Cin x taps on the matrix cores, pooled and squared in registers); other
+ * Cin <= 4 shapes, or variant 5, take the one-thread-per-cell fp32 kernel
+ * (C3D_ALGO_BN_CELLS). */
 int c3d_convT_bn_avgpool_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t pool,
                               int32_t* algo);
 

@@ -224,12 +224,15 @@ def test_kernel_choice(case):
 
 BN_ALGO_CASES = [
     # (x_shape, cout, kernel, stride, pad, pool, variant, expected)
-    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 0, "bn_cells"),   # c4
+    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 0, "bn_mfma"),    # c4
     ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 3, "bn_swap"),
-    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 2, "bn_cells"),
+    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 2, "bn_mfma"),
+    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 5, "bn_cells"),   # per-cell fp32 kernel on request
     ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 1, "direct"),
-    ((2, 4, 8, 8, 8), 16, 3, 2, 1, 4, 3, "bn_cells"),      # Cin 4: outside the swapped-sums path
-    ((2, 3, 8, 8, 8), 40, 3, 2, 1, 4, 3, "bn_cells"),      # Cout 40: outside it too
+    ((2, 4, 8, 8, 8), 16, 3, 2, 1, 4, 3, "bn_mfma"),       # Cin 4: outside the swapped-sums path
+    ((2, 3, 8, 8, 8), 40, 3, 2, 1, 4, 3, "bn_cells"),      # Cout 40: outside both
+    ((2, 3, 8, 8, 8), 17, 3, 2, 1, 4, 0, "bn_cells"),      # Cout 17: more than one MFMA N tile
+    ((2, 5, 8, 8, 8), 16, 3, 2, 1, 4, 0, "direct"),        # Cin 5
     ((2, 3, 8, 8, 8), 16, 3, 2, 1, 2, 3, "direct"),        # pool 2
     ((2, 3, 8, 8, 8), 16, 3, 1, 1, 4, 0, "direct"),        # stride 1
 ]

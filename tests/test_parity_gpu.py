@@ -38,7 +38,7 @@ def variant(request):
     B.set_variant(old)
 
 
-@pytest.fixture(params=[0, 1, 3], ids=["auto", "generic", "swapped_sums"])
+@pytest.fixture(params=[0, 1, 3, 5], ids=["auto", "generic", "swapped_sums", "per_cell"])
 def bn_variant(request):
     """Kernel choices of the c4 module: per-cell (default), generic, swapped sums."""
     old = B.set_variant(request.param)
@@ -326,13 +326,14 @@ def test_c3_full_size_sampled_and_checkerboard():
     assert torch.equal(y, y2)
 
 
-@pytest.mark.parametrize("v", [0, 3], ids=["per_cell", "swapped_sums"])
+@pytest.mark.parametrize("v", [0, 5, 3], ids=["matrix_cores", "per_cell", "swapped_sums"])
 def test_c4_full_size(v):
     old = B.set_variant(v)
     try:
         wl = W.CONFIGS["c4"]
         p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
-        assert B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool) == {0: "bn_cells", 3: "bn_swap"}[v]
+        assert B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool) == {0: "bn_mfma", 5: "bn_cells",
+                                                                             3: "bn_swap"}[v]
         inp = W.make_inputs(wl)
         y = check_full(wl, inp, "c4")
         # repeat (the workspace is reused) and compare bit for bit
@@ -340,6 +341,27 @@ def test_c4_full_size(v):
         assert torch.equal(y, y2)
     finally:
         B.set_variant(old)
+
+
+MFMA_MEDIUM = {
+    # the matrix-core phase-class path on ragged boxes, every supported input channel count, Cout <= 16
+    "c4_reduced": W.CONFIGS["c4"].with_(x_shape=(3, 3, 14, 13, 18)),
+    "cin1_cout5": W.CONFIGS["c4"].with_(x_shape=(2, 1, 6, 9, 8), cout=5),
+    "cin2_cout12_bias": W.CONFIGS["c4"].with_(x_shape=(1, 2, 17, 5, 6), cout=12, bias=True),
+    "cin4_cout16": W.CONFIGS["c4"].with_(x_shape=(2, 4, 9, 7, 20), cout=16),
+    "exact_windows": W.CONFIGS["c4"].with_(x_shape=(2, 3, 16, 16, 16)),
+    "several_boxes": W.CONFIGS["c4"].with_(x_shape=(1, 3, 40, 36, 20)),
+    "tiny": W.CONFIGS["c4"].with_(x_shape=(1, 3, 3, 3, 4), cout=7),
+}
+
+
+@pytest.mark.parametrize("name", list(MFMA_MEDIUM))
+def test_c4_matrix_core_medium(name):
+    wl = MFMA_MEDIUM[name]
+    p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+    assert B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool) == "bn_mfma"
+    print(f"[c4 matrix cores {name}] {wl}", flush=True)
+    check_full(wl, W.make_inputs(wl), name)
 
 
 SWAP_MEDIUM = {

@@ -29,7 +29,7 @@ EXPORTS = ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_
            "c3d_set_variant", "c3d_conv3d_algo", "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo")
 
 ALGO = {0: "direct", 1: "k1last", 2: "mfma333", 3: "sublattice", 4: "phase", 5: "bn_cells", 6: "bn_swap",
-        7: "scatter"}
+        7: "scatter", 8: "bn_mfma"}
 
 
 class C3DError(RuntimeError):
@@ -153,7 +153,8 @@ def set_variant(variant: int) -> int:
     """0 = automatic kernel choice, 1 = force the generic direct kernels,
     2 = skip the shape-specialised kernels (general MFMA paths where they apply),
     3 = automatic, but the swapped-sums algorithm for convT_bn_avgpool where it applies,
-    4 = automatic, but conv_transpose3d_fwd scatters into an LDS output tile."""
+    4 = automatic, but conv_transpose3d_fwd scatters into an LDS output tile,
+    5 = automatic, but convT_bn_avgpool runs its one-thread-per-cell fp32 kernel."""
     return int(_lib().c3d_set_variant(int(variant)))
 
 

@@ -110,6 +110,7 @@ int bn_algo(const PoolGeom& pg) {
     const int v = g_variant.load();
     if (v == 1) return C3D_ALGO_DIRECT;
     if (v == 3 && c3d::convT_bn_swap_supported(pg, nullptr)) return C3D_ALGO_BN_SWAP;
+    if (v != 5 && c3d::convT_bn_pool_mfma_supported(pg, nullptr)) return C3D_ALGO_BN_MFMA;
     if (c3d::convT_bn_pool_fast_supported(pg, nullptr)) return C3D_ALGO_BN_CELLS;
     return C3D_ALGO_DIRECT;
 }
@@ -268,11 +269,18 @@ size_t convT_bn_avgpool_workspace_bytes(const int64_t x_shape[5], int64_t cout, 
     PoolGeom pg;
     if (resolve(x_shape, cout, p, true, &g) || resolve_pool(g, pool, &pg)) return 0;
     // two float64 partials (sum, sum of squares) per phase-1 block and channel,
-    // or the swapped-sums path's partials, whichever is larger (the kernel
+    // or the swapped-sums path's partials, whichever is largest (the kernel
     // choice can change with c3d_set_variant)
-    const size_t direct = c3d::convT_bn_pool_partials(pg, 0) * (size_t)g.Cout * 2 * sizeof(double);
-    const size_t swap = c3d::convT_bn_swap_supported(pg, nullptr) ? c3d::convT_bn_swap_workspace_bytes(pg) : 0;
-    return direct > swap ? direct : swap;
+    size_t need = c3d::convT_bn_pool_partials(pg, 0) * (size_t)g.Cout * 2 * sizeof(double);
+    if (c3d::convT_bn_pool_mfma_supported(pg, nullptr)) {
+        const size_t m = c3d::convT_bn_pool_mfma_partials(pg) * (size_t)g.Cout * 2 * sizeof(double);
+        need = m > need ? m : need;
+    }
+    if (c3d::convT_bn_swap_supported(pg, nullptr)) {
+        const size_t sw = c3d::convT_bn_swap_workspace_bytes(pg);
+        need = sw > need ? sw : need;
+    }
+    return need;
 }
 
 int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
@@ -303,12 +311,14 @@ int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w
         const c3d::BnEval ev{gamma, beta, running_mean, running_var, conv_bias, eps};
         switch (algo) {
             case C3D_ALGO_BN_SWAP: return hip_status(c3d::launch_convT_bn_swap(x, w, y, nullptr, pg, ev, nullptr, s));
+            case C3D_ALGO_BN_MFMA: return hip_status(c3d::launch_convT_bn_pool_phase1_mfma(x, w, y, nullptr, pg, ev, s));
             case C3D_ALGO_BN_CELLS: return hip_status(c3d::launch_convT_bn_pool_phase1_fast(x, w, y, nullptr, pg, ev, s));
             default: return hip_status(c3d::launch_convT_bn_pool_phase1_direct(x, w, y, nullptr, pg, ev, s));
         }
     }
     if (update && g.N * g.O[0] * g.O[1] * g.O[2] < 2) return C3D_ERR_SHAPE;  // no unbiased variance
-    const size_t parts = c3d::convT_bn_pool_partials(pg, 0);
+    const size_t parts =
+        algo == C3D_ALGO_BN_MFMA ? c3d::convT_bn_pool_mfma_partials(pg) : c3d::convT_bn_pool_partials(pg, 0);
     const size_t need = algo == C3D_ALGO_BN_SWAP ? c3d::convT_bn_swap_workspace_bytes(pg)
                                                  : parts * (size_t)g.Cout * 2 * sizeof(double);
     if (!ws || ws_bytes < need) return C3D_ERR_WORKSPACE;
@@ -320,6 +330,8 @@ int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w
     if (algo == C3D_ALGO_BN_SWAP) {
         e = c3d::launch_convT_bn_swap(x, w, y, part, pg, none, &part, s);  // part -> the per-channel finals
         nparts = 1;
+    } else if (algo == C3D_ALGO_BN_MFMA) {
+        e = c3d::launch_convT_bn_pool_phase1_mfma(x, w, y, part, pg, none, s);
     } else if (algo == C3D_ALGO_BN_CELLS) {
         e = c3d::launch_convT_bn_pool_phase1_fast(x, w, y, part, pg, none, s);
     } else {

@@ -104,6 +104,10 @@ size_t convT_bn_swap_workspace_bytes(const PoolGeom& pg);
 hipError_t launch_convT_bn_swap(const float* x, const float* w, float* y, double* ws, const PoolGeom& pg,
                                 const BnEval& ev, double** stats_out, hipStream_t st);
 bool convT_bn_pool_fast_supported(const PoolGeom& pg, const void* x);
+bool convT_bn_pool_mfma_supported(const PoolGeom& pg, const void* x);
+size_t convT_bn_pool_mfma_partials(const PoolGeom& pg);
+hipError_t launch_convT_bn_pool_phase1_mfma(const float* x, const float* w, float* y, double* ws,
+                                            const PoolGeom& pg, const BnEval& ev, hipStream_t st);
 hipError_t launch_convT_bn_pool_phase1_fast(const float* x, const float* w, float* y, double* ws,
                                             const PoolGeom& pg, const BnEval& ev, hipStream_t st);
 

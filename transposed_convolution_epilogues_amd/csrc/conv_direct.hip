@@ -288,14 +288,24 @@ __global__ __launch_bounds__(kBlock) void bn_pool_phase2_kernel(float* __restric
     }
     __syncthreads();
     const float sc = s_scale, sh = s_shift;
+    // this block's slice [lo, hi) of the pooled positions, in every sample: a
+    // thread owns a position and loads it from 8 samples before storing any
+    constexpr int kBatch = 8;
     const int64_t pp = pg.P[0] * pg.P[1] * pg.P[2];
-    const int64_t per_channel = g.N * pp;
-    const int64_t per_block = ceil_div(per_channel, blocks_per_channel);
-    const int64_t lo = q * per_block, hi = lo + per_block < per_channel ? lo + per_block : per_channel;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) {
-        const int64_t n = i / pp, j = i % pp;
-        float* e = y + (n * g.Cout + c) * pp + j;
-        *e = fmaf(*e, sc, sh);
+    const int64_t per_block = ceil_div(pp, blocks_per_channel);
+    const int64_t lo = q * per_block, hi = lo + per_block < pp ? lo + per_block : pp;
+    const int64_t nstride = g.Cout * pp;
+    for (int64_t j = lo + threadIdx.x; j < hi; j += blockDim.x) {
+        float* yj = y + c * pp + j;
+        for (int64_t n0 = 0; n0 < g.N; n0 += kBatch) {
+            float v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (n0 + u < g.N) v[u] = yj[(n0 + u) * nstride];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (n0 + u < g.N) yj[(n0 + u) * nstride] = fmaf(v[u], sc, sh);
+        }
     }
 }
 
@@ -350,9 +360,11 @@ hipError_t launch_convT_bn_pool_phase1_direct(const float* x, const float* w, fl
 hipError_t launch_bn_pool_phase2(float* y, const double* ws, int64_t parts_per_channel, const float* conv_bias,
                                  const float* gamma, const float* beta, float eps, float* mean_out,
                                  float* var_out, const BnRunning& run, const PoolGeom& pg, hipStream_t st) {
+    // slices of at least kBlock pooled positions of one channel, at most
+    // about 1024 blocks in all (every block also merges its channel's partials)
     const int64_t pp = pg.P[0] * pg.P[1] * pg.P[2];
-    const int64_t per_channel = pg.g.N * pp;
-    int64_t bpc = ceil_div(per_channel, 4 * kBlock);
+    int64_t bpc = ceil_div(pp, kBlock);
+    if (bpc > ceil_div(1024, pg.g.Cout)) bpc = ceil_div(1024, pg.g.Cout);
     if (bpc < 1) bpc = 1;
     const int64_t count = pg.g.N * pg.g.O[0] * pg.g.O[1] * pg.g.O[2];
     hipLaunchKernelGGL(bn_pool_phase2_kernel, dim3((unsigned)(bpc * pg.g.Cout)), dim3(kBlock), 0, st, y, ws,
