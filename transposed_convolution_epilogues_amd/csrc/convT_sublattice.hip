@@ -12,14 +12,17 @@
 // the input's own size (the valid-residue decomposition the page arrives at,
 // with one non-empty residue per dim).
 //
-// Every output element is written once.  The even planes of the output hold
-// only the bias and do not depend on any tile, so they are shared out over the
-// whole grid, not by tile: during K-loop unit u, workgroup b writes chunk
-// u * gridDim + b of the even planes taken in memory order.  The workgroups
-// resident at one time then write adjacent chunks, a compact write front that
-// HBM absorbs far faster than every workgroup writing its own scattered box.
-// After the K loop a workgroup writes the odd planes of its box as whole
-// slabs, odd positions from the tile and the rest as the bias.
+// Every output element is written once.  The even planes, and the even rows
+// of the odd planes, hold only the bias and do not depend on any tile, so they
+// are shared out over the whole grid, not by tile: they are cut into units of
+// one (sample, channel) volume's plane pair (plane 2k whole, the even rows of
+// plane 2k + 1), and during K-loop unit u workgroup b writes chunk
+// u * gridDim + b of those units in memory order.  The workgroups resident at
+// one time then write adjacent chunks, a compact write front that HBM absorbs
+// far faster than every workgroup writing its own scattered box.  After the K
+// loop a workgroup writes the odd rows of the odd planes of its box, odd
+// positions from the tile and even positions as the bias, staging the tile in
+// LDS 32 output channels at a time.
 #include "conv333_mfma.h"
 
 namespace c3d {
@@ -27,10 +30,10 @@ namespace {
 
 using namespace mfma333;
 
-constexpr int kMT = 2;                    // tile depth: the result staging below must fit in LDS
+constexpr int kMT = 4;  // tile depth; the result staging (32 channels at a time) reuses the K-loop LDS
 constexpr int TD = Geo<kMT>::TD;
 constexpr int kStage = TD * TH * TW + 1;  // LDS floats per channel of the result staging (padded)
-constexpr int kLdsFloats = Geo<kMT>::LDS_MAIN > OCB * kStage ? Geo<kMT>::LDS_MAIN : OCB * kStage;
+constexpr int kLdsFloats = Geo<kMT>::LDS_MAIN > 32 * kStage ? Geo<kMT>::LDS_MAIN : 32 * kStage;
 constexpr int kMaxBiasLds = 1024;  // output channels whose bias the even-plane pass keeps in LDS
 
 // n / d for 0 <= n, d < 2^22 from a float reciprocal: the rounded product is
@@ -157,50 +160,46 @@ struct TileValue {
     }
 };
 
-// Side work of the transposed conv: the even planes of the whole output,
-// which hold only the bias.  They are taken as runs of P = Y1 * Y2 floats
-// (plane 2j of sample-channel nc), each cut into SL 16-byte aligned slots
-// counted from the run's address.  The total is split into n * gridDim chunks
-// of near-equal size; unit u of workgroup b writes chunk u * gridDim + b.
+// Side work of the transposed conv: the bias-only outputs of the whole grid.
+// Unit k of volume nc (sample-channel) is plane 2k whole and the even rows of
+// plane 2k + 1; each run is cut into 16-byte aligned slots counted from its
+// address.  The units are split into n * gridDim chunks of near-equal size;
+// K-loop unit u of workgroup b writes chunk u * gridDim + b.
 struct EvenPlanes {
     float* y;
     const float* bias;  // LDS copy of all Cout biases, or null for none
     int64_t P, vol;     // floats per plane and per (sample, channel) volume
-    int64_t total;      // slots over all even planes
-    int nEven, SL, Cout;
+    int64_t units;      // (sample, channel) volumes x plane pairs
+    int pairs, Y0, Y2, R, SLp, SLr, Cout;
+    __device__ __forceinline__ void slot(float* run, int s, int L, float v) const {
+        const int e0 = 4 * s - (int)(((uintptr_t)run >> 2) & 3);
+        if (e0 >= 0 && e0 + 3 < L) {
+            *reinterpret_cast<f32x4*>(run + e0) = f32x4{v, v, v, v};
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (e0 + k >= 0 && e0 + k < L) run[e0 + k] = v;
+        }
+    }
     __device__ void operator()(int64_t u, int64_t n) const {
         const int64_t nch = n * (int64_t)gridDim.x, chunk = u * (int64_t)gridDim.x + blockIdx.x;
-        const int64_t q = total / nch, rem = total - q * nch;
+        const int64_t q = units / nch, rem = units - q * nch;
         const int64_t g0 = chunk * q + (chunk < rem ? chunk : rem);
-        const int cnt = (int)(q + (chunk < rem ? 1 : 0));
-        const int64_t r0 = g0 / SL;
-        const int s0 = (int)(g0 - r0 * SL);
-        const int64_t nc0 = r0 / nEven;
-        const int j0 = (int)(r0 - nc0 * nEven);
-        const int c0 = (int)(nc0 % Cout);
-        const Div div_sl(SL), div_ne(nEven), div_c(Cout);
-        for (int l = threadIdx.x; l < cnt; l += kThreads) {
-            const int sl = s0 + l;  // < SL + cnt < 2^22 (checked on the host)
-            const int dr = div_sl.quot(sl);
-            const int s = sl - dr * SL;
-            const int jj = j0 + dr;
-            const int dnc = div_ne.quot(jj);
-            const int j = jj - dnc * nEven;
-            const int64_t nc = nc0 + dnc;
-            float* run = y + nc * vol + (int64_t)(2 * j) * P;
-            const int e0 = 4 * s - (int)(((uintptr_t)run >> 2) & 3);
-            float v = 0.f;
-            if (bias) {
-                const int cc = c0 + dnc;
-                v = bias[cc - div_c.quot(cc) * Cout];
-            }
-            if (e0 >= 0 && e0 + 3 < P) {
-                const f32x4 o = {v, v, v, v};
-                *reinterpret_cast<f32x4*>(run + e0) = o;
-            } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (e0 + k >= 0 && e0 + k < P) run[e0 + k] = v;
+        const int64_t g1 = g0 + q + (chunk < rem ? 1 : 0);
+        const Div div_slr(SLr);
+        for (int64_t unit = g0; unit < g1; ++unit) {
+            const int64_t volume = unit / pairs;
+            const int k = (int)(unit - volume * pairs);
+            const float v = bias ? bias[volume % Cout] : 0.f;
+            float* base = y + volume * vol + (int64_t)(2 * k) * P;
+            for (int s = threadIdx.x; s < SLp; s += kThreads) slot(base, s, (int)P, v);
+            if (2 * k + 1 < Y0) {
+                float* odd = base + P;
+                const int items = R * SLr;
+                for (int i = threadIdx.x; i < items; i += kThreads) {
+                    const int r = div_slr.quot(i);
+                    slot(odd + (int64_t)(2 * r) * Y2, i - r * SLr, Y2, v);
+                }
             }
         }
     }
@@ -209,8 +208,10 @@ struct EvenPlanes {
 // kLattice = 1: destination o = q (plain conv).  kLattice = 2: destination
 // o = 2q + 1 inside a destination grid of size Y (transposed conv); every
 // destination voxel with an even coordinate holds the bias.
+// two workgroups per CU: all 256 registers per lane hold the 4-plane tile's accumulators and the prefetch
 template <int kMode, int kLattice>
-__global__ __launch_bounds__(kThreads) void conv333_store_kernel(Args a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv333_store_kernel(
+    Args a) {
     __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
     __shared__ float sbias[OCB];
     __shared__ float all_bias[kLattice == 2 ? kMaxBiasLds : 1];
@@ -254,35 +255,44 @@ __global__ __launch_bounds__(kThreads) void conv333_store_kernel(Args a) {
         ep.bias = a.bias ? all_bias : nullptr;
         ep.P = a.Y[1] * a.Y[2];
         ep.vol = a.Y[0] * ep.P;
-        ep.nEven = (int)((a.Y[0] + 1) / 2);
-        ep.SL = (int)((ep.P + 6) >> 2);
-        ep.total = a.N * a.Cout * ep.nEven * ep.SL;
+        ep.pairs = (int)((a.Y[0] + 1) / 2);
+        ep.units = a.N * a.Cout * ep.pairs;
+        ep.Y0 = (int)a.Y[0];
+        ep.Y2 = (int)a.Y[2];
+        ep.R = (int)((a.Y[1] + 1) / 2);
+        ep.SLp = (int)((ep.P + 6) >> 2);
+        ep.SLr = (int)((a.Y[2] + 6) >> 2);
         ep.Cout = (int)a.Cout;
         mainloop<kMode, kMT>(a, t, lds, acc, ep);
     } else {
         mainloop<kMode, kMT>(a, t, lds, acc);
     }
 
+    // stage and write the tile 32 output channels (one N tile) at a time
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    __syncthreads();  // every wave is done reading the operand tiles
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+    for (int half = 0; half < 2; ++half) {
+        __syncthreads();  // every wave is done reading the operand tiles, or the previous half
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 int x, y, z;
                 acc_voxel(lane, wv, mt, i, x, y, z);
-                const int oc = nt * 32 + (lane & 31);
-                lds[oc * kStage + (z * TH + y) * TW + x] = acc[mt][nt][i];
+                lds[(lane & 31) * kStage + (z * TH + y) * TW + x] = acc[mt][half][i];
             }
-    __syncthreads();
-
-    // the rest of the box: all of it for the plain conv, its odd planes for
-    // the transposed conv
-    const RunSet rest = make_runs(b, kLattice == 1 ? 0 : 1, kLattice, 0, 1, b.full_rows);
-    store_runs(b, rest, 0, rest.items, TileValue<kLattice>{lds, sbias});
+        __syncthreads();
+        Box bh = b;
+        bh.yn = b.yn + 32 * half * b.plane;
+        bh.ocs = b.ocs - 32 * half < 32 ? b.ocs - 32 * half : 32;
+        if (bh.ocs > 0) {
+            // all of the box for the plain conv, the odd rows of its odd planes for the transposed conv
+            const RunSet rest =
+                kLattice == 1 ? make_runs(bh, 0, 1, 0, 1, bh.full_rows) : make_runs(bh, 1, 2, 1, 2, false);
+            store_runs(bh, rest, 0, rest.items, TileValue<kLattice>{lds, sbias + 32 * half});
+        }
+    }
 }
 
 Args make_args(const float* x, const float* w, const float* bias, float* y, const Geom& g) {
@@ -333,12 +343,9 @@ bool convT_s2_sublattice_supported(const Geom& g, const void*, const void*, cons
     if (g.groups != 1 || g.Cout > kMaxBiasLds || !mfma333::fits_int32_tiles(g.O[0]) ||
         !mfma333::fits_int32_tiles(g.O[1]) || !mfma333::fits_int32_tiles(g.O[2]))
         return false;
-    // the even-plane pass decodes slot indices below 2^22 with float reciprocals
-    const int64_t P = g.O[1] * g.O[2], SL = (P + 6) >> 2;
-    const int64_t units = 3 * ceil_div(g.Cin, ICC);
-    const int64_t grid = g.N * ceil_div(g.S[0], TD) * ceil_div(g.S[1], TH) * ceil_div(g.S[2], TW) * ceil_div(g.Cout, OCB);
-    const int64_t per_chunk = g.N * g.Cout * ((g.O[0] + 1) / 2) * SL / (units * grid) + 1;
-    return SL + per_chunk < (1 << 22) && g.Cout + per_chunk < (1 << 22);
+    // the bias pass indexes a plane in 32 bits and decodes row slots below
+    // 2^22 with float reciprocals
+    return g.O[1] * g.O[2] < (1 << 25);
 }
 
 hipError_t launch_convT_s2_sublattice(const float* x, const float* w, const float* bias, float* y, const Geom& g,
