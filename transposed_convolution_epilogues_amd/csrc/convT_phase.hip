@@ -13,9 +13,10 @@
 // work of the gather form.  A phase whose list is empty in some dim receives
 // no tap at all and equals the bias.
 //
-// A workgroup computes one phase of one 2 x 4 x 32 tile of q positions x 64
+// A workgroup computes one phase of one 4 x 4 x 32 tile of q positions x 64
 // output channels of one group (mainloop_taps in conv333_mfma.h), stages the
-// result in LDS and writes its outputs, which lie at stride s in each dim.
+// result in LDS 32 channels at a time and writes its outputs, which lie at
+// stride s in each dim.
 // The phases of a tile are consecutive workgroups, so after the XCD remap
 // they run at the same time on one XCD and their interleaved writes meet in
 // that XCD's L2 before they reach HBM.
@@ -33,10 +34,10 @@ namespace {
 
 using namespace mfma333;
 
-constexpr int kMT = 2;
+constexpr int kMT = 4;  // tile depth; the result staging (32 channels at a time) reuses the K-loop LDS
 constexpr int TD = Geo<kMT>::TD;
 constexpr int kStage = TD * TH * TW + 1;  // LDS floats per channel of the result staging (padded)
-constexpr int kLdsFloats = Geo<kMT>::LDS_MAIN > OCB * kStage ? Geo<kMT>::LDS_MAIN : OCB * kStage;
+constexpr int kLdsFloats = Geo<kMT>::LDS_MAIN > 32 * kStage ? Geo<kMT>::LDS_MAIN : 32 * kStage;
 constexpr int kMaxS = 4;                  // largest stride per dim
 constexpr int kMaxT = 3;                  // most taps per dim and phase
 
@@ -73,7 +74,9 @@ __device__ __forceinline__ DimTaps dim_taps(const DimPhases& dp, int r) {
     return t;
 }
 
-__global__ __launch_bounds__(kThreads) void convT_phase_kernel(PhaseArgs pa) {
+// two workgroups per CU: all 256 registers per lane hold the 4-plane tile's accumulators and the prefetch
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void convT_phase_kernel(
+    PhaseArgs pa) {
     __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
     __shared__ float sbias[OCB];
 
@@ -125,44 +128,47 @@ __global__ __launch_bounds__(kThreads) void convT_phase_kernel(PhaseArgs pa) {
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
+    f32x16 acc[kMT][2];
     if (has_taps) {
         const int32_t pad[3] = {pa.dim[0].org[r0], pa.dim[1].org[r1], pa.dim[2].org[r2]};
-        f32x16 acc[kMT][2];
         mainloop_taps<kMT>(a, t, ts, pad, lds, acc);
-        __syncthreads();  // every wave is done reading the operand tiles
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    int x, y, z;
-                    acc_voxel(lane, wv, mt, i, x, y, z);
-                    const int oc = nt * 32 + (lane & 31);
-                    lds[oc * kStage + (z * TH + y) * TW + x] = acc[mt][nt][i];
-                }
     }
-    __syncthreads();  // staging (and sbias) visible to every wave
-
-    // Write the tile: row (oc, z, y) holds q2 = w0 + x for x < 32, at output
-    // (s0 (d0 + z) + r0, s1 (h0 + y) + r1, s2 q2 + r2).  A wave writes two
-    // rows per instruction, one per half-wave.
     const int ocs = (int)(a.Cout - t.oc0 < OCB ? a.Cout - t.oc0 : OCB);
     const int s0 = pa.dim[0].s, s1 = pa.dim[1].s, s2 = pa.dim[2].s;
     const int64_t O1 = a.Y[1], O2 = a.Y[2];
     const int x = lane & 31;
     const int64_t q2 = t.w0 + x;
     const bool x_ok = q2 < Q2;
-    const int rows = ocs * TD * TH;
-    for (int row = wv * 2 + (lane >> 5); row < rows; row += 8) {
-        const int oc = row / (TD * TH);
-        const int zy = row - oc * (TD * TH);
-        const int z = zy / TH, y = zy - z * TH;
-        const int64_t qd = t.d0 + z, qh = t.h0 + y;
-        if (!x_ok || qd >= Q0 || qh >= Q1) continue;
-        const float v = (has_taps ? lds[oc * kStage + zy * TW + x] : 0.f) + sbias[oc];
-        const int64_t od = s0 * qd + r0, oh = s1 * qh + r1, ow = s2 * q2 + r2;
-        yg[(((t.n * pa.yC + t.oc0 + oc) * a.Y[0] + od) * O1 + oh) * O2 + ow] = v;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        __syncthreads();  // every wave is done reading the operand tiles, or the previous half
+        if (has_taps) {
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    int xx, y, z;
+                    acc_voxel(lane, wv, mt, i, xx, y, z);
+                    lds[(lane & 31) * kStage + (z * TH + y) * TW + xx] = acc[mt][half][i];
+                }
+        }
+        __syncthreads();  // staging (and sbias) visible to every wave
+        // write the half: row (oc, z, y) holds q2 = w0 + x for x < 32, at output
+        // (s0 (d0 + z) + r0, s1 (h0 + y) + r1, s2 q2 + r2); a wave writes two
+        // rows per instruction, one per half-wave
+        const int oh0 = 32 * half;
+        const int ocs_h = ocs - oh0 < 32 ? ocs - oh0 : 32;
+        const int rows = (ocs_h > 0 ? ocs_h : 0) * TD * TH;
+        for (int row = wv * 2 + (lane >> 5); row < rows; row += 8) {
+            const int oc = row / (TD * TH);
+            const int zy = row - oc * (TD * TH);
+            const int z = zy / TH, y = zy - z * TH;
+            const int64_t qd = t.d0 + z, qh = t.h0 + y;
+            if (!x_ok || qd >= Q0 || qh >= Q1) continue;
+            const float v = (has_taps ? lds[oc * kStage + zy * TW + x] : 0.f) + sbias[oh0 + oc];
+            const int64_t od = s0 * qd + r0, oh = s1 * qh + r1, ow = s2 * q2 + r2;
+            yg[(((t.n * pa.yC + t.oc0 + oh0 + oc) * a.Y[0] + od) * O1 + oh) * O2 + ow] = v;
+        }
     }
 }
 
