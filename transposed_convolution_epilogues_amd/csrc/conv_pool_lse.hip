@@ -9,7 +9,8 @@
 //     after the max (max(v) + b = max(v + b)).
 //   - logsumexp over the 64 channels: a channel lives in lane%32 of one of two
 //     N tiles, so each lane first combines its two channels, then the max and
-//     the shifted sum are reduced across the 32 lanes of its half; the running
+//     the shifted sum are reduced across the 32 lanes of its half (DPP moves
+//     and one swizzle, see half_max); the running
 //     maximum starts from real values, never from -inf ("Kimi-K2.6 l2_p43",
 //     the streaming-logsumexp initialisation caveat).
 //   - ReLU and one 4-byte store per pooled voxel.
@@ -22,6 +23,35 @@ namespace {
 using namespace mfma333;
 
 constexpr int kMT = 4;  // tile depth: two pooled planes per tile
+
+// Lane permutations within each 32-lane half of the wave.  DPP moves stay in
+// the ALU: quad_perm [1,0,3,2] and [2,3,0,1] pair lanes 1 and 2 apart,
+// row_half_mirror pairs the two quads of each 8 (i <-> 7 - i) and row_mirror
+// the two 8s of each 16 (i <-> 15 - i); one ds_swizzle in bitmask mode
+// (xor 16 within 32) pairs the two 16s.  Each step pairs every lane with a
+// partner from the other subset, so after all five every lane of the half
+// holds the reduction over its 32 lanes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swizzle_xor16(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+__device__ __forceinline__ float half_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    return fmaxf(v, swizzle_xor16(v));
+}
+__device__ __forceinline__ float half_sum(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    v += dpp<0x140>(v);
+    return v + swizzle_xor16(v);
+}
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv_pool_lse_mfma_kernel(Args a) {
     __shared__ __attribute__((aligned(16))) float lds[Geo<kMT>::LDS_MAIN];
@@ -62,12 +92,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         for (int u = 0; u < 2; ++u) v = fmaxf(v, acc[mt][nt][(2 * ay + ax) * 4 + bx + u]);
                 m[nt] = valid[nt] ? v + bias_v[nt] : -FLT_MAX;
             }
-            float M = fmaxf(m[0], m[1]);
-#pragma unroll
-            for (int off = 16; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-            float S = expf(m[0] - M) + expf(m[1] - M);
-#pragma unroll
-            for (int off = 16; off > 0; off >>= 1) S += __shfl_xor(S, off, 64);
+            const float M = half_max(fmaxf(m[0], m[1]));
+            const float S = half_sum(expf(m[0] - M) + expf(m[1] - M));
             const float L = M + logf(S);
             if ((lane & 31) == 0) {
                 const int64_t j2 = (t.w0 >> 1) + (wv & 1) * 8 + 4 * ax + 2 * h + (q & 1);
