@@ -82,6 +82,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=4.0, help="target oracle seconds per workload sample")
     ap.add_argument("--only", default=",".join(BENCH_KEYS), help="comma-separated subset (profiling runs)")
+    ap.add_argument("--probe-mfma", action="store_true",
+                    help="time the library's fp32 matrix-core throughput probe and print its TFLOP/s")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--widen", action="store_true",
@@ -98,6 +100,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.probe_mfma:
+        probe_mfma(torch)
         return
     if args.widen:
         widen(torch, args)
@@ -239,6 +244,30 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def probe_mfma(torch):
+    """Achievable fp32 MFMA throughput on this GPU: back-to-back independent
+    v_mfma_f32_32x32x2f32 chains, two waves per SIMD on every CU."""
+    from transposed_convolution_epilogues_amd import binding as B
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    iters = 2000
+    for _ in range(3):
+        flop = B.probe_mfma_f32(iters, out)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.probe_mfma_f32(iters, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    med = ts[len(ts) // 2]
+    print(json.dumps({"probe": "mfma_f32_32x32x2", "flop": flop, "ms_median": round(med, 4),
+                      "tflops": round(flop / (med * 1e-3) / 1e12, 2), "peak": FP32_PEAK_TFLOPS,
+                      "frac_of_peak": round(flop / (med * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4)}), flush=True)
 
 
 def calibrate_copy(torch):

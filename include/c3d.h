@@ -202,6 +202,17 @@ const char* c3d_status_string(int status);
  * different settings. */
 int c3d_set_variant(int variant);
 
+/* Diagnostic: a throughput probe of the fp32 matrix cores, to check the peak
+ * that roofline fractions are quoted against (not part of any operator).
+ * Launches 2048 workgroups of 256 threads on the stream; every wave runs
+ * 4 independent chains of `iters` back-to-back v_mfma_f32_32x32x2f32
+ * (4096 FLOP each).  out: device, >= 524288 floats (one sum per thread, so
+ * the work is kept; caller-owned scratch).  *flop (host) receives the FLOP
+ * count of the launch.  Errors: C3D_ERR_NULL (out or flop null),
+ * C3D_ERR_ALIGN, C3D_ERR_PARAM (iters outside [1, 2^24] or out too short);
+ * nothing is launched then.  Time it with events on the same stream. */
+int c3d_probe_mfma_f32(int64_t iters, float* out, int64_t out_len, int64_t* flop, void* stream);
+
 /* Kernel a call would use (under the current variant), for tests and
  * tuning; host-only, launches nothing. */
 enum {

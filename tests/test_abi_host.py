@@ -255,3 +255,18 @@ def test_kernel_choice_rejects_invalid_arguments():
     lib = B.library()
     xs = (ctypes.c_int64 * 5)(1, 4, 4, 4, 4)
     assert lib.c3d_conv3d_algo(xs, 8, ctypes.byref(B.make_params(3)), None) == 1  # C3D_ERR_NULL
+
+
+def _code(name):
+    return next(k for k, v in B.STATUS.items() if v == name)
+
+
+def test_mfma_probe_rejects_bad_arguments_before_launching():
+    lib = B.library()
+    flop = ctypes.c_int64(0)
+    assert lib.c3d_probe_mfma_f32(10, None, 1 << 20, ctypes.byref(flop), None) == 1  # C3D_ERR_NULL
+    fake = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+    assert lib.c3d_probe_mfma_f32(0, fake, 1 << 20, ctypes.byref(flop), None) == _code("C3D_ERR_PARAM")
+    assert lib.c3d_probe_mfma_f32(10, fake, 1000, ctypes.byref(flop), None) == _code("C3D_ERR_PARAM")
+    assert lib.c3d_probe_mfma_f32(10, ctypes.c_void_p(4098), 1 << 20, ctypes.byref(flop), None) == \
+        _code("C3D_ERR_ALIGN")

@@ -539,3 +539,25 @@ def test_runs_on_a_side_stream():
         y = B.conv3d_fwd(x, w, b, wl.stride, wl.pad, out=poisoned(ref.shape), stream=s)
     s.synchronize()
     assert_close("side stream", y.cpu().numpy(), ref)
+
+
+def test_mfma_probe_matches_its_closed_form():
+    """The throughput probe's per-thread sums follow from v_mfma_f32_32x32x2f32's
+    operand layout (lane l supplies A[l % 32][l / 32] and B[l / 32][l % 32];
+    accumulator v of lane l is D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32]), which
+    the conv engines rely on."""
+    iters = 3
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    flop = B.probe_mfma_f32(iters, out)
+    torch.cuda.synchronize()
+    assert flop == 2048 * 4 * iters * 4 * 4096
+    lane = np.arange(64)
+    a = 1e-3 * lane.astype(np.float64)                 # A value supplied by each lane
+    b = 1.0 / (1 + (lane & 7)).astype(np.float64)      # B value supplied by each lane
+    A = np.stack([a[np.arange(32) + 32 * k] for k in range(2)], axis=1)   # [32, 2]
+    Bm = np.stack([b[np.arange(32) + 32 * k] for k in range(2)], axis=0)  # [2, 32]
+    D = iters * (A @ Bm)
+    want = np.array([sum(D[8 * (v // 4) + 4 * (l // 32) + v % 4, l % 32] for v in range(16)) * 4 for l in range(64)])
+    got = out.view(-1, 256).cpu().numpy()
+    np.testing.assert_allclose(got[:, :64], np.broadcast_to(want, (2048, 64)), rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(got[:, 64:128], got[:, :64], rtol=0, atol=0)

@@ -26,7 +26,8 @@ EXPORTS = ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_
            "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
            "convT_bn_avgpool_workspace_bytes", "convT_bn_avgpool", "convT_bn_avgpool_ex", "conv_maxpool_lse_relu",
            "c3d_status_string",
-           "c3d_set_variant", "c3d_conv3d_algo", "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo")
+           "c3d_set_variant", "c3d_conv3d_algo", "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo",
+           "c3d_probe_mfma_f32")
 
 ALGO = {0: "direct", 1: "k1last", 2: "mfma333", 3: "sublattice", 4: "phase", 5: "bn_cells", 6: "bn_swap",
         7: "scatter", 8: "bn_mfma"}
@@ -103,6 +104,7 @@ def _lib():
     lib.c3d_conv3d_algo.argtypes = [i64p, i64, P, i32p]
     lib.c3d_conv_transpose3d_algo.argtypes = [i64p, i64, P, i32p]
     lib.c3d_convT_bn_avgpool_algo.argtypes = [i64p, i64, P, ctypes.c_int32, i32p]
+    lib.c3d_probe_mfma_f32.argtypes = [i64, ctypes.c_void_p, i64, i64p, ctypes.c_void_p]
     for name in ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_bn_avgpool_out_shape",
                  "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
                  "convT_bn_avgpool", "convT_bn_avgpool_ex", "conv_maxpool_lse_relu", "c3d_set_variant",
@@ -147,6 +149,15 @@ def _stream(stream) -> ctypes.c_void_p:
 def _check(st: int, where: str):
     if st != C3D_OK:
         raise C3DError(st, where)
+
+
+def probe_mfma_f32(iters: int, out: torch.Tensor, stream=None) -> int:
+    """Launch the matrix-core throughput probe on the stream; returns the
+    launch's FLOP count (time it with events on the same stream)."""
+    flop = ctypes.c_int64(0)
+    _check(_lib().c3d_probe_mfma_f32(int(iters), _dev(out, "out"), int(out.numel()), ctypes.byref(flop),
+                                    _stream(stream)), "c3d_probe_mfma_f32")
+    return int(flop.value)
 
 
 def set_variant(variant: int) -> int:

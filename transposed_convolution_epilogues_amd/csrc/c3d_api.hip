@@ -138,6 +138,14 @@ extern "C" {
 
 int c3d_set_variant(int variant) { return g_variant.exchange(variant); }
 
+int c3d_probe_mfma_f32(int64_t iters, float* out, int64_t out_len, int64_t* flop, void* stream) {
+    if (!out || !flop) return C3D_ERR_NULL;
+    if (!aligned4(out)) return C3D_ERR_ALIGN;
+    if (iters < 1 || iters > ((int64_t)1 << 24) || out_len < c3d::mfma_probe_out_len()) return C3D_ERR_PARAM;
+    *flop = c3d::mfma_probe_flop(iters);
+    return hip_status(c3d::launch_mfma_probe(iters, out, (hipStream_t)stream));
+}
+
 const char* c3d_status_string(int status) {
     switch (status) {
         case C3D_OK: return "ok";

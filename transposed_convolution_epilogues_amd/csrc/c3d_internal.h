@@ -67,6 +67,12 @@ struct BnRunning {
 };
 
 size_t convT_bn_pool_partials(const PoolGeom& pg, int fast);
+
+// matrix-core throughput probe (mfma_probe.hip)
+constexpr int kProbeWorkgroups = 2048;
+int64_t mfma_probe_out_len();
+int64_t mfma_probe_flop(int64_t iters);
+hipError_t launch_mfma_probe(int64_t iters, float* out, hipStream_t st);
 hipError_t launch_convT_bn_pool_phase1_direct(const float* x, const float* w, float* y, double* ws,
                                               const PoolGeom& pg, const BnEval& ev, hipStream_t st);
 hipError_t launch_bn_pool_phase2(float* y, const double* ws, int64_t parts_per_channel, const float* conv_bias,
