@@ -43,7 +43,7 @@ typedef enum {
     C3D_ERR_PARAM = 3,       /* kernel/stride/dilation < 1, padding < 0, bad output  */
                              /* padding, bad pool window, eps not finite and > 0     */
     C3D_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the query returns  */
-    C3D_ERR_UNSUPPORTED = 5, /* valid request outside what this build implements     */
+    C3D_ERR_UNSUPPORTED = 5, /* valid request outside what the library implements   */
     C3D_ERR_HIP = 6,         /* the HIP runtime reported an error at launch          */
     C3D_ERR_ALIGN = 7        /* a pointer is not 4-byte aligned                      */
 } c3d_status;
