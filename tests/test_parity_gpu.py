@@ -486,6 +486,15 @@ EDGE = {
     "bn_pool_pool1": W.make("e", "convT_bn_avgpool", (2, 2, 3, 3, 3), 3, 3, stride=2, pad=1, pool=1, seed=15),
     "lse_single_channel": W.make("e", "conv_maxpool_lse_relu", (1, 2, 4, 4, 4), 1, 3, pad=1, pool=2, seed=16),
     "lse_pool_whole": W.make("e", "conv_maxpool_lse_relu", (1, 3, 4, 4, 4), 6, 3, pad=1, pool=4, seed=17),
+    # the stride-2 dilation-2 sub-lattice path on degenerate grids: one input voxel (a 4-plane tile with
+    # 3 planes empty, bias-only output around one odd point), a thin grid, and W spanning two tiles with
+    # Cout past one 64-channel block
+    "convT_s2d2_single_voxel": W.make("e", "conv_transpose3d", (1, 4, 1, 1, 1), 8, 3, stride=2, pad=1,
+                                      dilation=2, bias=True, seed=18),
+    "convT_s2d2_thin": W.make("e", "conv_transpose3d", (2, 5, 1, 3, 1), 3, 3, stride=2, pad=1, dilation=2,
+                              seed=19),
+    "convT_s2d2_wide_cout70": W.make("e", "conv_transpose3d", (1, 3, 2, 1, 40), 70, 3, stride=2, pad=1,
+                                     dilation=2, bias=True, seed=20),
 }
 
 
