@@ -12,12 +12,14 @@
 // GEMM per output row: D[oc, j] = sum_k W[oc, k] * B[k, j], K = Cin*k0*k1
 // (27 for the (3,3,1) kernel on 3 channels, padded to an even count).  On
 // v_mfma_f32_32x32x2f32 the rows are output channels (the weights stay in
-// VGPRs for the whole kernel) and the columns are output positions.  One wave
-// owns one output row of 64 channels and walks it in blocks of 128 positions
-// (four N tiles); the four waves of a workgroup own four consecutive rows and
-// share the input they read through LDS.  The work is bound by the 2.6 GB of output stores, so the
-// column-to-position map is chosen for the store shape (see load_block); the
-// MFMA work runs underneath the stores.
+// VGPRs for the whole kernel) and the columns are output positions.  A wave
+// computes blocks of 128 positions (four N tiles) x 64 channels; the four
+// waves of a workgroup take the four consecutive blocks of one output row at a
+// time, walk the workgroup's two rows together, and share the input they read
+// through LDS.  The work is bound by the 2.6 GB of output stores, so both the
+// column-to-position map and the order in which the grid visits the output
+// are chosen for the stores (see store_block and the row loop); the MFMA work
+// runs underneath the stores.
 #include "c3d_internal.h"
 
 namespace c3d {
@@ -28,6 +30,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 256;
 constexpr int kMaxSteps = 16;  // K <= 32
 constexpr int kChunk = 512;    // output positions per workgroup (4 blocks of 128)
+constexpr int kRows = 2;       // output rows per workgroup
 constexpr int kMaxE = 12288;   // staged floats per workgroup (48 KB of LDS)
 
 struct K1Args {
@@ -41,7 +44,7 @@ struct K1Args {
     int32_t K, k0n, k1n, d0, d1S2;
     int32_t ocb;        // blocks of 64 output channels
     int32_t R, RL, E;   // staged input rows per workgroup, staged row length, staged floats
-    int32_t groups;     // row groups per (n, ocb): ceil(O0 / 4)
+    int32_t groups;     // row groups per (n, ocb): ceil(O0 / kRows)
     int32_t chunks;     // position chunks per row: ceil(J / kChunk)
 };
 
@@ -52,8 +55,9 @@ struct K1Args {
 // another.  Measured on MI355X with stores alone, writing this kernel's 2.6 GB
 // output in this shape takes ~0.83-0.93 ms (about 3.1 TB/s, whatever the
 // workgroup shape), against 1.19 ms with one 4-byte column per lane; only
-// long runs within one channel plane go faster (whole 10 KB rows 0.62 ms), and
-// a block of 64 channels cannot provide those.
+// long runs within one channel plane go faster (whole 10 KB rows 0.62 ms).  A
+// block of 64 channels cannot provide those runs itself; the row loop below
+// makes the workgroups that run at the same time provide them together.
 template <bool kBias, bool kVec, bool kFull>
 __device__ __forceinline__ void store_block(float* yb, uint32_t ystride, const f32x16 (&acc)[2][4],
                                             const float (&brow)[2][16], int64_t j0, int r, int h, int64_t J,
@@ -80,8 +84,8 @@ __device__ __forceinline__ void store_block(float* yb, uint32_t ystride, const f
         }
 }
 
-// A workgroup owns 4 consecutive output rows (one per wave) and a chunk of
-// kChunk positions of them.  Everything it reads - R = 4 + (k0-1)d0 rows of
+// A workgroup owns kRows consecutive output rows and a chunk of kChunk
+// positions of them.  Everything it reads - R = kRows + (k0-1)d0 rows of
 // every input channel, RL = kChunk + (k1-1)d1*S2 positions each - is staged in
 // LDS once, before its first output store.  The loop over the chunk's blocks
 // then issues no global load: on this GPU loads and stores share one in-order
@@ -102,7 +106,8 @@ __device__ __forceinline__ void stage(const K1Args& a, const float* xi, int64_t 
             const int rem = e - ic * (a.R * a.RL);
             const int row = rem / a.RL;
             const int col = rem - row * a.RL;
-            const int64_t g = (ic * a.S0 + o0b + row) * a.S1S2 + jc0 + col;
+            const int64_t irow = o0b + row;
+            const int64_t g = (ic * a.S0 + irow) * a.S1S2 + jc0 + col;
             v[q] = xi[g < last ? g : last];
         }
 #pragma unroll
@@ -127,13 +132,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     b /= a.groups;
     const int64_t ocb = b % a.ocb;
     const int64_t n = b / a.ocb;
-    const int64_t o0b = 4 * grp;            // first output row of this workgroup
-    const int64_t o0 = o0b + wave;          // this wave's output row
+    const int64_t o0b = kRows * grp;        // first output row of this workgroup
     const int64_t jc0 = chunk * kChunk;     // first position of this workgroup
     const float* xi = a.x + n * a.Cin * a.S0 * a.S1S2;
     stage(a, xi, o0b, jc0, lds);
     __syncthreads();
-    if (o0 >= a.O0) return;  // uniform per wave; no barrier follows
 
     // A operand (weights): lane holds W[oc][k] with oc = 64*ocb + 32*mt + r and
     // k = 2s + h.  Padding rows k >= K get a zero weight and read a valid
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int k1 = kk % a.k1n;
         const int k0 = (kk / a.k1n) % a.k0n;
         const int ic = kk / (a.k1n * a.k0n);
-        loff[s] = (ic * a.R + wave + k0 * a.d0) * a.RL + k1 * a.d1S2 + 4 * r;
+        loff[s] = (ic * a.R + k0 * a.d0) * a.RL + k1 * a.d1S2 + 128 * wave + 4 * r;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int64_t oc = 64 * ocb + 32 * mt + r;
@@ -165,12 +168,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             brow[mt][i] = (kBias && oc < a.Cout) ? a.bias[oc] : 0.f;
         }
     const bool all_oc = 64 * (ocb + 1) <= a.Cout;
-    float* yb = a.y + ((n * a.Cout + 64 * ocb) * a.O0 + o0) * a.J;
     const uint32_t ystride = (uint32_t)(a.O0 * a.J);  // between output channels
-
-    for (int jb = 0; jb < kChunk; jb += 128) {
-        const int64_t j0 = jc0 + jb;
-        if (j0 >= a.J) break;
+    // The four waves walk the workgroup's rows together: at row step q they
+    // take the four consecutive 128-position blocks of row o0b + q, so the
+    // workgroup writes 2 KB runs of every channel row at once, and the
+    // workgroups of the neighbouring chunks (dispatched together) extend those
+    // runs along the row.  With two rows per workgroup the rows being written
+    // at any moment span less of each channel plane than with four or eight;
+    // on MI355X the c2 layer took 0.72 ms with 2 rows, 0.81 ms with 3, 0.82 ms
+    // with 4, 0.85 ms with 8 and 0.94 ms with 1 (3 staged input rows per output
+    // row), against 0.90 ms when each wave owned one of 4 rows.
+    const int64_t j0 = jc0 + 128 * wave;
+    for (int q = 0; q < kRows; ++q) {
+        const int64_t o0 = o0b + q;
+        const int qoff = q * a.RL;
+        if (o0 >= a.O0) break;  // uniform per workgroup
+        if (j0 >= a.J) continue;  // uniform per wave
+        float* yb = a.y + ((n * a.Cout + 64 * ocb) * a.O0 + o0) * a.J;
         f32x16 acc[2][4];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -182,7 +196,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int s = 0; s < kSteps; ++s) {
             float bx[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) bx[t] = lds[loff[s] + jb + t];
+            for (int t = 0; t < 4; ++t) bx[t] = lds[loff[s] + qoff + t];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -203,7 +217,7 @@ bool conv_k1last_supported(const Geom& g, const void*, const void*, const void*)
     for (int j = 0; j < 3; ++j)
         if (g.s[j] != 1 || g.p[j] != 0) return false;
     const int64_t K = g.Cin * g.k[0] * g.k[1];
-    const int64_t R = 4 + (int64_t)(g.k[0] - 1) * g.d[0];
+    const int64_t R = kRows + (int64_t)(g.k[0] - 1) * g.d[0];
     const int64_t RL = kChunk + (int64_t)(g.k[1] - 1) * g.d[1] * g.S[2];
     const int64_t E = g.Cin * R * RL;
     // MFMA pays off with many output channels; K must fit the VGPR-resident
@@ -232,10 +246,10 @@ hipError_t launch_conv_k1last(const float* x, const float* w, const float* bias,
     a.d0 = g.d[0];
     a.d1S2 = (int32_t)(g.d[1] * g.S[2]);
     a.ocb = (int32_t)ceil_div(g.Cout, 64);
-    a.R = 4 + (g.k[0] - 1) * g.d[0];
+    a.R = kRows + (g.k[0] - 1) * g.d[0];
     a.RL = kChunk + (g.k[1] - 1) * a.d1S2;
     a.E = (int32_t)(g.Cin * a.R * a.RL);
-    a.groups = (int32_t)ceil_div(g.O[0], 4);
+    a.groups = (int32_t)ceil_div(g.O[0], kRows);
     a.chunks = (int32_t)ceil_div(a.J, kChunk);
     const int64_t blocks = g.N * a.ocb * (int64_t)a.groups * a.chunks;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
