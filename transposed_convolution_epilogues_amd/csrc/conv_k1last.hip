@@ -125,7 +125,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5, r = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Consecutive workgroup ids go round-robin to the 8 XCDs; remapped, each
+    // XCD takes a contiguous run of (chunk, row-pair) items, so the rows its
+    // workgroups write and the input rows they share stay within one L2
+    // (0.72 -> 0.70 ms on the c2 layer).
     int64_t b = blockIdx.x;
+    if ((gridDim.x & 7) == 0) b = (b & 7) * (int64_t)(gridDim.x >> 3) + (b >> 3);
     const int64_t chunk = b % a.chunks;
     b /= a.chunks;
     const int64_t grp = b % a.groups;
