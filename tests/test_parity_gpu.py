@@ -260,11 +260,16 @@ MEDIUM = {
     "convT_s2p1d2_bias_cout72": W.CONFIGS["c3"].with_(x_shape=(3, 6, 3, 3, 5), cout=72, bias=True),
     "conv3d_k331_bias_dil": W.CONFIGS["c2"].with_(x_shape=(1, 2, 9, 12, 5), cout=20, dilation=(2, 2, 1),
                                                   bias=True),
-    # rows of O1*S2 floats with O1*S2 % 4 == 0 and 64 channels: the persistent channel-run kernel,
-    # with a partial last chunk per row, bias and dilation, and a row shorter than one chunk
+    # rows of O1*S2 floats with O1*S2 % 4 == 0 and 64 channels: the float4 store path, with a partial
+    # last chunk per row, bias and dilation, and a row shorter than one chunk
     "conv3d_k331_rows_2chunks": W.CONFIGS["c2"].with_(x_shape=(2, 3, 9, 30, 10)),
     "conv3d_k331_rows_bias_dil": W.CONFIGS["c2"].with_(x_shape=(1, 3, 7, 25, 12), dilation=(2, 2, 1), bias=True),
     "conv3d_k331_rows_short": W.CONFIGS["c2"].with_(x_shape=(1, 3, 5, 8, 8)),
+    # 8 workgroups (a multiple of 8, so the XCD remap of the workgroup order applies) whose last one
+    # has a single output row
+    "conv3d_k331_xcd_odd_rows": W.CONFIGS["c2"].with_(x_shape=(1, 3, 17, 40, 10)),
+    # 2 samples x 3 row pairs x 4 chunks = 24 workgroups, last chunk partial
+    "conv3d_k331_xcd_chunks": W.CONFIGS["c2"].with_(x_shape=(2, 3, 8, 180, 10)),
     "convT_bn_pool_cin1_cout5": W.CONFIGS["c4"].with_(x_shape=(2, 1, 6, 9, 8), cout=5),
 }
 
