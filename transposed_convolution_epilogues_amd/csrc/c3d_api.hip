@@ -90,11 +90,12 @@ int resolve_pool(const Geom& g, int32_t pool, PoolGeom* pg) {
 int hip_status(hipError_t e) { return e == hipSuccess ? C3D_OK : C3D_ERR_HIP; }
 
 // Kernel choice (the C3D_ALGO_* codes of c3d.h).  Variant 1 forces the
-// generic kernels; variant 2 skips the shape-specialised ones (c2's
-// flattened-row conv, c3's sub-lattice transposed conv) so the general fast
-// paths can be compared with them; variants 3 and 4 select the second
-// algorithms of the c4 module (swapped sums) and of the transposed conv
-// (LDS scatter).
+// generic kernels; variant 2 skips the shape-specialised ones (the
+// flattened-row conv for (k,k,1) kernels, the sub-lattice kernel of the
+// stride-2 dilation-2 transposed conv) so the general fast paths can be
+// compared with them; variants 3 and 4 select the second algorithms of the
+// ConvT -> BatchNorm -> AvgPool module (swapped sums) and of the transposed
+// conv (LDS scatter).
 int conv3d_algo(const Geom& g) {
     const int v = g_variant.load();
     if (v == 1) return C3D_ALGO_DIRECT;
@@ -103,9 +104,10 @@ int conv3d_algo(const Geom& g) {
     return C3D_ALGO_DIRECT;
 }
 
-// c4 module: one thread per 4x4x4 cell (variants 0 and 2), the swapped sums
-// (variant 3; measured slower on MI355X, kept as the second algorithm),
-// generic (variant 1)
+// ConvT -> BatchNorm -> AvgPool module: the output-phase classes on the
+// matrix cores where they apply (variants 0, 2 and 4), one thread per 4x4x4
+// cell otherwise or with variant 5, the swapped sums (variant 3; measured
+// slower on MI355X, kept as the second algorithm), generic (variant 1)
 int bn_algo(const PoolGeom& pg) {
     const int v = g_variant.load();
     if (v == 1) return C3D_ALGO_DIRECT;

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Consecutive workgroup ids go round-robin to the 8 XCDs; remapped, each
     // XCD takes a contiguous run of (chunk, row-pair) items, so the rows its
     // workgroups write and the input rows they share stay within one L2
-    // (0.72 -> 0.70 ms on the c2 layer).
+    // (0.72 -> 0.70 ms on the 3->64 layer of x[16,3,256,256,10]).
     int64_t b = blockIdx.x;
     if ((gridDim.x & 7) == 0) b = (b & 7) * (int64_t)(gridDim.x >> 3) + (b >> 3);
     const int64_t chunk = b % a.chunks;
@@ -180,7 +180,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // workgroups of the neighbouring chunks (dispatched together) extend those
     // runs along the row.  With two rows per workgroup the rows being written
     // at any moment span less of each channel plane than with four or eight;
-    // on MI355X the c2 layer took 0.72 ms with 2 rows, 0.81 ms with 3, 0.82 ms
+    // on MI355X the 3->64 layer of x[16,3,256,256,10] took 0.72 ms with 2
+    // rows, 0.81 ms with 3, 0.82 ms
     // with 4, 0.85 ms with 8 and 0.94 ms with 1 (3 staged input rows per output
     // row), against 0.90 ms when each wave owned one of 4 rows.
     const int64_t j0 = jc0 + 128 * wave;
