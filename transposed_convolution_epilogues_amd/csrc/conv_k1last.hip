@@ -181,9 +181,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // runs along the row.  With two rows per workgroup the rows being written
     // at any moment span less of each channel plane than with four or eight;
     // on MI355X the 3->64 layer of x[16,3,256,256,10] took 0.72 ms with 2
-    // rows, 0.81 ms with 3, 0.82 ms
-    // with 4, 0.85 ms with 8 and 0.94 ms with 1 (3 staged input rows per output
-    // row), against 0.90 ms when each wave owned one of 4 rows.
+    // rows, 0.81 ms with 3, 0.82 ms with 4, 0.85 ms with 8 and 0.94 ms with 1
+    // (3 staged input rows per output row), against 0.90 ms when each wave
+    // owned one of 4 rows.
     const int64_t j0 = jc0 + 128 * wave;
     for (int q = 0; q < kRows; ++q) {
         const int64_t o0 = o0b + q;
