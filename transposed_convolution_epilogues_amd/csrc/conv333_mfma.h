@@ -29,8 +29,9 @@
 //                9 x 8 x 64 are double-buffered in LDS.  While a unit is being
 //                computed the next unit's weights (and, during a chunk's last
 //                unit, the next chunk's halo) are already being loaded into
-//                registers, so their latency hides under ~9K cycles of MFMA
-//                work; they are written to LDS after the unit.  Per tap a
+//                registers, issued in slices between the unit's taps, so their
+//                latency hides under ~9K cycles of MFMA work; they are written
+//                to LDS after the unit.  Per tap a
 //                lane fetches 4 K-steps of its A operand (4 consecutive
 //                channels of one voxel) and of its B operand (4 consecutive
 //                channels of one output channel) with one 16-byte LDS read
@@ -163,20 +164,25 @@ __device__ __forceinline__ XOffsets<kMT> x_offsets(const Args& a, const Tile& t,
 // when they are written to LDS.  A select right after a load would make the
 // wave wait for the load there, while the loads are meant to stay in flight
 // under a whole unit of MFMA work.
+// Channel ic0 + 4g + j of the halo (one of the 8 slices of a chunk's loads).
+template <int kMT>
+__device__ __forceinline__ void load_x_slice(const Args& a, const Tile& t, const XOffsets<kMT>& o, int64_t ic0,
+                                             int g, int j, XRegs<kMT>& r) {
+    const int64_t plane = a.S[0] * a.S[1] * a.S[2];
+    const int64_t ic = ic0 + 4 * g + j;
+    const bool icok = ic < a.Cin;
+    const float* xc = a.x + (t.n * a.xC + (icok ? ic : 0)) * plane;  // wave-uniform
+#pragma unroll
+    for (int q = 0; q < Geo<kMT>::XQ; ++q) r.v[g][q][j] = xc[o.off[q] >= 0 ? o.off[q] : 0];
+}
+
 template <int kMT>
 __device__ __forceinline__ void load_x(const Args& a, const Tile& t, const XOffsets<kMT>& o, int64_t ic0,
                                        XRegs<kMT>& r) {
-    const int64_t plane = a.S[0] * a.S[1] * a.S[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t ic = ic0 + 4 * g + j;
-            const bool icok = ic < a.Cin;
-            const float* xc = a.x + (t.n * a.xC + (icok ? ic : 0)) * plane;  // wave-uniform
-#pragma unroll
-            for (int q = 0; q < Geo<kMT>::XQ; ++q) r.v[g][q][j] = xc[o.off[q] >= 0 ? o.off[q] : 0];
-        }
+        for (int j = 0; j < 4; ++j) load_x_slice(a, t, o, ic0, g, j, r);
 }
 
 template <int kMT>
@@ -207,21 +213,25 @@ struct WRegs {
     float v[W_PAIRS_PER_THREAD][UNIT_TAPS];
 };
 
+// The 9 taps of (oc, ic) pair tid + 256q (one of the 2 slices of a unit's loads).
+template <int kMode>
+__device__ __forceinline__ void load_w_pair(const Args& a, const Tile& t, int64_t ic0, int kd, int q, WRegs& r) {
+    const int p = threadIdx.x + q * kThreads;
+    const int oc = p >> 3, j = p & 7;
+    const int64_t goc = t.oc0 + oc, gic = ic0 + j;
+    const bool ok = goc < a.Cout && gic < a.Cin;
+    // first source element of this unit's 9-tap run
+    const int64_t first = kMode == kConvWeights ? (goc * a.Cin + gic) * 27 + kd * UNIT_TAPS
+                                                : (gic * a.Cout + goc) * 27 + (18 - kd * UNIT_TAPS);
+    const float* src = a.w + (ok ? first : 0);
+#pragma unroll
+    for (int u = 0; u < UNIT_TAPS; ++u) r.v[q][u] = src[u];
+}
+
 template <int kMode>
 __device__ __forceinline__ void load_w(const Args& a, const Tile& t, int64_t ic0, int kd, WRegs& r) {
 #pragma unroll
-    for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) {
-        const int p = threadIdx.x + q * kThreads;
-        const int oc = p >> 3, j = p & 7;
-        const int64_t goc = t.oc0 + oc, gic = ic0 + j;
-        const bool ok = goc < a.Cout && gic < a.Cin;
-        // first source element of this unit's 9-tap run
-        const int64_t first = kMode == kConvWeights ? (goc * a.Cin + gic) * 27 + kd * UNIT_TAPS
-                                                    : (gic * a.Cout + goc) * 27 + (18 - kd * UNIT_TAPS);
-        const float* src = a.w + (ok ? first : 0);
-#pragma unroll
-        for (int u = 0; u < UNIT_TAPS; ++u) r.v[q][u] = src[u];
-    }
+    for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) load_w_pair<kMode>(a, t, ic0, kd, q, r);
 }
 
 template <int kMode>
@@ -299,8 +309,6 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
             const int nkd = kd < 2 ? kd + 1 : 0;
             WRegs wr;
             XRegs<kMT> xr;
-            if (!last_unit) load_w<kMode>(a, t, nc * ICC, nkd, wr);
-            if (kd == 2 && !last_unit) load_x(a, t, xo, nc * ICC, xr);
             const float* lw = lw0 + buf * LDS_W;
 #pragma unroll
             for (int kh = 0; kh < 3; ++kh)
@@ -322,6 +330,16 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
                             for (int nt = 0; nt < 2; ++nt)
                                 acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[mt][s], bv[nt][s],
                                                                                    acc[mt][nt], 0, 0, 0);
+                    // The next unit's loads are issued in slices behind the taps'
+                    // MFMAs (the weights behind taps 0 and 1, the halo's 8 channels
+                    // behind taps 1-8), fenced so the compiler keeps them there: a
+                    // burst of all of them before the first tap cost about 1% on the
+                    // fused conv-pool kernel and 2% on the transposed conv.
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (t9 < W_PAIRS_PER_THREAD && !last_unit) load_w_pair<kMode>(a, t, nc * ICC, nkd, t9, wr);
+                    if (t9 >= 1 && kd == 2 && !last_unit)
+                        load_x_slice(a, t, xo, nc * ICC, (t9 - 1) >> 2, (t9 - 1) & 3, xr);
+                    __builtin_amdgcn_sched_barrier(0);
                     // side work goes behind the first tap's MFMAs: its stores issue
                     // while the matrix core runs them (about 2% faster on the
                     // 32->64 stride-2 dilation-2 transposed conv of x[16,32,16,32,32]
