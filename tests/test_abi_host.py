@@ -207,6 +207,11 @@ ALGO_CASES = [
     ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 4, "scatter"),     # variant 4
     ("conv_transpose3d", (2, 3, 8, 8, 8), 4, 3, 5, 1, 1, 0, 1, 4, "scatter"),
     ("conv3d", (16, 3, 256, 256, 10), 64, (3, 3, 1), 1, 0, 1, 0, 1, 4, "k1last"),       # conv unaffected
+    ("conv3d", (1, 3, 7, 20, 8), 80, (3, 3, 1), 1, 0, 1, 0, 1, 0, "k1last"),            # two channel blocks
+    ("conv3d", (1, 2, 9, 21, 6), 64, (4, 4, 1), 1, 0, 1, 0, 1, 0, "k1last"),            # K = 32
+    ("conv3d", (1, 4, 9, 21, 6), 64, (3, 3, 1), 1, 0, 1, 0, 1, 0, "direct"),            # K = 36 > 32
+    ("conv3d", (1, 3, 9, 21, 6), 8, (3, 3, 1), 1, 0, 1, 0, 1, 0, "direct"),             # Cout < 16
+    ("conv3d", (1, 3, 9, 21, 6), 64, (3, 3, 1), 1, 1, 1, 0, 1, 0, "direct"),            # padding
 ]
 
 

@@ -270,6 +270,11 @@ MEDIUM = {
     "conv3d_k331_xcd_odd_rows": W.CONFIGS["c2"].with_(x_shape=(1, 3, 17, 40, 10)),
     # 2 samples x 3 row pairs x 4 chunks = 24 workgroups, last chunk partial
     "conv3d_k331_xcd_chunks": W.CONFIGS["c2"].with_(x_shape=(2, 3, 8, 180, 10)),
+    # a second, partial block of 64 output channels; one input channel (K = 9, the 8-step
+    # instantiation); a (4,4,1) kernel on 2 channels (K = 32, the 16-step instantiation)
+    "conv3d_k331_cout80": W.CONFIGS["c2"].with_(x_shape=(1, 3, 7, 20, 8), cout=80),
+    "conv3d_k331_cin1": W.CONFIGS["c2"].with_(x_shape=(1, 1, 6, 30, 12)),
+    "conv3d_k441_cin2": W.CONFIGS["c2"].with_(x_shape=(1, 2, 9, 21, 6), kernel=(4, 4, 1)),
     "convT_bn_pool_cin1_cout5": W.CONFIGS["c4"].with_(x_shape=(2, 1, 6, 9, 8), cout=5),
 }
 
