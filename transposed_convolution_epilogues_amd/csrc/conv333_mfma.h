@@ -31,11 +31,10 @@
 //                unit, the next chunk's halo) are already being loaded into
 //                registers, issued in slices between the unit's taps, so their
 //                latency hides under ~9K cycles of MFMA work; they are written
-//                to LDS after the unit.  Per tap a
-//                lane fetches 4 K-steps of its A operand (4 consecutive
-//                channels of one voxel) and of its B operand (4 consecutive
-//                channels of one output channel) with one 16-byte LDS read
-//                each.
+//                to LDS after the unit.  Per tap a lane fetches 4 K-steps of
+//                its A operand (4 consecutive channels of one voxel) and of
+//                its B operand (4 consecutive channels of one output channel)
+//                with one 16-byte LDS read each.
 //   K order    = within a chunk, K-step s and lane half h use channel
 //                4h + s; A and B agree on it, so the contraction is exact.
 // LDS: halo 26,112 B (kMT = 2) or 39,168 B (kMT = 4) + 2 x 18,576 B weights
@@ -259,10 +258,10 @@ struct NoSideWork {
 };
 
 // Runs the whole K loop; acc[mt][nt] holds the 32x32 result tiles.  side(u, n)
-// is called once per weight unit u of n, after that unit's prefetch loads and
-// its first tap's MFMAs are issued: work placed there (stores that do not
-// depend on the result) overlaps the matrix-core work.  It must not touch the
-// operand LDS.
+// is called once per weight unit u of n, after the unit's first tap of MFMAs
+// and its first slice of prefetch loads are issued: work placed there (stores
+// that do not depend on the result) overlaps the matrix-core work.  It must
+// not touch the operand LDS.
 template <int kMode, int kMT, class Side = NoSideWork>
 __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* lds, f32x16 (&acc)[kMT][2],
                                          const Side& side = Side()) {
