@@ -1,0 +1,75 @@
+"""The work counts the benchmark divides by time (CPU only).
+
+bench.py's effective TFLOP/s is 2 * MAC / time with MAC the algorithmic work:
+the dense GEMM count N * Cout * prod(O) * Cin/groups * kvol for direct convs,
+and the valid-tap count N * Cout * Cin/groups * prod_j #{(i_j, k_j) landing
+inside the output} for transposed convs.  Here those counts are checked
+against closed forms worked out by hand for the four full-size workloads, so
+a slip in the benchmark's accounting (a wrong output size, dense instead of
+valid taps, a dropped factor) cannot inflate or deflate the reported rate.
+"""
+import bench
+from transposed_convolution_epilogues_amd import workloads as W
+
+
+def _conv_out(S, k, s, p, d):
+    return (S + 2 * p - d * (k - 1) - 1) // s + 1
+
+
+def _convT_out(S, k, s, p, d, op=0):
+    return (S - 1) * s - 2 * p + d * (k - 1) + op + 1
+
+
+def test_c2_dense_gemm_count():
+    # x[16,3,256,256,10], (3,3,1) kernel, 64 channels, no padding: output 254 x 254 x 10
+    wl = W.CONFIGS["c2"]
+    O = (254, 254, 10)
+    mac, xb, wb = bench.work(wl, (16, 64) + O)
+    assert mac == 16 * 64 * 254 * 254 * 10 * 3 * 9 == 17_837_383_680
+    assert xb == 4 * 16 * 3 * 256 * 256 * 10 and wb == 4 * 64 * 3 * 9
+
+
+def test_c3_valid_tap_count():
+    # stride 2, pad 1, dilation 2, kernel 3: o = 2(i + k) - 1, so per dim every (i, k) pair lands
+    # inside the output except i + k = 0 and i + k = S + 1 (one pair each): 3S - 2 pairs
+    wl = W.CONFIGS["c3"]
+    O = tuple(_convT_out(S, 3, 2, 1, 2) for S in (16, 32, 32))
+    assert O == (33, 65, 65)
+    mac, _, _ = bench.work(wl, (16, 64) + O)
+    assert mac == 16 * 64 * 32 * (3 * 16 - 2) * (3 * 32 - 2) ** 2 == 13_318_750_208
+
+
+def test_c4_valid_tap_count():
+    # stride 2, pad 1, kernel 3, dilation 1 on 32 inputs: output 63; o = 2i - 1 + k is outside only for
+    # (i, k) = (0, 0) and (31, 2), so 94 pairs per dim; per pooled output and channel that is the
+    # page's 8 * 81 = 648 taps over a 4 x 4 x 4 window
+    wl = W.CONFIGS["c4"]
+    O = tuple(_convT_out(32, 3, 2, 1, 1) for _ in range(3))
+    assert O == (63, 63, 63)
+    mac, _, _ = bench.work(wl, (64, 16) + O)
+    assert mac == 64 * 16 * 3 * 94 ** 3 == 2_551_554_048
+    assert 8 * 81 == 648 and 94 == 3 * 32 - 2
+
+
+def test_c5_dense_gemm_count():
+    wl = W.CONFIGS["c5"]
+    O = tuple(_conv_out(S, 3, 1, 1, 1) for S in (32, 128, 128))
+    assert O == (32, 128, 128)
+    mac, xb, _ = bench.work(wl, (4, 64) + O)
+    assert mac == 4 * 64 * 32 * 128 * 128 * 32 * 27 == 115_964_116_992
+    assert xb == 4 * 4 * 32 * 32 * 128 * 128
+
+
+def test_valid_pairs_matches_direct_enumeration_on_small_cases():
+    # bench.valid_pairs against an explicit scatter of every (i, k) into the output range
+    for L_in, k, s, p, d in [(1, 1, 1, 0, 1), (5, 3, 2, 1, 1), (4, 3, 3, 2, 2), (7, 4, 2, 0, 1), (3, 2, 1, 3, 3)]:
+        L_out = _convT_out(L_in, k, s, p, d)
+        hits = [0] * max(L_out, 1)
+        n = 0
+        for i in range(L_in):
+            for kk in range(k):
+                o = i * s - p + kk * d
+                if 0 <= o < L_out:
+                    hits[o] += 1
+                    n += 1
+        assert bench.valid_pairs(L_in, k, s, p, d, L_out) == n == sum(hits)
