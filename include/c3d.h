@@ -39,7 +39,7 @@ typedef enum {
     C3D_OK = 0,
     C3D_ERR_NULL = 1,        /* a required pointer is NULL                           */
     C3D_ERR_SHAPE = 2,       /* a dim is non-positive, channels/groups mismatch,     */
-                             /* or an output dim would be < 1                        */
+                             /* Cin or Cout above 2^30, or an output dim would be < 1 */
     C3D_ERR_PARAM = 3,       /* kernel/stride/dilation < 1, padding < 0, bad output  */
                              /* padding, bad pool window, eps not finite and > 0     */
     C3D_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the query returns  */

@@ -92,6 +92,7 @@ def test_errors_are_reported_before_launch():
     assert _call_conv(lib, shape=(1, 4, 0, 8, 8)) == 2
     assert _call_conv(lib, shape=(0, 4, 8, 8, 8)) == 2  # empty batch: rejected, nothing launched
     assert _call_conv(lib, shape=(1, 0, 8, 8, 8)) == 2
+    assert _call_conv(lib, shape=(1, (1 << 30) + 4, 1, 1, 1), params=_p(1, 1, 0)) == 2  # Cin above 2^30
     assert _call_conv(lib, shape=(1, 6, 8, 8, 8), params=_p(3, 1, 1, 1, 0, 4)) == 2  # Cin % groups
     assert _call_conv(lib, cout=6, params=_p(3, 1, 1, 1, 0, 4), shape=(1, 8, 8, 8, 8)) == 2  # Cout % groups
     assert _call_conv(lib, shape=(1, 4, 2, 8, 8), params=_p(3, 1, 0)) == 2  # empty output

@@ -49,7 +49,8 @@ int resolve(const int64_t xs[5], int64_t cout, const c3d_conv_params* p, bool tr
     if (st) return st;
     for (int j = 0; j < 5; ++j)
         if (xs[j] < 1 || xs[j] > ((int64_t)1 << 40)) return C3D_ERR_SHAPE;
-    if (cout < 1 || cout > ((int64_t)1 << 30)) return C3D_ERR_SHAPE;
+    // channel counts (and so the per-group counts kept in 32 bits) stay below 2^30
+    if (cout < 1 || cout > ((int64_t)1 << 30) || xs[1] > ((int64_t)1 << 30)) return C3D_ERR_SHAPE;
     if (xs[1] % p->groups != 0 || cout % p->groups != 0) return C3D_ERR_SHAPE;
     g->N = xs[0];
     g->Cin = xs[1];
