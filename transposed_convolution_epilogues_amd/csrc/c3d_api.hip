@@ -153,7 +153,8 @@ const char* c3d_status_string(int status) {
     switch (status) {
         case C3D_OK: return "ok";
         case C3D_ERR_NULL: return "a required pointer is NULL";
-        case C3D_ERR_SHAPE: return "invalid shape (non-positive dim, channel/groups mismatch or empty output)";
+        case C3D_ERR_SHAPE:
+            return "invalid shape (non-positive dim, channel/groups mismatch, channels above 2^30 or empty output)";
         case C3D_ERR_PARAM: return "invalid parameter (kernel/stride/dilation/padding/output_padding/pool/eps)";
         case C3D_ERR_WORKSPACE: return "workspace missing or too small";
         case C3D_ERR_UNSUPPORTED: return "unsupported request";
