@@ -182,7 +182,14 @@ struct EvenPlanes {
         }
     }
     __device__ void operator()(int64_t u, int64_t n) const {
-        const int64_t nch = n * (int64_t)gridDim.x, chunk = u * (int64_t)gridDim.x + blockIdx.x;
+        // chunks in XCD-aware order: consecutive workgroup ids go round-robin
+        // to the 8 XCDs, so remapped, each XCD writes one contiguous run of
+        // the unit's chunks (about 0.5 % on the 32->64 stride-2 dilation-2
+        // transposed conv of x[16,32,16,32,32])
+        const int64_t nb = gridDim.x;
+        int64_t bx = blockIdx.x;
+        if ((nb & 7) == 0) bx = (bx & 7) * (nb >> 3) + (bx >> 3);
+        const int64_t nch = n * nb, chunk = u * nb + bx;
         const int64_t q = units / nch, rem = units - q * nch;
         const int64_t g0 = chunk * q + (chunk < rem ? chunk : rem);
         const int64_t g1 = g0 + q + (chunk < rem ? 1 : 0);
