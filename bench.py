@@ -12,7 +12,7 @@ the four full-size workloads back to back, each through its C-ABI entry point
 value = effective TFLOP/s of the whole step = sum over workloads of 2*MAC / step time, where MAC is the
 algorithmic work: the dense GEMM count for direct convs and the valid-tap count for transposed convs.
 
-Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  `--gpus N` with N > 1 exits: the library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -92,8 +92,8 @@ def main():
                          "and print one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a design "
-              "note, not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU "
+              "path: batch sharding across GPUs is a design note", file=sys.stderr)
         sys.exit(2)
 
     import torch
