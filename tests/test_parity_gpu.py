@@ -270,6 +270,8 @@ MEDIUM = {
     "conv3d_k331_xcd_odd_rows": W.CONFIGS["c2"].with_(x_shape=(1, 3, 17, 40, 10)),
     # 2 samples x 3 row pairs x 4 chunks = 24 workgroups, last chunk partial
     "conv3d_k331_xcd_chunks": W.CONFIGS["c2"].with_(x_shape=(2, 3, 8, 180, 10)),
+    # 40 row pairs x 2 chunks = 80 workgroups: the remap into interleaved runs of 10 per XCD
+    "conv3d_k331_xcd_runs": W.CONFIGS["c2"].with_(x_shape=(1, 3, 82, 100, 10)),
     # a second, partial block of 64 output channels; one input channel (K = 9, the 8-step
     # instantiation); a (4,4,1) kernel on 2 channels (K = 32, the 16-step instantiation)
     "conv3d_k331_cout80": W.CONFIGS["c2"].with_(x_shape=(1, 3, 7, 20, 8), cout=80),
