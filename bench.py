@@ -126,20 +126,20 @@ def main():
         x, w, b = g(inp.x), g(inp.w), g(inp.b)
         p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
         if wl.op == "conv3d":
-            oshape = B.conv3d_out_shape(wl.x_shape, wl.cout, p)
+            oshape = B.conv3d_out_dims(wl.x_shape, wl.cout, p)
             conv_shape = oshape
             y = torch.empty(oshape, device=dev)
             fn = (lambda x=x, w=w, b=b, y=y, wl=wl: B.conv3d_fwd(x, w, b, wl.stride, wl.pad, wl.dilation,
                                                                  wl.groups, out=y))
         elif wl.op == "conv_transpose3d":
-            oshape = B.conv_transpose3d_out_shape(wl.x_shape, wl.cout, p)
+            oshape = B.conv_transpose3d_out_dims(wl.x_shape, wl.cout, p)
             conv_shape = oshape
             y = torch.empty(oshape, device=dev)
             fn = (lambda x=x, w=w, b=b, y=y, wl=wl: B.conv_transpose3d_fwd(x, w, b, wl.stride, wl.pad, wl.dilation,
                                                                            wl.output_pad, wl.groups, out=y))
         elif wl.op == "convT_bn_avgpool":
-            conv_shape = B.conv_transpose3d_out_shape(wl.x_shape, wl.cout, p)
-            oshape = B.convT_bn_avgpool_out_shape(wl.x_shape, wl.cout, p, wl.pool)
+            conv_shape = B.conv_transpose3d_out_dims(wl.x_shape, wl.cout, p)
+            oshape = B.convT_bn_avgpool_out_dims(wl.x_shape, wl.cout, p, wl.pool)
             y = torch.empty(oshape, device=dev)
             ws = torch.empty(B.convT_bn_avgpool_workspace_bytes(wl.x_shape, wl.cout, p, wl.pool),
                              dtype=torch.uint8, device=dev)
@@ -148,8 +148,8 @@ def main():
                   B.convT_bn_avgpool(x, w, b, gm, bt, wl.eps, wl.pool, wl.stride, wl.pad, wl.dilation,
                                      wl.output_pad, wl.groups, out=y, workspace=ws))
         else:
-            conv_shape = B.conv3d_out_shape(wl.x_shape, wl.cout, p)
-            oshape = B.conv_maxpool_lse_relu_out_shape(wl.x_shape, wl.cout, p, wl.pool)
+            conv_shape = B.conv3d_out_dims(wl.x_shape, wl.cout, p)
+            oshape = B.conv_maxpool_lse_relu_out_dims(wl.x_shape, wl.cout, p, wl.pool)
             y = torch.empty(oshape, device=dev)
             fn = (lambda x=x, w=w, b=b, y=y, wl=wl: B.conv_maxpool_lse_relu(x, w, b, wl.pool, wl.stride, wl.pad,
                                                                             wl.dilation, wl.groups, out=y))
@@ -318,7 +318,7 @@ def widen(torch, args):
         t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
         x, w, b = t(inp.x), t(inp.w), t(inp.b)
         p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
-        conv_shape = B.conv_transpose3d_out_shape(wl.x_shape, wl.cout, p)
+        conv_shape = B.conv_transpose3d_out_dims(wl.x_shape, wl.cout, p)
         mac, xb, wb = work(wl, conv_shape)
         kw = dict(stride=wl.stride, pad=wl.pad, dilation=wl.dilation, output_pad=wl.output_pad, groups=wl.groups)
         if kind == "convT":
@@ -326,7 +326,7 @@ def widen(torch, args):
             fn = lambda: B.conv_transpose3d_fwd(x, w, b, out=y, **kw)
             algo = lambda: B.conv_transpose3d_algo(wl.x_shape, wl.cout, p)
         else:
-            y = torch.empty(B.convT_bn_avgpool_out_shape(wl.x_shape, wl.cout, p, wl.pool), device=dev)
+            y = torch.empty(B.convT_bn_avgpool_out_dims(wl.x_shape, wl.cout, p, wl.pool), device=dev)
             gm, bt = t(inp.gamma), t(inp.beta)
             rm0, rv0 = W.make_running_stats(wl.cout, 5)
             rm, rv = t(rm0), t(rv0)

@@ -21,8 +21,14 @@
  *   error nothing is launched and a non-zero c3d_status is returned.
  * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *   null stream).  A launch failure reported by hipGetLastError maps to
- *   C3D_ERR_HIP.  No exceptions cross the ABI; the calls keep no global
- *   mutable state and are thread-safe.  Index arithmetic is 64-bit.
+ *   C3D_ERR_HIP.  No exceptions cross the ABI.  Index arithmetic is 64-bit.
+ * - The operators keep no process-wide mutable state and may be called from
+ *   several threads at once.  The one piece of library state is the kernel
+ *   override of c3d_set_variant, which is held per calling thread: it changes
+ *   only the kernels of later calls made from the thread that set it.
+ * - The C calls cannot see buffer sizes: every buffer must hold at least the
+ *   elements its shape (or the shape queries) implies.  The Python binding
+ *   checks every tensor against these shapes before it calls in.
  * - Pointers must be 4-byte aligned; 16-byte alignment enables the fast paths.
  */
 #ifndef C3D_H
@@ -65,24 +71,24 @@ typedef struct {
 /* Output shape of conv3d_fwd: per dim floor((S + 2p - d(k-1) - 1)/s) + 1
  * ("Kimi-K2.6 l2_p43", the conv output-size formula).  Writes y_shape on
  * success. */
-int c3d_conv3d_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+c3d_status c3d_conv3d_out_dims(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
                          int64_t y_shape[5]);
 
 /* Output shape of conv_transpose3d_fwd: per dim (S-1)s - 2p + d(k-1) + op + 1
  * ("Kimi-K2.6 l1_p77", the output-size formula with dilation). */
-int c3d_conv_transpose3d_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+c3d_status c3d_conv_transpose3d_out_dims(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
                                    int64_t y_shape[5]);
 
 /* Output shape of convT_bn_avgpool: the transposed-conv shape with each
  * spatial dim pooled in floor mode, floor((O - pool)/pool) + 1
  * ("Kimi-K2.6 l2_p72", the AvgPool3d sizes 63 -> 31 -> 15). */
-int c3d_convT_bn_avgpool_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+c3d_status c3d_convT_bn_avgpool_out_dims(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
                                    int32_t pool, int64_t y_shape[5]);
 
 /* Output shape of conv_maxpool_lse_relu: [N, 1, P0, P1, P2] with the conv
  * shape pooled in floor mode ("Kimi-K2.6 l2_p43", MaxPool3d(2) then the
  * keepdim logsumexp). */
-int c3d_conv_maxpool_lse_relu_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+c3d_status c3d_conv_maxpool_lse_relu_out_dims(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
                                         int32_t pool, int64_t y_shape[5]);
 
 /* Direct 3D convolution ("Kimi-K2.6 l1_p59", the output formula summed over
@@ -95,7 +101,7 @@ int c3d_conv_maxpool_lse_relu_out_shape(const int64_t x_shape[5], int64_t cout, 
  *   bias  [Cout] or NULL                      (device, read)
  *   y     [N, Cout, O0, O1, O2]               (device, written in full)
  */
-int conv3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+c3d_status conv3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
                const c3d_conv_params* p, const float* bias, float* y, void* stream);
 
 /* 3D transposed convolution in its gather form ("Kimi-K2.6 l1_p77", the
@@ -111,7 +117,7 @@ int conv3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t
  *   y     [N, Cout, O0, O1, O2]               (device, written in full,
  *                                              including positions no tap reaches)
  */
-int conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+c3d_status conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
                          const c3d_conv_params* p, const float* bias, float* y, void* stream);
 
 /* Bytes of device workspace convT_bn_avgpool (and convT_bn_avgpool_ex in
@@ -139,7 +145,7 @@ size_t convT_bn_avgpool_workspace_bytes(const int64_t x_shape[5], int64_t cout, 
  *   batch_mean, batch_var [Cout] or NULL      (device, written if given: the
  *          statistics of t including conv_bias; var is the biased one)
  */
-int convT_bn_avgpool(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+c3d_status convT_bn_avgpool(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
                      const c3d_conv_params* p, const float* conv_bias, const float* gamma, const float* beta,
                      float eps, int32_t pool, float* y, void* ws, size_t ws_bytes, float* batch_mean,
                      float* batch_var, void* stream);
@@ -166,7 +172,7 @@ int convT_bn_avgpool(const float* x, const int64_t x_shape[5], const float* w, i
  *   running_mean, running_var [Cout] or NULL (device, read; written in
  *     training mode)
  * Calls that update the same running buffers must not overlap. */
-int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+c3d_status convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
                         const c3d_conv_params* p, const float* conv_bias, const float* gamma, const float* beta,
                         float eps, int32_t pool, int32_t training, float momentum, float* running_mean,
                         float* running_var, float* y, void* ws, size_t ws_bytes, float* batch_mean,
@@ -180,11 +186,11 @@ int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w
  *   y[n,0,j] = max(0, M + log(sum_c exp(m[n,c,j] - M))),  M = max_c m[n,c,j]
  *   y      [N, 1, O0/pool, O1/pool, O2/pool]  (device, written)
  */
-int conv_maxpool_lse_relu(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+c3d_status conv_maxpool_lse_relu(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
                           const c3d_conv_params* p, const float* bias, int32_t pool, float* y, void* stream);
 
 /* Human-readable name of a status code (static storage). */
-const char* c3d_status_string(int status);
+const char* c3d_status_str(c3d_status status);
 
 /* Kernel-variant override for A/B tests: 0 = automatic (default), 1 = force
  * the generic direct kernels, 2 = skip the shape-specialised kernels (the
@@ -198,8 +204,8 @@ const char* c3d_status_string(int status);
  * injective there; LDS-bound, the second algorithm to compare against),
  * 5 = as 0 but convT_bn_avgpool uses its one-thread-per-cell fp32 kernel
  * (C3D_ALGO_BN_CELLS) instead of the matrix-core one.
- * Returns the previous value.  Process-wide; not for concurrent use with
- * different settings. */
+ * Returns the previous value.  The setting belongs to the calling thread
+ * (thread-local): other threads keep their own, starting at 0. */
 int c3d_set_variant(int variant);
 
 /* Diagnostic: a throughput probe of the fp32 matrix cores, to check the peak
@@ -211,7 +217,7 @@ int c3d_set_variant(int variant);
  * count of the launch.  Errors: C3D_ERR_NULL (out or flop null),
  * C3D_ERR_ALIGN, C3D_ERR_PARAM (iters outside [1, 2^24] or out too short);
  * nothing is launched then.  Time it with events on the same stream. */
-int c3d_probe_mfma_f32(int64_t iters, float* out, int64_t out_len, int64_t* flop, void* stream);
+c3d_status c3d_probe_mfma_f32(int64_t iters, float* out, int64_t out_len, int64_t* flop, void* stream);
 
 /* Kernel a call would use (under the current variant), for tests and
  * tuning; host-only, launches nothing. */
@@ -229,14 +235,14 @@ enum {
 
 /* Writes the C3D_ALGO_* code conv3d_fwd would use to *algo; returns the
  * validation status conv3d_fwd would return (nothing is written on error). */
-int c3d_conv3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo);
+c3d_status c3d_conv3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo);
 
 /* The same for conv_transpose3d_fwd.  The phase path ("Kimi-K2.6 l1_p77",
  * the residue classes of o mod s, each a stride-1 correlation with its own
  * taps) applies when every stride is at most 4, every residue class has at
  * most 3 taps per dim whose input offsets span at most 3 positions, and
  * Cin/groups >= 4, Cout/groups >= 8. */
-int c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo);
+c3d_status c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo);
 
 /* The same for convT_bn_avgpool and convT_bn_avgpool_ex.  The swapped-sums
  * path ("Kimi-K2.6 l2_p72", the proposal to swap the pooled sum and the conv
@@ -249,7 +255,7 @@ int c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_
  * Cin x taps on the matrix cores, pooled and squared in registers); other
  * Cin <= 4 shapes, or variant 5, take the one-thread-per-cell fp32 kernel
  * (C3D_ALGO_BN_CELLS). */
-int c3d_convT_bn_avgpool_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t pool,
+c3d_status c3d_convT_bn_avgpool_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t pool,
                               int32_t* algo);
 
 #ifdef __cplusplus

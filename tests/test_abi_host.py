@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def header_symbols():
     text = open(os.path.join(ROOT, "include", "c3d.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|c3d_status|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
                                  text, flags=re.M)))
 
 
@@ -48,13 +48,13 @@ def test_shape_queries_match_oracle(name):
     wl = W.CONFIGS[name]
     p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
     if wl.op == "conv3d":
-        got = B.conv3d_out_shape(wl.x_shape, wl.cout, p)
+        got = B.conv3d_out_dims(wl.x_shape, wl.cout, p)
     elif wl.op == "conv_transpose3d":
-        got = B.conv_transpose3d_out_shape(wl.x_shape, wl.cout, p)
+        got = B.conv_transpose3d_out_dims(wl.x_shape, wl.cout, p)
     elif wl.op == "convT_bn_avgpool":
-        got = B.convT_bn_avgpool_out_shape(wl.x_shape, wl.cout, p, wl.pool)
+        got = B.convT_bn_avgpool_out_dims(wl.x_shape, wl.cout, p, wl.pool)
     else:
-        got = B.conv_maxpool_lse_relu_out_shape(wl.x_shape, wl.cout, p, wl.pool)
+        got = B.conv_maxpool_lse_relu_out_dims(wl.x_shape, wl.cout, p, wl.pool)
     assert got == O.output_shape(wl)
 
 
@@ -65,7 +65,7 @@ def test_shape_queries_random_match_oracle():
         wl = W.random_small_workload(op, rng)
         p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
         ref = O.output_shape(wl)
-        fn = B.conv3d_out_shape if op == "conv3d" else B.conv_transpose3d_out_shape
+        fn = B.conv3d_out_dims if op == "conv3d" else B.conv_transpose3d_out_dims
         if all(v > 0 for v in ref):
             assert fn(wl.x_shape, wl.cout, p) == ref
         else:
@@ -173,8 +173,8 @@ def test_bn_running_stats_and_eval_errors_are_reported_before_launch():
 def test_status_strings():
     lib = B.library()
     for code in range(8):
-        assert lib.c3d_status_string(code)
-    assert lib.c3d_status_string(99) == b"unknown status"
+        assert lib.c3d_status_str(code)
+    assert lib.c3d_status_str(99) == b"unknown status"
 
 
 def test_binding_rejects_cpu_tensors():
@@ -184,6 +184,175 @@ def test_binding_rejects_cpu_tensors():
     w = torch.zeros(8, 4, 3, 3, 3)
     with pytest.raises(TypeError):
         B.conv3d_fwd(x, w, None, 1, 1, out=torch.zeros(1, 8, 8, 8, 8))
+
+
+# ------------------------------------------- binding validation before launch
+LAUNCHES = ("conv3d_fwd", "conv_transpose3d_fwd", "convT_bn_avgpool", "convT_bn_avgpool_ex",
+            "conv_maxpool_lse_relu", "c3d_probe_mfma_f32")
+
+
+class _NoLaunch:
+    """The real library for host-only queries; every entry point that would
+    launch a kernel fails the test instead."""
+
+    def __init__(self, lib):
+        self._lib = lib
+
+    def __getattr__(self, name):
+        if name in LAUNCHES:
+            def launched(*a, **k):
+                raise AssertionError(f"{name} was called: validation should have failed first")
+            return launched
+        return getattr(self._lib, name)
+
+
+@pytest.fixture
+def no_launch(monkeypatch):
+    monkeypatch.setattr(B, "_LIB", _NoLaunch(B.library()))
+    yield
+    monkeypatch.setattr(B, "_LIB", None)
+
+
+def _z(*shape):
+    import torch
+    return torch.zeros(*shape)
+
+
+def _conv_ok():
+    # conv3d / conv_maxpool_lse_relu: x[1,4,8,8,8], w[8,4,3,3,3], pad 1
+    return dict(x=_z(1, 4, 8, 8, 8), w=_z(8, 4, 3, 3, 3), bias=_z(8))
+
+
+CONV_BAD = {
+    "x_not_5d": dict(x=_z(4, 8, 8, 8)),
+    "w_not_5d": dict(w=_z(8, 4, 3, 3)),
+    "w_channels": dict(w=_z(8, 3, 3, 3, 3)),
+    "w_channels_groups": dict(w=_z(8, 4, 3, 3, 3), groups=2),
+    "groups_zero": dict(groups=0),
+    "bias_length": dict(bias=_z(7)),
+    "bias_2d": dict(bias=_z(8, 1)),
+    "out_shape": dict(out=_z(1, 8, 8, 8, 7)),
+}
+
+
+@pytest.mark.parametrize("case", list(CONV_BAD))
+def test_conv3d_binding_rejects_mis_shaped_tensors(case, no_launch):
+    a = dict(_conv_ok(), groups=1, out=None)
+    a.update(CONV_BAD[case])
+    with pytest.raises(ValueError):
+        B.conv3d_fwd(a["x"], a["w"], a["bias"], 1, 1, 1, a["groups"], out=a["out"])
+
+
+LSE_BAD = dict(CONV_BAD, out_shape=dict(out=_z(1, 8, 4, 4, 4)))
+
+
+@pytest.mark.parametrize("case", list(LSE_BAD))
+def test_conv_maxpool_lse_relu_binding_rejects_mis_shaped_tensors(case, no_launch):
+    a = dict(_conv_ok(), groups=1, out=None)
+    a.update(LSE_BAD[case])
+    with pytest.raises(ValueError):
+        B.conv_maxpool_lse_relu(a["x"], a["w"], a["bias"], 2, 1, 1, 1, a["groups"], out=a["out"])
+
+
+def _convT_ok():
+    # x[2,8,4,4,4], w[8,16,3,3,3], s2 p1 -> y[2,16,7,7,7]
+    return dict(x=_z(2, 8, 4, 4, 4), w=_z(8, 16, 3, 3, 3), bias=_z(16))
+
+
+CONVT_BAD = {
+    "x_not_5d": dict(x=_z(2, 8, 4, 4)),
+    "w_in_channels": dict(w=_z(4, 16, 3, 3, 3)),
+    "bias_length": dict(bias=_z(8)),
+    "bias_length_groups": dict(bias=_z(16), groups=2),  # Cout = 16 * 2 = 32
+    "out_shape": dict(out=_z(2, 16, 7, 7, 8)),
+}
+
+
+@pytest.mark.parametrize("case", list(CONVT_BAD))
+def test_conv_transpose3d_binding_rejects_mis_shaped_tensors(case, no_launch):
+    a = dict(_convT_ok(), groups=1, out=None)
+    a.update(CONVT_BAD[case])
+    with pytest.raises(ValueError):
+        B.conv_transpose3d_fwd(a["x"], a["w"], a["bias"], 2, 1, 1, 0, a["groups"], out=a["out"])
+
+
+def _bn_ok():
+    # the module's geometry at a small size: x[2,3,8,8,8], w[3,16,3,3,3] -> t[2,16,15,15,15] -> y[2,16,3,3,3]
+    return dict(x=_z(2, 3, 8, 8, 8), w=_z(3, 16, 3, 3, 3), conv_bias=_z(16), gamma=_z(16), beta=_z(16),
+                out=None, workspace=None, batch_mean=None, batch_var=None, running_mean=None, running_var=None,
+                training=True)
+
+
+BN_BAD = {
+    "w_in_channels": dict(w=_z(4, 16, 3, 3, 3)),
+    "conv_bias_length": dict(conv_bias=_z(15)),
+    "gamma_length": dict(gamma=_z(17)),
+    "beta_length": dict(beta=_z(8)),
+    "gamma_missing": dict(gamma=None),
+    "batch_mean_length": dict(batch_mean=_z(15)),
+    "batch_var_length": dict(batch_var=_z(1)),
+    "running_mean_length": dict(running_mean=_z(15), running_var=_z(16)),
+    "running_var_length": dict(running_mean=_z(16), running_var=_z(32)),
+    "running_mean_alone": dict(running_mean=_z(16)),
+    "eval_without_running": dict(training=False),
+    "out_shape": dict(out=_z(2, 16, 3, 3, 4)),
+    "workspace_small": dict(workspace=_z(1)),
+}
+
+
+@pytest.mark.parametrize("case", list(BN_BAD))
+def test_convT_bn_avgpool_binding_rejects_mis_shaped_tensors(case, no_launch):
+    a = _bn_ok()
+    a.update(BN_BAD[case])
+    with pytest.raises(ValueError):
+        B.convT_bn_avgpool(a["x"], a["w"], a["conv_bias"], a["gamma"], a["beta"], 1e-5, 4, 2, 1,
+                           out=a["out"], workspace=a["workspace"], batch_mean=a["batch_mean"],
+                           batch_var=a["batch_var"], training=a["training"], running_mean=a["running_mean"],
+                           running_var=a["running_var"])
+
+
+def test_well_shaped_host_tensors_stop_at_the_device_check(no_launch):
+    """Correct shapes reach the device check, which rejects host tensors
+    (TypeError) before any launch."""
+    c = _conv_ok()
+    with pytest.raises(TypeError):
+        B.conv3d_fwd(c["x"], c["w"], c["bias"], 1, 1, out=_z(1, 8, 8, 8, 8))
+    with pytest.raises(TypeError):
+        B.conv_maxpool_lse_relu(c["x"], c["w"], c["bias"], 2, 1, 1, out=_z(1, 1, 4, 4, 4))
+    t = _convT_ok()
+    with pytest.raises(TypeError):
+        B.conv_transpose3d_fwd(t["x"], t["w"], t["bias"], 2, 1, out=_z(2, 16, 7, 7, 7))
+    a = _bn_ok()
+    with pytest.raises(TypeError):
+        B.convT_bn_avgpool(a["x"], a["w"], a["conv_bias"], a["gamma"], a["beta"], 1e-5, 4, 2, 1,
+                           out=_z(2, 16, 3, 3, 3), workspace=_z(1 << 16), batch_mean=_z(16), batch_var=_z(16),
+                           running_mean=_z(16), running_var=_z(16))
+    with pytest.raises(TypeError):
+        B.probe_mfma_f32(10, _z(1 << 19))
+
+
+def test_variant_override_is_per_thread():
+    """c3d_set_variant changes only the calling thread's kernel choice."""
+    import threading
+
+    params = B.make_params((3, 3, 1), 1, 0, 1, 0, 1)
+    xs, cout = (16, 3, 256, 256, 10), 64
+    old = B.set_variant(1)
+    try:
+        assert B.conv3d_algo(xs, cout, params) == "direct"
+        seen = {}
+
+        def other():
+            seen["algo"] = B.conv3d_algo(xs, cout, params)
+            seen["old"] = B.set_variant(2)
+
+        th = threading.Thread(target=other)
+        th.start()
+        th.join()
+        assert seen == {"algo": "k1last", "old": 0}
+        assert B.conv3d_algo(xs, cout, params) == "direct"  # the other thread's setting did not leak here
+    finally:
+        B.set_variant(old)
 
 
 # ----------------------------------------------------------- kernel choice
@@ -278,3 +447,4 @@ def test_mfma_probe_rejects_bad_arguments_before_launching():
     assert lib.c3d_probe_mfma_f32(10, fake, 1000, ctypes.byref(flop), None) == _code("C3D_ERR_PARAM")
     assert lib.c3d_probe_mfma_f32(10, ctypes.c_void_p(4098), 1 << 20, ctypes.byref(flop), None) == \
         _code("C3D_ERR_ALIGN")
+

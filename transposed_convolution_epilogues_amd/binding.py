@@ -22,10 +22,11 @@ C3D_OK = 0
 STATUS = {0: "C3D_OK", 1: "C3D_ERR_NULL", 2: "C3D_ERR_SHAPE", 3: "C3D_ERR_PARAM", 4: "C3D_ERR_WORKSPACE",
           5: "C3D_ERR_UNSUPPORTED", 6: "C3D_ERR_HIP", 7: "C3D_ERR_ALIGN"}
 
-EXPORTS = ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_bn_avgpool_out_shape",
-           "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
-           "convT_bn_avgpool_workspace_bytes", "convT_bn_avgpool", "convT_bn_avgpool_ex", "conv_maxpool_lse_relu",
-           "c3d_status_string",
+EXPORTS = ("c3d_conv3d_out_dims", "c3d_conv_transpose3d_out_dims", "c3d_convT_bn_avgpool_out_dims",
+           "c3d_conv_maxpool_lse_relu_out_dims", "conv3d_fwd", "conv_transpose3d_fwd",
+           "convT_bn_avgpool_workspace_bytes", "convT_bn_avgpool", "convT_bn_avgpool_ex",
+           "conv_maxpool_lse_relu",
+           "c3d_status_str",
            "c3d_set_variant", "c3d_conv3d_algo", "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo",
            "c3d_probe_mfma_f32")
 
@@ -36,7 +37,7 @@ ALGO = {0: "direct", 1: "k1last", 2: "mfma333", 3: "sublattice", 4: "phase", 5: 
 class C3DError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {STATUS.get(status, status)} ({_lib().c3d_status_string(status).decode()})")
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_lib().c3d_status_str(status).decode()})")
 
 
 class ConvParams(ctypes.Structure):
@@ -84,10 +85,10 @@ def _lib():
     P = ctypes.POINTER(ConvParams)
     vp = ctypes.c_void_p
     i64 = ctypes.c_int64
-    lib.c3d_conv3d_out_shape.argtypes = [i64p, i64, P, i64p]
-    lib.c3d_conv_transpose3d_out_shape.argtypes = [i64p, i64, P, i64p]
-    lib.c3d_convT_bn_avgpool_out_shape.argtypes = [i64p, i64, P, ctypes.c_int32, i64p]
-    lib.c3d_conv_maxpool_lse_relu_out_shape.argtypes = [i64p, i64, P, ctypes.c_int32, i64p]
+    lib.c3d_conv3d_out_dims.argtypes = [i64p, i64, P, i64p]
+    lib.c3d_conv_transpose3d_out_dims.argtypes = [i64p, i64, P, i64p]
+    lib.c3d_convT_bn_avgpool_out_dims.argtypes = [i64p, i64, P, ctypes.c_int32, i64p]
+    lib.c3d_conv_maxpool_lse_relu_out_dims.argtypes = [i64p, i64, P, ctypes.c_int32, i64p]
     lib.conv3d_fwd.argtypes = [vp, i64p, vp, i64, P, vp, vp, vp]
     lib.conv_transpose3d_fwd.argtypes = [vp, i64p, vp, i64, P, vp, vp, vp]
     lib.convT_bn_avgpool_workspace_bytes.argtypes = [i64p, i64, P, ctypes.c_int32]
@@ -97,19 +98,19 @@ def _lib():
     lib.convT_bn_avgpool_ex.argtypes = [vp, i64p, vp, i64, P, vp, vp, vp, ctypes.c_float, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp]
     lib.conv_maxpool_lse_relu.argtypes = [vp, i64p, vp, i64, P, vp, ctypes.c_int32, vp, vp]
-    lib.c3d_status_string.argtypes = [ctypes.c_int]
-    lib.c3d_status_string.restype = ctypes.c_char_p
+    lib.c3d_status_str.argtypes = [ctypes.c_int]  # c3d_status is an int-sized enum
+    lib.c3d_status_str.restype = ctypes.c_char_p
     lib.c3d_set_variant.argtypes = [ctypes.c_int]
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.c3d_conv3d_algo.argtypes = [i64p, i64, P, i32p]
     lib.c3d_conv_transpose3d_algo.argtypes = [i64p, i64, P, i32p]
     lib.c3d_convT_bn_avgpool_algo.argtypes = [i64p, i64, P, ctypes.c_int32, i32p]
     lib.c3d_probe_mfma_f32.argtypes = [i64, ctypes.c_void_p, i64, i64p, ctypes.c_void_p]
-    for name in ("c3d_conv3d_out_shape", "c3d_conv_transpose3d_out_shape", "c3d_convT_bn_avgpool_out_shape",
-                 "c3d_conv_maxpool_lse_relu_out_shape", "conv3d_fwd", "conv_transpose3d_fwd",
+    for name in ("c3d_conv3d_out_dims", "c3d_conv_transpose3d_out_dims", "c3d_convT_bn_avgpool_out_dims",
+                 "c3d_conv_maxpool_lse_relu_out_dims", "conv3d_fwd", "conv_transpose3d_fwd",
                  "convT_bn_avgpool", "convT_bn_avgpool_ex", "conv_maxpool_lse_relu", "c3d_set_variant",
                  "c3d_conv3d_algo",
-                 "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo"):
+                 "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo", "c3d_probe_mfma_f32"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -126,16 +127,106 @@ def _shape5(shape) -> ctypes.Array:
     return (ctypes.c_int64 * 5)(*[int(v) for v in shape])
 
 
-def _dev(t: Optional[torch.Tensor], name: str, required: bool = True):
+# ---------------------------------------------------------------- validation
+# The C ABI takes raw device pointers and cannot see how large a buffer is, so
+# a tensor of the wrong shape would turn into an out-of-bounds device access.
+# Every wrapper below therefore checks, before anything is launched:
+#   1. shapes: x and w are 5-D, the weight's channel dim matches x, every
+#      per-channel vector holds exactly Cout elements, `out` has the shape the
+#      C shape query returns, the workspace holds at least the queried bytes
+#      (ValueError);
+#   2. then every tensor is float32 (the workspace: any dtype), on the GPU
+#      (TypeError), on x's device and contiguous (ValueError).
+# Shapes are checked first, so a mis-shaped call fails the same way with or
+# without a GPU.
+
+
+def _tensor(t, name: str, required: bool = True) -> Optional[torch.Tensor]:
     if t is None:
         if required:
             raise ValueError(f"{name} is required")
         return None
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.float32:
-        raise TypeError(f"{name} must be a float32 tensor on the GPU")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    return t
+
+
+def _rank5(t: torch.Tensor, name: str):
+    if t.dim() != 5:
+        raise ValueError(f"{name} must be 5-D, got shape {tuple(t.shape)}")
+
+
+def _vec(t: Optional[torch.Tensor], name: str, n: int):
+    if t is not None and (t.dim() != 1 or int(t.shape[0]) != n):
+        raise ValueError(f"{name} must have shape ({n},), got {tuple(t.shape)}")
+
+
+def _out(out: Optional[torch.Tensor], shape, like: torch.Tensor) -> torch.Tensor:
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=like.device)
+    out = _tensor(out, "out")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    return out
+
+
+def _placed(x: torch.Tensor, **tensors):
+    """Device checks (after the shape checks): float32, on the GPU, on x's
+    device, contiguous.  Returns the raw pointers by name (None stays None)."""
+    ptrs = {}
+    for name, t in (("x", x),) + tuple(tensors.items()):
+        if t is None:
+            ptrs[name] = None
+            continue
+        if t.dtype != torch.float32 or t.device.type != "cuda":
+            raise TypeError(f"{name} must be a float32 tensor on the GPU (got {t.dtype} on {t.device})")
+        if t.device != x.device:
+            raise ValueError(f"{name} is on {t.device}, x on {x.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        ptrs[name] = ctypes.c_void_p(t.data_ptr())
+    return ptrs
+
+
+def _workspace(ws: torch.Tensor, need: int):
+    ws = _tensor(ws, "workspace")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, the call needs {need}")
+    return ws
+
+
+def _workspace_ptr(ws: torch.Tensor, x: torch.Tensor):
+    if ws.device.type != "cuda":
+        raise TypeError(f"workspace must be on the GPU (got {ws.device})")
+    if ws.device != x.device:
+        raise ValueError(f"workspace is on {ws.device}, x on {x.device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if ws.data_ptr() % 8:
+        raise ValueError("workspace must be 8-byte aligned")
+    return ctypes.c_void_p(ws.data_ptr())
+
+
+def _conv_operands(x, w, groups: int, transposed: bool) -> int:
+    """Checks x and w against each other; returns Cout."""
+    x = _tensor(x, "x")
+    w = _tensor(w, "w")
+    _rank5(x, "x")
+    _rank5(w, "w")
+    groups = int(groups)
+    if groups < 1:
+        raise ValueError(f"groups must be >= 1, got {groups}")
+    if transposed:
+        # [Cin, Cout/groups, k0, k1, k2]
+        if int(w.shape[0]) != int(x.shape[1]):
+            raise ValueError(f"w.shape[0] = {int(w.shape[0])} must equal x's {int(x.shape[1])} input channels")
+        return int(w.shape[1]) * groups
+    # [Cout, Cin/groups, k0, k1, k2]
+    if int(w.shape[1]) * groups != int(x.shape[1]):
+        raise ValueError(f"w.shape[1] * groups = {int(w.shape[1]) * groups} must equal x's {int(x.shape[1])} "
+                         "input channels")
+    return int(w.shape[0])
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -155,8 +246,11 @@ def probe_mfma_f32(iters: int, out: torch.Tensor, stream=None) -> int:
     """Launch the matrix-core throughput probe on the stream; returns the
     launch's FLOP count (time it with events on the same stream)."""
     flop = ctypes.c_int64(0)
-    _check(_lib().c3d_probe_mfma_f32(int(iters), _dev(out, "out"), int(out.numel()), ctypes.byref(flop),
-                                    _stream(stream)), "c3d_probe_mfma_f32")
+    out = _tensor(out, "out")
+    if out.dtype != torch.float32 or out.device.type != "cuda" or not out.is_contiguous():
+        raise TypeError("out must be a contiguous float32 tensor on the GPU")
+    _check(_lib().c3d_probe_mfma_f32(int(iters), ctypes.c_void_p(out.data_ptr()), int(out.numel()),
+                                     ctypes.byref(flop), _stream(stream)), "c3d_probe_mfma_f32")
     return int(flop.value)
 
 
@@ -165,7 +259,8 @@ def set_variant(variant: int) -> int:
     2 = skip the shape-specialised kernels (general MFMA paths where they apply),
     3 = automatic, but the swapped-sums algorithm for convT_bn_avgpool where it applies,
     4 = automatic, but conv_transpose3d_fwd scatters into an LDS output tile,
-    5 = automatic, but convT_bn_avgpool runs its one-thread-per-cell fp32 kernel."""
+    5 = automatic, but convT_bn_avgpool runs its one-thread-per-cell fp32 kernel.
+    The setting is the calling thread's own (the library keeps it thread-local)."""
     return int(_lib().c3d_set_variant(int(variant)))
 
 
@@ -193,31 +288,31 @@ def conv_transpose3d_algo(x_shape, cout: int, params: ConvParams) -> str:
     return ALGO[v.value]
 
 
-def conv3d_out_shape(x_shape, cout: int, params: ConvParams) -> Tuple[int, ...]:
+def conv3d_out_dims(x_shape, cout: int, params: ConvParams) -> Tuple[int, ...]:
     ys = (ctypes.c_int64 * 5)()
-    _check(_lib().c3d_conv3d_out_shape(_shape5(x_shape), int(cout), ctypes.byref(params), ys),
-           "c3d_conv3d_out_shape")
+    _check(_lib().c3d_conv3d_out_dims(_shape5(x_shape), int(cout), ctypes.byref(params), ys),
+           "c3d_conv3d_out_dims")
     return tuple(int(v) for v in ys)
 
 
-def conv_transpose3d_out_shape(x_shape, cout: int, params: ConvParams) -> Tuple[int, ...]:
+def conv_transpose3d_out_dims(x_shape, cout: int, params: ConvParams) -> Tuple[int, ...]:
     ys = (ctypes.c_int64 * 5)()
-    _check(_lib().c3d_conv_transpose3d_out_shape(_shape5(x_shape), int(cout), ctypes.byref(params), ys),
-           "c3d_conv_transpose3d_out_shape")
+    _check(_lib().c3d_conv_transpose3d_out_dims(_shape5(x_shape), int(cout), ctypes.byref(params), ys),
+           "c3d_conv_transpose3d_out_dims")
     return tuple(int(v) for v in ys)
 
 
-def convT_bn_avgpool_out_shape(x_shape, cout: int, params: ConvParams, pool: int) -> Tuple[int, ...]:
+def convT_bn_avgpool_out_dims(x_shape, cout: int, params: ConvParams, pool: int) -> Tuple[int, ...]:
     ys = (ctypes.c_int64 * 5)()
-    _check(_lib().c3d_convT_bn_avgpool_out_shape(_shape5(x_shape), int(cout), ctypes.byref(params), int(pool), ys),
-           "c3d_convT_bn_avgpool_out_shape")
+    _check(_lib().c3d_convT_bn_avgpool_out_dims(_shape5(x_shape), int(cout), ctypes.byref(params), int(pool), ys),
+           "c3d_convT_bn_avgpool_out_dims")
     return tuple(int(v) for v in ys)
 
 
-def conv_maxpool_lse_relu_out_shape(x_shape, cout: int, params: ConvParams, pool: int) -> Tuple[int, ...]:
+def conv_maxpool_lse_relu_out_dims(x_shape, cout: int, params: ConvParams, pool: int) -> Tuple[int, ...]:
     ys = (ctypes.c_int64 * 5)()
-    _check(_lib().c3d_conv_maxpool_lse_relu_out_shape(_shape5(x_shape), int(cout), ctypes.byref(params),
-                                                      int(pool), ys), "c3d_conv_maxpool_lse_relu_out_shape")
+    _check(_lib().c3d_conv_maxpool_lse_relu_out_dims(_shape5(x_shape), int(cout), ctypes.byref(params),
+                                                      int(pool), ys), "c3d_conv_maxpool_lse_relu_out_dims")
     return tuple(int(v) for v in ys)
 
 
@@ -225,15 +320,14 @@ def conv3d_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = 
                pad: Int3 = 0, dilation: Int3 = 1, groups: int = 1, out: Optional[torch.Tensor] = None,
                stream=None) -> torch.Tensor:
     """y = conv3d(x, w, bias); w is [Cout, Cin/groups, k0, k1, k2]."""
+    cout = _conv_operands(x, w, groups, transposed=False)
     params = make_params(tuple(w.shape[2:]), stride, pad, dilation, 0, groups)
-    cout = int(w.shape[0])
-    ys = conv3d_out_shape(x.shape, cout, params)
-    if out is None:
-        out = torch.empty(ys, dtype=torch.float32, device=x.device)
-    elif tuple(out.shape) != ys:
-        raise ValueError(f"out has shape {tuple(out.shape)}, expected {ys}")
-    _check(_lib().conv3d_fwd(_dev(x, "x"), _shape5(x.shape), _dev(w, "w"), cout, ctypes.byref(params),
-                             _dev(bias, "bias", False), _dev(out, "out"), _stream(stream)), "conv3d_fwd")
+    ys = conv3d_out_dims(x.shape, cout, params)
+    _vec(_tensor(bias, "bias", False), "bias", cout)
+    out = _out(out, ys, x)
+    ptr = _placed(x, w=w, bias=bias, out=out)
+    _check(_lib().conv3d_fwd(ptr["x"], _shape5(x.shape), ptr["w"], cout, ctypes.byref(params), ptr["bias"],
+                             ptr["out"], _stream(stream)), "conv3d_fwd")
     return out
 
 
@@ -241,16 +335,14 @@ def conv_transpose3d_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.
                          pad: Int3 = 0, dilation: Int3 = 1, output_pad: Int3 = 0, groups: int = 1,
                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """y = conv_transpose3d(x, w, bias); w is [Cin, Cout/groups, k0, k1, k2]."""
+    cout = _conv_operands(x, w, groups, transposed=True)
     params = make_params(tuple(w.shape[2:]), stride, pad, dilation, output_pad, groups)
-    cout = int(w.shape[1]) * int(groups)
-    ys = conv_transpose3d_out_shape(x.shape, cout, params)
-    if out is None:
-        out = torch.empty(ys, dtype=torch.float32, device=x.device)
-    elif tuple(out.shape) != ys:
-        raise ValueError(f"out has shape {tuple(out.shape)}, expected {ys}")
-    _check(_lib().conv_transpose3d_fwd(_dev(x, "x"), _shape5(x.shape), _dev(w, "w"), cout, ctypes.byref(params),
-                                       _dev(bias, "bias", False), _dev(out, "out"), _stream(stream)),
-           "conv_transpose3d_fwd")
+    ys = conv_transpose3d_out_dims(x.shape, cout, params)
+    _vec(_tensor(bias, "bias", False), "bias", cout)
+    out = _out(out, ys, x)
+    ptr = _placed(x, w=w, bias=bias, out=out)
+    _check(_lib().conv_transpose3d_fwd(ptr["x"], _shape5(x.shape), ptr["w"], cout, ctypes.byref(params),
+                                       ptr["bias"], ptr["out"], _stream(stream)), "conv_transpose3d_fwd")
     return out
 
 
@@ -271,30 +363,39 @@ def convT_bn_avgpool(x: torch.Tensor, w: torch.Tensor, conv_bias: Optional[torch
     normalises with the batch statistics and, when running_mean/running_var
     are given, updates them in place; eval mode (training=False) normalises
     with them."""
+    cout = _conv_operands(x, w, groups, transposed=True)
     params = make_params(tuple(w.shape[2:]), stride, pad, dilation, output_pad, groups)
-    cout = int(w.shape[1]) * int(groups)
-    ys = convT_bn_avgpool_out_shape(x.shape, cout, params, pool)
-    if out is None:
-        out = torch.empty(ys, dtype=torch.float32, device=x.device)
-    plain = training and running_mean is None and running_var is None
+    ys = convT_bn_avgpool_out_dims(x.shape, cout, params, pool)
+    vecs = dict(conv_bias=_tensor(conv_bias, "conv_bias", False), gamma=_tensor(gamma, "gamma"),
+                beta=_tensor(beta, "beta"), batch_mean=_tensor(batch_mean, "batch_mean", False),
+                batch_var=_tensor(batch_var, "batch_var", False),
+                running_mean=_tensor(running_mean, "running_mean", False),
+                running_var=_tensor(running_var, "running_var", False))
+    for name, t in vecs.items():
+        _vec(t, name, cout)
+    if (running_mean is None) != (running_var is None):
+        raise ValueError("running_mean and running_var go together")
+    if not training and running_mean is None:
+        raise ValueError("eval mode (training=False) needs running_mean and running_var")
+    out = _out(out, ys, x)
     if training:
         nbytes = convT_bn_avgpool_workspace_bytes(x.shape, cout, params, pool)
         if workspace is None:
             workspace = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=x.device)
-        ws_ptr, ws_bytes = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+        workspace = _workspace(workspace, nbytes)
+    ptr = _placed(x, w=w, out=out, **vecs)
+    if training:
+        ws_ptr, ws_bytes = _workspace_ptr(workspace, x), workspace.numel() * workspace.element_size()
     else:
         ws_ptr, ws_bytes = None, 0
-    head = (_dev(x, "x"), _shape5(x.shape), _dev(w, "w"), cout, ctypes.byref(params),
-            _dev(conv_bias, "conv_bias", False), _dev(gamma, "gamma"), _dev(beta, "beta"), float(eps), int(pool))
-    tail = (ws_ptr, ws_bytes, _dev(batch_mean, "batch_mean", False), _dev(batch_var, "batch_var", False),
-            _stream(stream))
-    if plain:
-        _check(_lib().convT_bn_avgpool(*head, _dev(out, "out"), *tail), "convT_bn_avgpool")
+    head = (ptr["x"], _shape5(x.shape), ptr["w"], cout, ctypes.byref(params), ptr["conv_bias"], ptr["gamma"],
+            ptr["beta"], float(eps), int(pool))
+    tail = (ws_ptr, ws_bytes, ptr["batch_mean"], ptr["batch_var"], _stream(stream))
+    if training and running_mean is None:
+        _check(_lib().convT_bn_avgpool(*head, ptr["out"], *tail), "convT_bn_avgpool")
     else:
-        _check(_lib().convT_bn_avgpool_ex(*head, int(bool(training)), float(momentum),
-                                          _dev(running_mean, "running_mean", False),
-                                          _dev(running_var, "running_var", False), _dev(out, "out"), *tail),
-               "convT_bn_avgpool_ex")
+        _check(_lib().convT_bn_avgpool_ex(*head, int(bool(training)), float(momentum), ptr["running_mean"],
+                                          ptr["running_var"], ptr["out"], *tail), "convT_bn_avgpool_ex")
     return out
 
 
@@ -302,12 +403,13 @@ def conv_maxpool_lse_relu(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch
                           stride: Int3 = 1, pad: Int3 = 1, dilation: Int3 = 1, groups: int = 1,
                           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Conv3d -> MaxPool3d(pool) -> logsumexp over channels (keepdim) -> ReLU."""
+    cout = _conv_operands(x, w, groups, transposed=False)
     params = make_params(tuple(w.shape[2:]), stride, pad, dilation, 0, groups)
-    cout = int(w.shape[0])
-    ys = conv_maxpool_lse_relu_out_shape(x.shape, cout, params, pool)
-    if out is None:
-        out = torch.empty(ys, dtype=torch.float32, device=x.device)
-    _check(_lib().conv_maxpool_lse_relu(_dev(x, "x"), _shape5(x.shape), _dev(w, "w"), cout, ctypes.byref(params),
-                                        _dev(bias, "bias", False), int(pool), _dev(out, "out"), _stream(stream)),
+    ys = conv_maxpool_lse_relu_out_dims(x.shape, cout, params, pool)
+    _vec(_tensor(bias, "bias", False), "bias", cout)
+    out = _out(out, ys, x)
+    ptr = _placed(x, w=w, bias=bias, out=out)
+    _check(_lib().conv_maxpool_lse_relu(ptr["x"], _shape5(x.shape), ptr["w"], cout, ctypes.byref(params),
+                                        ptr["bias"], int(pool), ptr["out"], _stream(stream)),
            "conv_maxpool_lse_relu")
     return out

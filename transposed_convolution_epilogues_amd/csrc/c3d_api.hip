@@ -1,6 +1,5 @@
 // c3d_api.hip - the C ABI declared in include/c3d.h: host-side validation,
 // output-shape rules, and dispatch to the fast or the generic kernels.
-#include <atomic>
 #include <math.h>
 
 #include "../../include/c3d.h"
@@ -11,7 +10,10 @@ using c3d::PoolGeom;
 
 namespace {
 
-std::atomic<int> g_variant{0};
+// Kernel-variant override of c3d_set_variant.  It is per calling thread, so a
+// setting made for an A/B run on one thread never changes the kernels that
+// calls from other threads run.
+thread_local int t_variant = 0;
 
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
@@ -26,7 +28,7 @@ int64_t convT_len(int64_t L, int32_t k, int32_t s, int32_t p, int32_t d, int32_t
     return (L - 1) * s - 2 * (int64_t)p + (int64_t)d * (k - 1) + op + 1;
 }
 
-int check_params(const c3d_conv_params* p, bool transposed) {
+c3d_status check_params(const c3d_conv_params* p, bool transposed) {
     for (int j = 0; j < 3; ++j) {
         if (p->kernel[j] < 1 || p->stride[j] < 1 || p->dilation[j] < 1 || p->pad[j] < 0) return C3D_ERR_PARAM;
         if (p->kernel[j] > 64 || p->stride[j] > 1024 || p->dilation[j] > 1024 || p->pad[j] > 65536)
@@ -43,9 +45,9 @@ int check_params(const c3d_conv_params* p, bool transposed) {
 }
 
 // Resolves and validates the geometry.  No HIP call is made here.
-int resolve(const int64_t xs[5], int64_t cout, const c3d_conv_params* p, bool transposed, Geom* g) {
+c3d_status resolve(const int64_t xs[5], int64_t cout, const c3d_conv_params* p, bool transposed, Geom* g) {
     if (!xs || !p || !g) return C3D_ERR_NULL;
-    int st = check_params(p, transposed);
+    c3d_status st = check_params(p, transposed);
     if (st) return st;
     for (int j = 0; j < 5; ++j)
         if (xs[j] < 1 || xs[j] > ((int64_t)1 << 40)) return C3D_ERR_SHAPE;
@@ -76,7 +78,7 @@ int resolve(const int64_t xs[5], int64_t cout, const c3d_conv_params* p, bool tr
     return C3D_OK;
 }
 
-int resolve_pool(const Geom& g, int32_t pool, PoolGeom* pg) {
+c3d_status resolve_pool(const Geom& g, int32_t pool, PoolGeom* pg) {
     if (pool < 1 || pool > 64) return C3D_ERR_PARAM;
     pg->g = g;
     pg->pool = pool;
@@ -88,7 +90,7 @@ int resolve_pool(const Geom& g, int32_t pool, PoolGeom* pg) {
     return C3D_OK;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? C3D_OK : C3D_ERR_HIP; }
+c3d_status hip_status(hipError_t e) { return e == hipSuccess ? C3D_OK : C3D_ERR_HIP; }
 
 // Kernel choice (the C3D_ALGO_* codes of c3d.h).  Variant 1 forces the
 // generic kernels; variant 2 skips the shape-specialised ones (the
@@ -98,7 +100,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? C3D_OK : C3D_ERR_HIP; }
 // ConvT -> BatchNorm -> AvgPool module (swapped sums) and of the transposed
 // conv (LDS scatter).
 int conv3d_algo(const Geom& g) {
-    const int v = g_variant.load();
+    const int v = t_variant;
     if (v == 1) return C3D_ALGO_DIRECT;
     if (v != 2 && c3d::conv_k1last_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_K1LAST;
     if (c3d::conv3x3x3_mfma_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_MFMA333;
@@ -110,7 +112,7 @@ int conv3d_algo(const Geom& g) {
 // cell otherwise or with variant 5, the swapped sums (variant 3; measured
 // slower on MI355X, kept as the second algorithm), generic (variant 1)
 int bn_algo(const PoolGeom& pg) {
-    const int v = g_variant.load();
+    const int v = t_variant;
     if (v == 1) return C3D_ALGO_DIRECT;
     if (v == 3 && c3d::convT_bn_swap_supported(pg, nullptr)) return C3D_ALGO_BN_SWAP;
     if (v != 5 && c3d::convT_bn_pool_mfma_supported(pg, nullptr)) return C3D_ALGO_BN_MFMA;
@@ -119,13 +121,24 @@ int bn_algo(const PoolGeom& pg) {
 }
 
 int convT_algo(const Geom& g) {
-    const int v = g_variant.load();
+    const int v = t_variant;
     if (v == 1) return C3D_ALGO_DIRECT;
     if (v == 4 && c3d::convT_scatter_supported(g)) return C3D_ALGO_SCATTER;
     if (v != 2 && c3d::convT_s2_sublattice_supported(g, nullptr, nullptr, nullptr))
         return C3D_ALGO_SUBLATTICE;
     if (c3d::convT_phase_mfma_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_PHASE;
     return C3D_ALGO_DIRECT;
+}
+
+// float64 partials per channel that phase 1 of a training-mode call leaves
+// for phase 2, and the workspace bytes the call needs, for kernel `algo`
+size_t bn_parts(const PoolGeom& pg, int algo) {
+    return algo == C3D_ALGO_BN_MFMA ? c3d::convT_bn_pool_mfma_partials(pg) : c3d::convT_bn_pool_partials(pg, 0);
+}
+
+size_t bn_training_bytes(const PoolGeom& pg, int algo) {
+    if (algo == C3D_ALGO_BN_SWAP) return c3d::convT_bn_swap_workspace_bytes(pg);
+    return bn_parts(pg, algo) * (size_t)pg.g.Cout * 2 * sizeof(double);
 }
 
 void write_shape(const Geom& g, int64_t ys[5]) {
@@ -139,9 +152,13 @@ void write_shape(const Geom& g, int64_t ys[5]) {
 #pragma GCC visibility push(default)
 extern "C" {
 
-int c3d_set_variant(int variant) { return g_variant.exchange(variant); }
+int c3d_set_variant(int variant) {
+    const int old = t_variant;
+    t_variant = variant;
+    return old;
+}
 
-int c3d_probe_mfma_f32(int64_t iters, float* out, int64_t out_len, int64_t* flop, void* stream) {
+c3d_status c3d_probe_mfma_f32(int64_t iters, float* out, int64_t out_len, int64_t* flop, void* stream) {
     if (!out || !flop) return C3D_ERR_NULL;
     if (!aligned4(out)) return C3D_ERR_ALIGN;
     if (iters < 1 || iters > ((int64_t)1 << 24) || out_len < c3d::mfma_probe_out_len()) return C3D_ERR_PARAM;
@@ -149,7 +166,7 @@ int c3d_probe_mfma_f32(int64_t iters, float* out, int64_t out_len, int64_t* flop
     return hip_status(c3d::launch_mfma_probe(iters, out, (hipStream_t)stream));
 }
 
-const char* c3d_status_string(int status) {
+const char* c3d_status_str(c3d_status status) {
     switch (status) {
         case C3D_OK: return "ok";
         case C3D_ERR_NULL: return "a required pointer is NULL";
@@ -164,31 +181,31 @@ const char* c3d_status_string(int status) {
     }
 }
 
-int c3d_conv3d_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int64_t y_shape[5]) {
+c3d_status c3d_conv3d_out_dims(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int64_t y_shape[5]) {
     if (!y_shape) return C3D_ERR_NULL;
     Geom g;
-    int st = resolve(x_shape, cout, p, false, &g);
+    c3d_status st = resolve(x_shape, cout, p, false, &g);
     if (st) return st;
     write_shape(g, y_shape);
     return C3D_OK;
 }
 
-int c3d_conv_transpose3d_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+c3d_status c3d_conv_transpose3d_out_dims(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
                                    int64_t y_shape[5]) {
     if (!y_shape) return C3D_ERR_NULL;
     Geom g;
-    int st = resolve(x_shape, cout, p, true, &g);
+    c3d_status st = resolve(x_shape, cout, p, true, &g);
     if (st) return st;
     write_shape(g, y_shape);
     return C3D_OK;
 }
 
-int c3d_convT_bn_avgpool_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+c3d_status c3d_convT_bn_avgpool_out_dims(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
                                    int32_t pool, int64_t y_shape[5]) {
     if (!y_shape) return C3D_ERR_NULL;
     Geom g;
     PoolGeom pg;
-    int st = resolve(x_shape, cout, p, true, &g);
+    c3d_status st = resolve(x_shape, cout, p, true, &g);
     if (st) return st;
     st = resolve_pool(g, pool, &pg);
     if (st) return st;
@@ -198,12 +215,12 @@ int c3d_convT_bn_avgpool_out_shape(const int64_t x_shape[5], int64_t cout, const
     return C3D_OK;
 }
 
-int c3d_conv_maxpool_lse_relu_out_shape(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
+c3d_status c3d_conv_maxpool_lse_relu_out_dims(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p,
                                         int32_t pool, int64_t y_shape[5]) {
     if (!y_shape) return C3D_ERR_NULL;
     Geom g;
     PoolGeom pg;
-    int st = resolve(x_shape, cout, p, false, &g);
+    c3d_status st = resolve(x_shape, cout, p, false, &g);
     if (st) return st;
     st = resolve_pool(g, pool, &pg);
     if (st) return st;
@@ -213,12 +230,12 @@ int c3d_conv_maxpool_lse_relu_out_shape(const int64_t x_shape[5], int64_t cout, 
     return C3D_OK;
 }
 
-int conv3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout, const c3d_conv_params* p,
+c3d_status conv3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout, const c3d_conv_params* p,
                const float* bias, float* y, void* stream) {
     if (!x || !w || !y) return C3D_ERR_NULL;
     if (!aligned4(x) || !aligned4(w) || !aligned4(y) || !aligned4(bias)) return C3D_ERR_ALIGN;
     Geom g;
-    int st = resolve(x_shape, cout, p, false, &g);
+    c3d_status st = resolve(x_shape, cout, p, false, &g);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     switch (conv3d_algo(g)) {
@@ -228,12 +245,12 @@ int conv3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t
     }
 }
 
-int conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+c3d_status conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
                          const c3d_conv_params* p, const float* bias, float* y, void* stream) {
     if (!x || !w || !y) return C3D_ERR_NULL;
     if (!aligned4(x) || !aligned4(w) || !aligned4(y) || !aligned4(bias)) return C3D_ERR_ALIGN;
     Geom g;
-    int st = resolve(x_shape, cout, p, true, &g);
+    c3d_status st = resolve(x_shape, cout, p, true, &g);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     switch (convT_algo(g)) {
@@ -244,21 +261,21 @@ int conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const float* 
     }
 }
 
-int c3d_conv3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo) {
+c3d_status c3d_conv3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo) {
     if (!algo) return C3D_ERR_NULL;
     Geom g;
-    const int st = resolve(x_shape, cout, p, false, &g);
+    const c3d_status st = resolve(x_shape, cout, p, false, &g);
     if (st) return st;
     *algo = conv3d_algo(g);
     return C3D_OK;
 }
 
-int c3d_convT_bn_avgpool_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t pool,
+c3d_status c3d_convT_bn_avgpool_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t pool,
                               int32_t* algo) {
     if (!algo) return C3D_ERR_NULL;
     Geom g;
     PoolGeom pg;
-    int st = resolve(x_shape, cout, p, true, &g);
+    c3d_status st = resolve(x_shape, cout, p, true, &g);
     if (st) return st;
     st = resolve_pool(g, pool, &pg);
     if (st) return st;
@@ -266,10 +283,10 @@ int c3d_convT_bn_avgpool_algo(const int64_t x_shape[5], int64_t cout, const c3d_
     return C3D_OK;
 }
 
-int c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo) {
+c3d_status c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo) {
     if (!algo) return C3D_ERR_NULL;
     Geom g;
-    const int st = resolve(x_shape, cout, p, true, &g);
+    const c3d_status st = resolve(x_shape, cout, p, true, &g);
     if (st) return st;
     *algo = convT_algo(g);
     return C3D_OK;
@@ -295,7 +312,7 @@ size_t convT_bn_avgpool_workspace_bytes(const int64_t x_shape[5], int64_t cout, 
     return need;
 }
 
-int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+c3d_status convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
                         const c3d_conv_params* p, const float* conv_bias, const float* gamma, const float* beta,
                         float eps, int32_t pool, int32_t training, float momentum, float* running_mean,
                         float* running_var, float* y, void* ws, size_t ws_bytes, float* batch_mean,
@@ -312,7 +329,7 @@ int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w
     if (training && update && !(momentum >= 0.f && momentum <= 1.f)) return C3D_ERR_PARAM;
     Geom g;
     PoolGeom pg;
-    int st = resolve(x_shape, cout, p, true, &g);
+    c3d_status st = resolve(x_shape, cout, p, true, &g);
     if (st) return st;
     st = resolve_pool(g, pool, &pg);
     if (st) return st;
@@ -329,10 +346,8 @@ int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w
         }
     }
     if (update && g.N * g.O[0] * g.O[1] * g.O[2] < 2) return C3D_ERR_SHAPE;  // no unbiased variance
-    const size_t parts =
-        algo == C3D_ALGO_BN_MFMA ? c3d::convT_bn_pool_mfma_partials(pg) : c3d::convT_bn_pool_partials(pg, 0);
-    const size_t need = algo == C3D_ALGO_BN_SWAP ? c3d::convT_bn_swap_workspace_bytes(pg)
-                                                 : parts * (size_t)g.Cout * 2 * sizeof(double);
+    const size_t parts = bn_parts(pg, algo);
+    const size_t need = bn_training_bytes(pg, algo);
     if (!ws || ws_bytes < need) return C3D_ERR_WORKSPACE;
     if (((uintptr_t)ws & 7u) != 0) return C3D_ERR_ALIGN;
     double* part = (double*)ws;
@@ -355,7 +370,7 @@ int convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const float* w
                                                  batch_var, run, pg, s));
 }
 
-int convT_bn_avgpool(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+c3d_status convT_bn_avgpool(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
                      const c3d_conv_params* p, const float* conv_bias, const float* gamma, const float* beta,
                      float eps, int32_t pool, float* y, void* ws, size_t ws_bytes, float* batch_mean,
                      float* batch_var, void* stream) {
@@ -363,18 +378,18 @@ int convT_bn_avgpool(const float* x, const int64_t x_shape[5], const float* w, i
                                y, ws, ws_bytes, batch_mean, batch_var, stream);
 }
 
-int conv_maxpool_lse_relu(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+c3d_status conv_maxpool_lse_relu(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
                           const c3d_conv_params* p, const float* bias, int32_t pool, float* y, void* stream) {
     if (!x || !w || !y) return C3D_ERR_NULL;
     if (!aligned4(x) || !aligned4(w) || !aligned4(y) || !aligned4(bias)) return C3D_ERR_ALIGN;
     Geom g;
     PoolGeom pg;
-    int st = resolve(x_shape, cout, p, false, &g);
+    c3d_status st = resolve(x_shape, cout, p, false, &g);
     if (st) return st;
     st = resolve_pool(g, pool, &pg);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (g_variant.load() != 1 && c3d::conv_pool_lse_mfma_supported(pg, x, w))
+    if (t_variant != 1 && c3d::conv_pool_lse_mfma_supported(pg, x, w))
         return hip_status(c3d::launch_conv_pool_lse_mfma(x, w, bias, y, pg, s));
     return hip_status(c3d::launch_conv_pool_lse_relu_direct(x, w, bias, y, pg, s));
 }
