@@ -51,7 +51,9 @@ typedef enum {
     C3D_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the query returns  */
     C3D_ERR_UNSUPPORTED = 5, /* valid request outside what the library implements   */
     C3D_ERR_HIP = 6,         /* the HIP runtime reported an error at launch          */
-    C3D_ERR_ALIGN = 7        /* a pointer is not 4-byte aligned                      */
+    C3D_ERR_ALIGN = 7,       /* a pointer is not 4-byte aligned                      */
+    C3D_ERR_SCRATCH_LIMIT = 8 /* convT_bn_avgpool_noalloc: the call needs more than  */
+                             /* its static scratch of C3D_NOALLOC_SCRATCH_BYTES      */
 } c3d_status;
 
 /* Convolution hyper-parameters, as in PyTorch's Conv3d / ConvTranspose3d
@@ -177,6 +179,33 @@ c3d_status convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const f
                         float eps, int32_t pool, int32_t training, float momentum, float* running_mean,
                         float* running_var, float* y, void* ws, size_t ws_bytes, float* batch_mean,
                         float* batch_var, void* stream);
+
+/* Size of the static device scratch convT_bn_avgpool_noalloc uses (per GPU,
+ * held until the process ends). */
+#define C3D_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* convT_bn_avgpool without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, result and kernels as
+ * convT_bn_avgpool (training mode, batch statistics) minus ws / ws_bytes:
+ * the float64 BatchNorm partials go to a static device array of
+ * C3D_NOALLOC_SCRATCH_BYTES that the library owns, one per GPU.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * the first call on a device looks up that device's copy of the array.
+ *   stream   must belong to the current device (else C3D_ERR_PARAM).
+ *   Errors   as convT_bn_avgpool; C3D_ERR_SCRATCH_LIMIT when the arguments
+ *            need more than C3D_NOALLOC_SCRATCH_BYTES of partials (64 x 16
+ *            channels x 63^3 outputs need 256 KiB on the default kernel);
+ *            nothing is launched then.
+ * All calls on one GPU share its scratch, which keeps the last call's
+ * partials: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.  Nothing in the
+ * scratch needs to start at zero: phase 1 writes every partial phase 2
+ * reads. */
+c3d_status convT_bn_avgpool_noalloc(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+                                    const c3d_conv_params* p, const float* conv_bias, const float* gamma,
+                                    const float* beta, float eps, int32_t pool, float* y, float* batch_mean,
+                                    float* batch_var, void* stream);
 
 /* Conv3d -> MaxPool3d(pool, stride pool) -> logsumexp over channels
  * (keepdim) -> ReLU ("Kimi-K2.6 l2_p43": the module, floor-mode pooling and

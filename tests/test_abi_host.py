@@ -448,3 +448,20 @@ def test_mfma_probe_rejects_bad_arguments_before_launching():
     assert lib.c3d_probe_mfma_f32(10, ctypes.c_void_p(4098), 1 << 20, ctypes.byref(flop), None) == \
         _code("C3D_ERR_ALIGN")
 
+
+def test_noalloc_refuses_more_than_its_scratch_before_any_hip_call():
+    """convT_bn_avgpool_noalloc checks the partials its kernels need against
+    its static scratch before it touches the GPU (no GPU is needed here)."""
+    wl = W.CONFIGS["c4"].with_(x_shape=(4096, 3, 32, 32, 32))  # about 16 MiB of partials
+    p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+    assert B.convT_bn_avgpool_workspace_bytes(wl.x_shape, wl.cout, p, wl.pool) > B.NOALLOC_SCRATCH_BYTES
+    lib = B.library()
+    vp = ctypes.c_void_p
+    st = lib.convT_bn_avgpool_noalloc(vp(4096), B._shape5(wl.x_shape), vp(8192), wl.cout, ctypes.byref(p), None,
+                                      vp(12288), vp(16384), 1e-5, 4, vp(20480), None, None, None)
+    assert st == 8  # C3D_ERR_SCRATCH_LIMIT
+    assert b"static scratch" in lib.c3d_status_str(8)
+    # invalid geometry is still reported as such
+    st = lib.convT_bn_avgpool_noalloc(vp(4096), B._shape5((1, 3, 1, 1, 1)), vp(8192), wl.cout, ctypes.byref(p),
+                                      None, vp(12288), vp(16384), 1e-5, 4, vp(20480), None, None, None)
+    assert st == 2

@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(HERE, "libc3d.so")
 
 C3D_OK = 0
 STATUS = {0: "C3D_OK", 1: "C3D_ERR_NULL", 2: "C3D_ERR_SHAPE", 3: "C3D_ERR_PARAM", 4: "C3D_ERR_WORKSPACE",
-          5: "C3D_ERR_UNSUPPORTED", 6: "C3D_ERR_HIP", 7: "C3D_ERR_ALIGN"}
+          5: "C3D_ERR_UNSUPPORTED", 6: "C3D_ERR_HIP", 7: "C3D_ERR_ALIGN", 8: "C3D_ERR_SCRATCH_LIMIT"}
+NOALLOC_SCRATCH_BYTES = 4 << 20  # C3D_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ("c3d_conv3d_out_dims", "c3d_conv_transpose3d_out_dims", "c3d_convT_bn_avgpool_out_dims",
            "c3d_conv_maxpool_lse_relu_out_dims", "conv3d_fwd", "conv_transpose3d_fwd",
-           "convT_bn_avgpool_workspace_bytes", "convT_bn_avgpool", "convT_bn_avgpool_ex",
+           "convT_bn_avgpool_workspace_bytes", "convT_bn_avgpool", "convT_bn_avgpool_ex", "convT_bn_avgpool_noalloc",
            "conv_maxpool_lse_relu",
            "c3d_status_str",
            "c3d_set_variant", "c3d_conv3d_algo", "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo",
@@ -98,6 +99,8 @@ def _lib():
     lib.convT_bn_avgpool_ex.argtypes = [vp, i64p, vp, i64, P, vp, vp, vp, ctypes.c_float, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp]
     lib.conv_maxpool_lse_relu.argtypes = [vp, i64p, vp, i64, P, vp, ctypes.c_int32, vp, vp]
+    lib.convT_bn_avgpool_noalloc.argtypes = [vp, i64p, vp, i64, P, vp, vp, vp, ctypes.c_float, ctypes.c_int32, vp,
+                                             vp, vp, vp]
     lib.c3d_status_str.argtypes = [ctypes.c_int]  # c3d_status is an int-sized enum
     lib.c3d_status_str.restype = ctypes.c_char_p
     lib.c3d_set_variant.argtypes = [ctypes.c_int]
@@ -110,7 +113,8 @@ def _lib():
                  "c3d_conv_maxpool_lse_relu_out_dims", "conv3d_fwd", "conv_transpose3d_fwd",
                  "convT_bn_avgpool", "convT_bn_avgpool_ex", "conv_maxpool_lse_relu", "c3d_set_variant",
                  "c3d_conv3d_algo",
-                 "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo", "c3d_probe_mfma_f32"):
+                 "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo", "c3d_probe_mfma_f32",
+                 "convT_bn_avgpool_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -396,6 +400,33 @@ def convT_bn_avgpool(x: torch.Tensor, w: torch.Tensor, conv_bias: Optional[torch
     else:
         _check(_lib().convT_bn_avgpool_ex(*head, int(bool(training)), float(momentum), ptr["running_mean"],
                                           ptr["running_var"], ptr["out"], *tail), "convT_bn_avgpool_ex")
+    return out
+
+
+def convT_bn_avgpool_noalloc(x: torch.Tensor, w: torch.Tensor, conv_bias: Optional[torch.Tensor],
+                             gamma: torch.Tensor, beta: torch.Tensor, out: torch.Tensor, eps: float = 1e-5,
+                             pool: int = 4, stride: Int3 = 2, pad: Int3 = 1, dilation: Int3 = 1,
+                             output_pad: Int3 = 0, groups: int = 1, batch_mean: Optional[torch.Tensor] = None,
+                             batch_var: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """convT_bn_avgpool (training mode, batch statistics) through the entry
+    point that allocates nothing: its partials go to the library's static
+    per-GPU scratch, and the caller passes `out`.  Calls that overlap on one
+    GPU share that scratch and race."""
+    cout = _conv_operands(x, w, groups, transposed=True)
+    params = make_params(tuple(w.shape[2:]), stride, pad, dilation, output_pad, groups)
+    ys = convT_bn_avgpool_out_dims(x.shape, cout, params, pool)
+    vecs = dict(conv_bias=_tensor(conv_bias, "conv_bias", False), gamma=_tensor(gamma, "gamma"),
+                beta=_tensor(beta, "beta"), batch_mean=_tensor(batch_mean, "batch_mean", False),
+                batch_var=_tensor(batch_var, "batch_var", False))
+    for name, t in vecs.items():
+        _vec(t, name, cout)
+    out = _tensor(out, "out")
+    out = _out(out, ys, x)
+    ptr = _placed(x, w=w, out=out, **vecs)
+    _check(_lib().convT_bn_avgpool_noalloc(ptr["x"], _shape5(x.shape), ptr["w"], cout, ctypes.byref(params),
+                                           ptr["conv_bias"], ptr["gamma"], ptr["beta"], float(eps), int(pool),
+                                           ptr["out"], ptr["batch_mean"], ptr["batch_var"], _stream(stream)),
+           "convT_bn_avgpool_noalloc")
     return out
 
 

@@ -2,11 +2,21 @@
 // output-shape rules, and dispatch to the fast or the generic kernels.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/c3d.h"
 #include "c3d_internal.h"
 
 using c3d::Geom;
 using c3d::PoolGeom;
+
+// Scratch of convT_bn_avgpool_noalloc: the BatchNorm partials that the
+// allocating entry points keep in the caller's workspace.  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code
+// never passes the name `scratch` to a kernel (on the host it is only a
+// stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[C3D_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -91,6 +101,24 @@ c3d_status resolve_pool(const Geom& g, int32_t pool, PoolGeom* pg) {
 }
 
 c3d_status hip_status(hipError_t e) { return e == hipSuccess ? C3D_OK : C3D_ERR_HIP; }
+
+// Device address of `scratch` on each GPU, looked up once per device (with
+// that device current) on the first no-allocation call there.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+c3d_status scratch_on_device(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return C3D_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return C3D_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return C3D_OK;
+}
 
 // Kernel choice (the C3D_ALGO_* codes of c3d.h).  Variant 1 forces the
 // generic kernels; variant 2 skips the shape-specialised ones (the
@@ -177,6 +205,8 @@ const char* c3d_status_str(c3d_status status) {
         case C3D_ERR_UNSUPPORTED: return "unsupported request";
         case C3D_ERR_HIP: return "HIP runtime error at launch";
         case C3D_ERR_ALIGN: return "pointer not 4-byte aligned";
+        case C3D_ERR_SCRATCH_LIMIT:
+            return "the call needs more than the no-allocation entry point's static scratch holds";
         default: return "unknown status";
     }
 }
@@ -376,6 +406,36 @@ c3d_status convT_bn_avgpool(const float* x, const int64_t x_shape[5], const floa
                      float* batch_var, void* stream) {
     return convT_bn_avgpool_ex(x, x_shape, w, cout, p, conv_bias, gamma, beta, eps, pool, 1, 0.f, nullptr, nullptr,
                                y, ws, ws_bytes, batch_mean, batch_var, stream);
+}
+
+c3d_status convT_bn_avgpool_noalloc(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
+                                    const c3d_conv_params* p, const float* conv_bias, const float* gamma,
+                                    const float* beta, float eps, int32_t pool, float* y, float* batch_mean,
+                                    float* batch_var, void* stream) {
+    // the geometry first, so that a request beyond the static scratch is
+    // rejected before any HIP call
+    Geom g;
+    PoolGeom pg;
+    c3d_status st = resolve(x_shape, cout, p, true, &g);
+    if (st) return st;
+    st = resolve_pool(g, pool, &pg);
+    if (st) return st;
+    if (bn_training_bytes(pg, bn_algo(pg)) > (size_t)C3D_NOALLOC_SCRATCH_BYTES) return C3D_ERR_SCRATCH_LIMIT;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return C3D_ERR_HIP;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return C3D_ERR_HIP;
+        if (sdev != dev) return C3D_ERR_PARAM;  // the scratch looked up is the current device's
+    }
+    void* ws = nullptr;
+    st = scratch_on_device(dev, &ws);
+    if (st) return st;
+    // the kernels of the allocating entry point, with the scratch as their
+    // workspace; phase 1 writes every partial phase 2 reads, so nothing in
+    // the scratch has to start at zero
+    return convT_bn_avgpool_ex(x, x_shape, w, cout, p, conv_bias, gamma, beta, eps, pool, 1, 0.f, nullptr, nullptr,
+                               y, ws, (size_t)C3D_NOALLOC_SCRATCH_BYTES, batch_mean, batch_var, stream);
 }
 
 c3d_status conv_maxpool_lse_relu(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
