@@ -381,6 +381,24 @@ def test_c4_matrix_core_medium(name):
     check_full(wl, W.make_inputs(wl), name)
 
 
+def test_c4_matrix_core_unaligned_input():
+    """x 4 bytes off a 16-byte boundary: the matrix-core path stages the input
+    box with scalar loads instead of 16-byte ones (S2 % 4 == 0 here)."""
+    wl = W.CONFIGS["c4"].with_(x_shape=(2, 3, 9, 10, 20))
+    inp = W.make_inputs(wl)
+    ref, ref_mean, ref_var = O.run_workload(wl, inp)
+    flat = torch.empty(int(np.prod(wl.x_shape)) + 1, dtype=torch.float32, device="cuda")
+    x = flat[1:].view(wl.x_shape)
+    x.copy_(dev(inp.x))
+    assert x.data_ptr() % 16 == 4
+    out, mean, var = poisoned(ref.shape), poisoned((wl.cout,)), poisoned((wl.cout,))
+    B.convT_bn_avgpool(x, dev(inp.w), dev(inp.b), dev(inp.gamma), dev(inp.beta), wl.eps, wl.pool, wl.stride,
+                       wl.pad, wl.dilation, out=out, batch_mean=mean, batch_var=var)
+    assert_close("c4 unaligned out", out.cpu().numpy(), ref)
+    assert_close("c4 unaligned mean", mean.cpu().numpy(), ref_mean)
+    assert_close("c4 unaligned var", var.cpu().numpy(), ref_var)
+
+
 SWAP_MEDIUM = {
     # the swapped-sums path on ragged shapes and every supported channel count
     "c4_reduced": W.CONFIGS["c4"].with_(x_shape=(3, 3, 14, 13, 18)),

@@ -48,13 +48,27 @@ __host__ __device__ constexpr int class_steps(int cls) {
     return (CIN * class_taps(cls) + 3) / 4;
 }
 template <int CIN>
+__host__ __device__ constexpr int max_steps() {
+    int m = 0;
+    for (int c = 0; c < 8; ++c) m = class_steps<CIN>(c) > m ? class_steps<CIN>(c) : m;
+    return m;
+}
+template <int CIN>
+__host__ __device__ constexpr int first_step(int cls) {
+    int s = 0;
+    for (int c = 0; c < cls; ++c) s += class_steps<CIN>(c);
+    return s;
+}
+template <int CIN>
 __host__ __device__ constexpr int total_steps() {
     int s = 0;
     for (int c = 0; c < 8; ++c) s += class_steps<CIN>(c);
     return s;
 }
 
-template <int CIN>
+// VEC: S2 % 4 == 0 and x 16-byte aligned, so the input box is staged with
+// 16-byte loads
+template <int CIN, bool VEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CIN == 4 ? 3 : 4, 4))) void convT_bn_pool_mfma_kernel(
     const float* __restrict__ x, const float* __restrict__ w, float* __restrict__ y, double* __restrict__ ws,
     PoolGeom pg, int32_t nb1, int32_t nb2, int64_t boxes_per_sample, BnEval ev) {
@@ -72,35 +86,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CIN ==
     const int64_t cb1 = ((bx / nb2) % nb1) * B1;
     const int64_t cb0 = (bx / ((int64_t)nb2 * nb1)) * B0;
 
-    // stage inputs 2 cb + [0, R) per dim of every input channel, zero outside
-    // x: all of a thread's loads are issued before its first LDS write, so
-    // their latencies overlap
-    {
-        constexpr int kIter = (CIN * kRegion + kThreads - 1) / kThreads;
-        const int S0 = (int)g.S[0], S1 = (int)g.S[1], S2 = (int)g.S[2];
-        const float* xn = x + n * CIN * (int64_t)S0 * S1 * S2;
-        const int j0 = 2 * (int)cb0, j1 = 2 * (int)cb1, j2 = 2 * (int)cb2;
-        float v[kIter];
-#pragma unroll
-        for (int q = 0; q < kIter; ++q) {
-            const int e = q * kThreads + (int)threadIdx.x;
-            const int ic = e / kRegion;
-            int rem = e - ic * kRegion;
-            const int a = rem / (R1 * R2);
-            rem -= a * (R1 * R2);
-            const int b = rem / R2;
-            const int c = rem - b * R2;
-            const int i0 = j0 + a, i1 = j1 + b, i2 = j2 + c;
-            const bool in = e < CIN * kRegion && i0 < S0 && i1 < S1 && i2 < S2;
-            v[q] = in ? xn[(int64_t)ic * S0 * S1 * S2 + (i0 * S1 + i1) * S2 + i2] : 0.f;
-        }
-#pragma unroll
-        for (int q = 0; q < kIter; ++q) {
-            const int e = q * kThreads + (int)threadIdx.x;
-            if (e < CIN * kRegion) xs[e] = v[q];
-        }
-    }
-
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int m = lane & 15;   // A row (voxel) of this lane, and its B / D column (output channel)
@@ -111,6 +96,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CIN ==
     const int am_cell = m >> 3, ae0 = (m >> 2) & 1, ae1 = (m >> 1) & 1, ae2 = m & 1;
 
     // per class and K step: this lane's A offset in xs (tile 0) and B weight
+    // (loaded before the input box, so that the two sets of loads overlap)
     int aoff[total_steps<CIN>()];
     float bw[total_steps<CIN>()];
     {
@@ -132,10 +118,92 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CIN ==
                 const int d0 = (r0 + 2 * ae0 + 1 - k0) >> 1, d1 = (r1 + 2 * ae1 + 1 - k1) >> 1,
                           d2 = (r2 + 2 * ae2 + 1 - k2) >> 1;
                 aoff[q] = ((ic * R0 + 2 * wv + d0) * R1 + d1) * R2 + 2 * am_cell + d2;
-                bw[q] = (kv && oc_ok) ? w[((ic * g.Cout + oc) * 3 + k0) * 9 + k1 * 3 + k2] : 0.f;
+                // unconditional load (channel clamped into w), zero selected after it
+                const int ocl = oc_ok ? oc : 0;
+                bw[q] = w[((ic * g.Cout + ocl) * 3 + k0) * 9 + k1 * 3 + k2];
+                bw[q] = (kv && oc_ok) ? bw[q] : 0.f;
             }
         }
     }
+    // stage inputs 2 cb + [0, R) per dim of every input channel, zero outside
+    // x.  The loads are unconditional, from addresses clamped into x, and the
+    // zero padding is applied when the registers are written to LDS: a
+    // conditional load would be a branch, and the compiler waits for every
+    // earlier load before one (their destination registers get reused), which
+    // serialises the whole staging.  All of a thread's loads are issued before
+    // its first LDS write, so their latencies overlap.
+    {
+        const int S0 = (int)g.S[0], S1 = (int)g.S[1], S2 = (int)g.S[2];
+        const float* xn = x + n * CIN * (int64_t)S0 * S1 * S2;
+        const int j0 = 2 * (int)cb0, j1 = 2 * (int)cb1, j2 = 2 * (int)cb2;
+        if constexpr (VEC) {
+            // A staged row holds R2 = 17 inputs along S2 from j2, a multiple
+            // of 16: five aligned 16-byte chunks, of which the last one
+            // contributes its first element.  With S2 % 4 == 0 a chunk lies
+            // wholly inside or wholly outside the row.
+            constexpr int kChunks = (R2 + 3) / 4;
+            constexpr int kItems = CIN * R0 * R1 * kChunks;
+            constexpr int kIter = (kItems + kThreads - 1) / kThreads;
+            static_assert(kIter <= 64, "one mask bit per staging load");
+            f32x4 v[kIter];
+            uint64_t inside = 0;
+#pragma unroll
+            for (int q = 0; q < kIter; ++q) {
+                const int e = q * kThreads + (int)threadIdx.x;
+                const int ec = e < kItems ? e : kItems - 1;
+                const int row = ec / kChunks, ch = ec - row * kChunks;
+                const int ic = row / (R0 * R1), r = row - ic * (R0 * R1);
+                const int a = r / R1, b = r - a * R1;
+                const int i0 = j0 + a, i1 = j1 + b, i2 = j2 + 4 * ch;
+                inside |= (uint64_t)(i0 < S0 && i1 < S1 && i2 < S2) << q;
+                const int k0 = i0 < S0 ? i0 : S0 - 1, k1 = i1 < S1 ? i1 : S1 - 1, k2 = i2 < S2 ? i2 : S2 - 4;
+                v[q] = *reinterpret_cast<const f32x4*>(xn + (int64_t)ic * S0 * S1 * S2 + (k0 * S1 + k1) * S2 + k2);
+            }
+#pragma unroll
+            for (int q = 0; q < kIter; ++q) {
+                const int e = q * kThreads + (int)threadIdx.x;
+                if (e < kItems) {
+                    const int row = e / kChunks, ch = e - row * kChunks;
+                    float* dst = xs + row * R2 + 4 * ch;  // row = (ic R0 + a) R1 + b
+                    const bool ok = (inside >> q) & 1;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (4 * ch + u < R2) dst[u] = ok ? v[q][u] : 0.f;
+                }
+            }
+        } else {
+            constexpr int kIter = (CIN * kRegion + kThreads - 1) / kThreads;
+            static_assert(kIter <= 64, "one mask bit per staging load");
+            float v[kIter];
+            uint64_t inside = 0;
+#pragma unroll
+            for (int q = 0; q < kIter; ++q) {
+                const int e = q * kThreads + (int)threadIdx.x;
+                const int ec = e < CIN * kRegion ? e : CIN * kRegion - 1;
+                const int ic = ec / kRegion;
+                int rem = ec - ic * kRegion;
+                const int a = rem / (R1 * R2);
+                rem -= a * (R1 * R2);
+                const int b = rem / R2;
+                const int c = rem - b * R2;
+                const int i0 = j0 + a, i1 = j1 + b, i2 = j2 + c;
+                inside |= (uint64_t)(i0 < S0 && i1 < S1 && i2 < S2) << q;
+                const int k0 = i0 < S0 ? i0 : S0 - 1, k1 = i1 < S1 ? i1 : S1 - 1, k2 = i2 < S2 ? i2 : S2 - 1;
+                v[q] = xn[(int64_t)ic * S0 * S1 * S2 + (k0 * S1 + k1) * S2 + k2];
+            }
+#pragma unroll
+            for (int q = 0; q < kIter; ++q) {
+                const int e = q * kThreads + (int)threadIdx.x;
+                if (e < CIN * kRegion) xs[e] = (inside >> q) & 1 ? v[q] : 0.f;
+            }
+        }
+    }
+
+    // Wait here for the weight loads: otherwise the first tile that uses
+    // them waits, and since any tile may be skipped, so does every later
+    // tile, and that wait also drains the earlier tiles' output stores
+    // (loads and stores share one in-order counter on this chip).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();  // xs staged
 
     const int64_t c0 = cb0 + wv;                        // this wave's cell plane
@@ -154,59 +222,71 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CIN ==
         const int b1 = (int)cb1, b2 = (int)cb2 + dcell;
         const bool row_ok = oc_ok && c0 < pg.P[0];
         float* yl = y + ((n * g.Cout + oc) * pg.P[0] + c0) * (int64_t)P1 * P2;  // this lane's pooled plane
-        // fully unrolled over the tiles, so that every A read is this lane's
-        // offset plus an immediate
+        // The tiles of a box row share one A offset per K step: each row
+        // adds its offset to them once, and the row's four tiles read at
+        // this offset plus an immediate.  A loop over the rows (not unrolled)
+        // keeps the kernel small enough for the instruction cache.
+#pragma unroll 1
+        for (int jr = 0; jr < B1; ++jr) {
+            const int c1 = b1 + jr;
+            if (c1 >= C1) break;  // wave-uniform: the rows below lie past the output
+            const int lim1 = (int)g.O[1] - 4 * c1;
+            const float* xr = xs + 2 * jr * R2;
+            int arow[total_steps<CIN>()];
 #pragma unroll
-        for (int j = 0; j < kTiles; ++j) {
-            const int c1 = b1 + (j >> 2);
-            const int c2a = (int)cb2 + 2 * (j & 3);  // first cell of the tile
-            if (c1 >= C1 || c2a >= C2) continue;     // wave-uniform: the tile lies past the output
-            const int c2 = b2 + 2 * (j & 3);         // this lane's D cell
-            const float* xt = xs + 2 * (j >> 2) * R2 + 4 * (j & 3);
-            // the 8 classes are independent accumulation chains
-            f32x4 acc[8];
-            {
-                int q = 0;
+            for (int q = 0; q < total_steps<CIN>(); ++q) arow[q] = aoff[q] + 2 * jr * R2;
 #pragma unroll
-                for (int cls = 0; cls < 8; ++cls) {
-                    acc[cls] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int jc = 0; jc < 4; ++jc) {
+                const int c2a = (int)cb2 + 2 * jc;  // first cell of the tile
+                if (c2a >= C2) break;               // wave-uniform: the tile lies past the output
+                const int c2 = b2 + 2 * jc;         // this lane's D cell
+                const float* xt = xs + 4 * jc;
+                // the 8 classes are independent accumulation chains
+                f32x4 acc[8];
+                {
+                    int q = 0;
 #pragma unroll
-                    for (int s = 0; s < class_steps<CIN>(cls); ++s, ++q)
-                        acc[cls] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[aoff[q]], bw[q], acc[cls], 0, 0, 0);
-                }
-            }
-            // two partial sums each, to halve the dependent chains
-            float win[2] = {0.f, 0.f}, s2[2] = {0.f, 0.f};
-            const int lim1 = (int)g.O[1] - 4 * c1, lim2 = (int)g.O[2] - 4 * c2;
-            // every voxel of the tile is inside the output (wave-uniform)
-            if (lim0 >= 4 && lim1 >= 4 && (int)g.O[2] - 4 * (c2a + 1) >= 4) {
+                    for (int cls = 0; cls < 8; ++cls) {
+                        acc[cls] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int cls = 0; cls < 8; ++cls)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        win[i & 1] += acc[cls][i];
-                        s2[i & 1] = fmaf(acc[cls][i], acc[cls][i], s2[i & 1]);
-                    }
-            } else {
-#pragma unroll
-                for (int cls = 0; cls < 8; ++cls) {
-                    const int r0 = (cls >> 2) & 1, r1 = (cls >> 1) & 1, r2 = cls & 1;
-                    const bool in0 = r0 + 2 * de0 < lim0;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool in = in0 && r1 + 2 * (i >> 1) < lim1 && r2 + 2 * (i & 1) < lim2;
-                        const float v = in ? acc[cls][i] : 0.f;
-                        win[i & 1] += v;
-                        s2[i & 1] = fmaf(v, v, s2[i & 1]);
+                        for (int s = 0; s < class_steps<CIN>(cls); ++s, ++q)
+                            acc[cls] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[arow[q]], bw[q], acc[cls], 0, 0, 0);
                     }
                 }
-            }
-            sq += (double)(s2[0] + s2[1]);
-            float wsum = win[0] + win[1];
-            wsum += __shfl_xor(wsum, 16, 64);  // the other half (e0) of the cell's window
-            if (de0 == 0) {
-                st += (double)wsum;
-                if (row_ok && c1 < P1 && c2 < P2) yl[c1 * P2 + c2] = fmaf(wsum, sc, sh);
+                (void)xr;
+                // two partial sums each, to halve the dependent chains
+                float win[2] = {0.f, 0.f}, s2[2] = {0.f, 0.f};
+                const int lim2 = (int)g.O[2] - 4 * c2;
+                // every voxel of the tile is inside the output (wave-uniform)
+                if (lim0 >= 4 && lim1 >= 4 && (int)g.O[2] - 4 * (c2a + 1) >= 4) {
+#pragma unroll
+                    for (int cls = 0; cls < 8; ++cls)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            win[i & 1] += acc[cls][i];
+                            s2[i & 1] = fmaf(acc[cls][i], acc[cls][i], s2[i & 1]);
+                        }
+                } else {
+#pragma unroll
+                    for (int cls = 0; cls < 8; ++cls) {
+                        const int r0 = (cls >> 2) & 1, r1 = (cls >> 1) & 1, r2 = cls & 1;
+                        const bool in0 = r0 + 2 * de0 < lim0;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const bool in = in0 && r1 + 2 * (i >> 1) < lim1 && r2 + 2 * (i & 1) < lim2;
+                            const float v = in ? acc[cls][i] : 0.f;
+                            win[i & 1] += v;
+                            s2[i & 1] = fmaf(v, v, s2[i & 1]);
+                        }
+                    }
+                }
+                sq += (double)(s2[0] + s2[1]);
+                float wsum = win[0] + win[1];
+                wsum += __shfl_xor(wsum, 16, 64);  // the other half (e0) of the cell's window
+                if (de0 == 0) {
+                    st += (double)wsum;
+                    if (row_ok && c1 < P1 && c2 < P2) yl[c1 * P2 + c2] = fmaf(wsum, sc, sh);
+                }
             }
         }
     }
@@ -264,11 +344,21 @@ hipError_t launch_convT_bn_pool_phase1_mfma(const float* x, const float* w, floa
     if (blocks > 0x7fffffff || nb1 > 0x7fffffff || nb2 > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks), block(kThreads);
     const int32_t b1 = (int32_t)nb1, b2 = (int32_t)nb2;
-    switch (pg.g.Cin) {
-        case 1: hipLaunchKernelGGL(convT_bn_pool_mfma_kernel<1>, grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
-        case 2: hipLaunchKernelGGL(convT_bn_pool_mfma_kernel<2>, grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
-        case 3: hipLaunchKernelGGL(convT_bn_pool_mfma_kernel<3>, grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
-        default: hipLaunchKernelGGL(convT_bn_pool_mfma_kernel<4>, grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
+    const bool vec = pg.g.S[2] % 4 == 0 && ((uintptr_t)x & 15u) == 0;
+    if (vec) {
+        switch (pg.g.Cin) {
+            case 1: hipLaunchKernelGGL((convT_bn_pool_mfma_kernel<1, true>), grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
+            case 2: hipLaunchKernelGGL((convT_bn_pool_mfma_kernel<2, true>), grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
+            case 3: hipLaunchKernelGGL((convT_bn_pool_mfma_kernel<3, true>), grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
+            default: hipLaunchKernelGGL((convT_bn_pool_mfma_kernel<4, true>), grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
+        }
+    } else {
+        switch (pg.g.Cin) {
+            case 1: hipLaunchKernelGGL((convT_bn_pool_mfma_kernel<1, false>), grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
+            case 2: hipLaunchKernelGGL((convT_bn_pool_mfma_kernel<2, false>), grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
+            case 3: hipLaunchKernelGGL((convT_bn_pool_mfma_kernel<3, false>), grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
+            default: hipLaunchKernelGGL((convT_bn_pool_mfma_kernel<4, false>), grid, block, 0, st, x, w, y, ws, pg, b1, b2, bps, ev); break;
+        }
     }
     return hipGetLastError();
 }
