@@ -310,9 +310,23 @@ def test_c2_full_size_sampled():
     got = y.view(-1)[torch.from_numpy(flat).cuda()].cpu().numpy()
     ref = O.conv3d_at(inp.x, inp.w, flat, inp.b, wl.stride, wl.pad, wl.dilation, wl.groups)
     assert_close("c2 sampled", got, ref)
+    # the first and the last image in full (both ends of the workgroup order)
+    for n in (0, wl.x_shape[0] - 1):
+        ref_n = O.conv3d(np.ascontiguousarray(inp.x[n:n + 1]), inp.w, inp.b, wl.stride, wl.pad, wl.dilation,
+                         wl.groups)
+        assert_close(f"c2 image {n}", y[n:n + 1].cpu().numpy(), ref_n)
     # repeat and compare bit for bit
     y2 = run_gpu(wl, inp)
     assert torch.equal(y, y2)
+
+
+def test_c3_full_size_every_element():
+    """The whole 16x64x33x65x65 output against the oracle's scatter definition."""
+    wl = W.CONFIGS["c3"]
+    inp = W.make_inputs(wl)
+    y = run_gpu(wl, inp)
+    torch.cuda.synchronize()
+    assert_close("c3 full", y.cpu().numpy(), O.run_workload(wl, inp))
 
 
 def test_c3_full_size_sampled_and_checkerboard():
@@ -356,6 +370,32 @@ def test_c4_full_size(v):
         # repeat (the workspace is reused) and compare bit for bit
         y2 = run_gpu(wl, inp)
         assert torch.equal(y, y2)
+    finally:
+        B.set_variant(old)
+
+
+@pytest.mark.parametrize("dist", ["unit", "offset4"])
+@pytest.mark.parametrize("v", [0, 5, 3], ids=["matrix_cores", "per_cell", "swapped_sums"])
+def test_c4_full_size_offset_inputs(v, dist):
+    """The module at full size with inputs whose mean is far from zero: U[0,1)
+    (the pages' torch.rand) and 4 + U[-1,1].  The batch variance is then a
+    difference of large sums, the case that exposes cancellation."""
+    wl = W.CONFIGS["c4"]
+    inp = W.make_inputs(wl, x_dist=dist)
+    old = B.set_variant(v)
+    try:
+        print(f"[c4 {dist} v{v}]", flush=True)
+        check_full(wl, inp, f"c4 {dist} v{v}")
+    finally:
+        B.set_variant(old)
+
+
+@pytest.mark.parametrize("dist", ["unit", "offset4"])
+def test_c4_generic_offset_inputs(dist):
+    wl = W.CONFIGS["c4"].with_(x_shape=(3, 3, 14, 13, 18))
+    old = B.set_variant(1)
+    try:
+        check_full(wl, W.make_inputs(wl, x_dist=dist), f"c4 generic {dist}")
     finally:
         B.set_variant(old)
 
@@ -420,6 +460,16 @@ def test_c4_swapped_sums_medium(name):
         check_full(wl, W.make_inputs(wl), name)
     finally:
         B.set_variant(old)
+
+
+def test_c5_full_size_every_element():
+    """All 4x1x16x64x64 outputs against the oracle's module (conv, max-pool,
+    two-pass logsumexp, ReLU in float64)."""
+    wl = W.CONFIGS["c5"]
+    inp = W.make_inputs(wl)
+    y = run_gpu(wl, inp)
+    torch.cuda.synchronize()
+    assert_close("c5 full", y.cpu().numpy(), O.run_workload(wl, inp))
 
 
 def test_c5_full_size_sampled():
@@ -499,6 +549,30 @@ def test_bn_running_statistics_update(name, bn_variant):
     erm, erv = O.bn_running_update(rm0, rv0, mean, var, count, 0.1)
     assert_close(f"running mean {name}", rm.cpu().numpy(), erm)
     assert_close(f"running var {name}", rv.cpu().numpy(), erv)
+
+
+@pytest.mark.parametrize("dist", ["unit", "offset4"])
+def test_bn_eval_and_running_update_offset_inputs(dist, bn_variant):
+    """Eval mode and the running-statistics update on inputs with a large mean."""
+    wl = BN_EVAL["c4_reduced"]
+    inp = W.make_inputs(wl, x_dist=dist)
+    rm0, rv0 = W.make_running_stats(wl.cout, 29)
+    y = _bn_eval_gpu(wl, inp, rm0, rv0)
+    torch.cuda.synchronize()
+    ref = O.convT_bn_eval_avgpool(inp.x, inp.w, inp.b, inp.gamma, inp.beta, rm0, rv0, wl.eps, wl.pool, wl.stride,
+                                  wl.pad, wl.dilation, wl.output_pad, wl.groups)
+    assert_close(f"bn eval {dist}", y.cpu().numpy(), ref)
+    rm, rv = dev(rm0), dev(rv0)
+    kw = dict(stride=wl.stride, pad=wl.pad, dilation=wl.dilation, output_pad=wl.output_pad, groups=wl.groups)
+    y = B.convT_bn_avgpool(dev(inp.x), dev(inp.w), dev(inp.b), dev(inp.gamma), dev(inp.beta), wl.eps, wl.pool,
+                           out=poisoned(O.output_shape(wl)), running_mean=rm, running_var=rv, momentum=0.1, **kw)
+    torch.cuda.synchronize()
+    out, mean, var = O.run_workload(wl, inp)
+    assert_close(f"bn running out {dist}", y.cpu().numpy(), out)
+    cshape = O.convT_out_shape(wl.x_shape, wl.cout, wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad)
+    erm, erv = O.bn_running_update(rm0, rv0, mean, var, cshape[0] * cshape[2] * cshape[3] * cshape[4], 0.1)
+    assert_close(f"running mean {dist}", rm.cpu().numpy(), erm)
+    assert_close(f"running var {dist}", rv.cpu().numpy(), erv)
 
 
 # ----------------------------------------------------------- edge cases

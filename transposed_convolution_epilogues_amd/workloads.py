@@ -143,12 +143,19 @@ def make_inputs(wl: Workload, seed: Optional[int] = None,
                 x_dist: str = "uniform") -> Inputs:
     """Draw x, W, b, gamma, beta (in that order) for a workload.
 
-    ``x_dist`` may be ``"uniform"`` (U[-1,1], the default) or ``"ones"`` /
-    ``"zeros"`` for structured test inputs; the parameter draws are unchanged.
+    ``x_dist`` may be ``"uniform"`` (U[-1,1], the default), ``"unit"``
+    (U[0,1), the distribution of ``torch.rand`` that the pages' harness draws
+    inputs from), ``"offset4"`` (4 + U[-1,1], a mean well away from zero) or
+    ``"ones"`` / ``"zeros"`` for structured test inputs; the parameter draws
+    are unchanged.
     """
     rng = np.random.default_rng(wl.seed if seed is None else seed)
     if x_dist == "uniform":
         x = _uniform(rng, -1.0, 1.0, wl.x_shape)
+    elif x_dist == "unit":
+        x = _uniform(rng, 0.0, 1.0, wl.x_shape)
+    elif x_dist == "offset4":
+        x = (_uniform(rng, -1.0, 1.0, wl.x_shape).astype(np.float64) + 4.0).astype(np.float32)
     elif x_dist == "ones":
         x = np.ones(wl.x_shape, np.float32)
     elif x_dist == "zeros":
