@@ -1,9 +1,10 @@
 """Benchmark of the fused 3D conv / transposed-conv forward path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-the four full-size workloads back to back, each through its C-ABI entry point
-(inputs resident in HBM, outputs and workspace preallocated):
+the five workloads back to back, each through its C-ABI entry point (inputs
+resident in HBM, outputs and workspace preallocated):
 
+  c1  conv3d_fwd              Conv3d 4->8 k3 p1 with bias, x[1,4,8,8,8] (launch-latency bound)
   c2  conv3d_fwd              Conv3d (3,3,1) kernel, depth-last x[16,3,256,256,10] -> [16,64,254,254,10]
   c3  conv_transpose3d_fwd    ConvTranspose3d 32->64 k3 s2 p1 d2, x[16,32,16,32,32] -> [16,64,33,65,65]
   c4  convT_bn_avgpool        ConvTranspose3d 3->16 k3 s2 p1 + BatchNorm3d (batch stats) + AvgPool3d(2) x2
@@ -32,10 +33,11 @@ if ROOT not in sys.path:
 
 FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 (MFMA and packed VALU)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
-BENCH_KEYS = ("c2", "c3", "c4", "c5")
+BENCH_KEYS = ("c1", "c2", "c3", "c4", "c5")
 # kernel that carries each workload (the roofline object names the dominant one)
 CSRC = "transposed_convolution_epilogues_amd/csrc/"
 KERNELS = {
+    "c1": ("conv3d_direct_kernel", [CSRC + "conv_direct.hip"]),
     "c2": ("conv_k1last_kernel", [CSRC + "conv_k1last.hip"]),
     "c3": ("conv333_store_kernel", [CSRC + "convT_sublattice.hip", CSRC + "conv333_mfma.h"]),
     "c4": ("convT_bn_pool_mfma_kernel", [CSRC + "convT_bn_pool_mfma.hip"]),
@@ -155,7 +157,7 @@ def main():
                                                                             wl.dilation, wl.groups, out=y))
         mac, xb, wb = work(wl, conv_shape)
         runs[key] = dict(wl=wl, fn=fn, mac=mac, bytes=xb + wb + 4 * math.prod(oshape), out_shape=oshape,
-                         inp=inp, ev=[])
+                         inp=inp, ev=[], y=y)
         print(f"[bench] {key}: {wl.description}; out {oshape}; MAC {mac:,}", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
@@ -217,9 +219,12 @@ def main():
     roofline = dict(kernel=kname, workload=dom, bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
                     frac=round(achieved / peak, 4), traffic=traffic)
 
+    hw = hardware(torch)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(runs, args.cpu_seconds)
+        cpu, errs = cpu_baseline(runs, args.cpu_seconds)
+        for key, e in errs.items():
+            per[key].update(e)
 
     line = {
         "metric": "effective TFLOP/s (2*MACs/time) and % of MI355X fp32 peak, per config",
@@ -242,11 +247,12 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "hw": hw,
     }
     print(json.dumps(line), flush=True)
 
 
-def probe_mfma(torch):
+def measure_probe(torch, reps=10):
     """Achievable fp32 MFMA throughput on this GPU: back-to-back independent
     v_mfma_f32_32x32x2f32 chains, two waves per SIMD on every CU."""
     from transposed_convolution_epilogues_amd import binding as B
@@ -256,7 +262,7 @@ def probe_mfma(torch):
         flop = B.probe_mfma_f32(iters, out)
     torch.cuda.synchronize()
     ts = []
-    for _ in range(10):
+    for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         B.probe_mfma_f32(iters, out)
@@ -265,9 +271,46 @@ def probe_mfma(torch):
         ts.append(e0.elapsed_time(e1))
     ts.sort()
     med = ts[len(ts) // 2]
-    print(json.dumps({"probe": "mfma_f32_32x32x2", "flop": flop, "ms_median": round(med, 4),
-                      "tflops": round(flop / (med * 1e-3) / 1e12, 2), "peak": FP32_PEAK_TFLOPS,
-                      "frac_of_peak": round(flop / (med * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4)}), flush=True)
+    return {"probe": "mfma_f32_32x32x2", "flop": flop, "ms_median": round(med, 4),
+            "tflops": round(flop / (med * 1e-3) / 1e12, 2), "peak": FP32_PEAK_TFLOPS,
+            "frac_of_peak": round(flop / (med * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4)}
+
+
+def probe_mfma(torch):
+    print(json.dumps(measure_probe(torch)), flush=True)
+
+
+def gpu_clocks():
+    """Current and maximum shader clock from rocm-smi (None where it is not available)."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"sclk clock level:\s*\d+:\s*\(?(\d+)\s*Mhz", txt, re.I)
+    return int(m.group(1)) if m else None
+
+
+def hardware(torch):
+    """What the line's peaks are checked against: the device, its clocks and
+    the measured matrix-core throughput, taken after the timed steps."""
+    prop = torch.cuda.get_device_properties(0)
+    hw = {"device": prop.name, "gcn_arch": getattr(prop, "gcnArchName", None),
+          "compute_units": prop.multi_processor_count,
+          "max_clock_mhz": None, "sclk_mhz_after_run": gpu_clocks()}
+    try:
+        from transposed_convolution_epilogues_amd import binding as B  # noqa: F401
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        rate = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate = 5 (kHz)
+        if hip.hipDeviceGetAttribute(ctypes.byref(rate), 5, 0) == 0:
+            hw["max_clock_mhz"] = rate.value // 1000
+    except OSError:
+        pass
+    hw["mfma_probe"] = measure_probe(torch, reps=5)
+    return hw
 
 
 def calibrate_copy(torch):
@@ -377,60 +420,74 @@ def widen(torch, args):
                       "steps": args.steps, "widen": out}), flush=True)
 
 
+def errors(got, ref):
+    """max |gpu - oracle|, the max relative error over outputs with |oracle| >= 1e-3,
+    and the largest error as a fraction of the parity bar 1e-4 + 1e-4 |oracle|."""
+    got = np.asarray(got, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    err = np.abs(got - ref)
+    big = np.abs(ref) >= 1e-3
+    return {"max_abs_err": float(err.max()),
+            "max_rel_err": float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0,
+            "err_over_tol": float((err / (1e-4 + 1e-4 * np.abs(ref))).max()),
+            "checked": int(err.size)}
+
+
 def cpu_baseline(runs, seconds_per_workload):
     """The CPU oracle, timed on a bounded sample of each workload and scaled to the
-    whole workload; reported in the same effective TFLOP/s as the GPU value."""
+    whole workload; reported in the same effective TFLOP/s as the GPU value.  The
+    same oracle outputs are compared with the GPU's outputs of the last timed
+    step (errors per workload)."""
     import oracle as O
 
     rng = np.random.default_rng(0)
     total_flop = 0.0
     total_s = 0.0
     parts = []
+    errs = {}
     for key, r in runs.items():
         wl, inp = r["wl"], r["inp"]
         kw = dict(stride=wl.stride, pad=wl.pad, dilation=wl.dilation, groups=wl.groups)
         full_units = math.prod(r["out_shape"])
-        if wl.op == "convT_bn_avgpool":
-            # the module needs whole-batch statistics: sample = a leading sub-batch
-            nb = 1
-            while True:
-                sub = wl.with_(x_shape=(nb,) + wl.x_shape[1:])
-                t0 = time.perf_counter()
-                O.convT_bn_avgpool(np.ascontiguousarray(inp.x[:nb]), inp.w, inp.b, inp.gamma, inp.beta, wl.eps,
-                                   wl.pool, **dict(kw, output_pad=wl.output_pad))
-                dt = time.perf_counter() - t0
-                if dt > seconds_per_workload / 4 or nb >= wl.x_shape[0]:
-                    break
-                nb *= 2
-            frac = nb / wl.x_shape[0]
-            desc = f"{key}: batch {nb} of {wl.x_shape[0]}"
+        y = r["y"].detach().cpu().numpy()
+        if wl.op == "convT_bn_avgpool" or full_units <= 65536:
+            # the whole module (BatchNorm needs whole-batch statistics; c1 is tiny)
+            t0 = time.perf_counter()
+            ref = O.run_workload(wl, inp)
+            dt = time.perf_counter() - t0
+            ref = ref[0] if isinstance(ref, tuple) else ref
+            errs[key] = errors(y, ref)
+            frac = 1.0
+            desc = f"{key}: whole workload"
         else:
             n = 256
             while True:
                 flat = rng.integers(0, full_units, n)
                 t0 = time.perf_counter()
                 if wl.op == "conv3d":
-                    O.conv3d_at(inp.x, inp.w, flat, inp.b, **kw)
+                    ref = O.conv3d_at(inp.x, inp.w, flat, inp.b, **kw)
                 elif wl.op == "conv_transpose3d":
-                    O.conv_transpose3d_at(inp.x, inp.w, flat, inp.b, output_pad=wl.output_pad, **kw)
+                    ref = O.conv_transpose3d_at(inp.x, inp.w, flat, inp.b, output_pad=wl.output_pad, **kw)
                 else:
-                    O.conv_maxpool_lse_relu_at(inp.x, inp.w, inp.b, flat, wl.pool, **kw)
+                    ref = O.conv_maxpool_lse_relu_at(inp.x, inp.w, inp.b, flat, wl.pool, **kw)
                 dt = time.perf_counter() - t0
                 if dt > seconds_per_workload / 4 or n >= full_units:
                     break
                 n *= 4
+            errs[key] = errors(y.reshape(-1)[flat], ref)
             frac = n / full_units
             desc = f"{key}: {n} random outputs of {full_units}"
         t_full = dt / frac
         total_s += t_full
         total_flop += 2.0 * r["mac"]
         parts.append(f"{desc} in {dt:.2f}s")
-        print(f"[bench] cpu oracle {desc}: {dt:.2f}s -> {t_full:.1f}s for the whole workload", file=sys.stderr,
-              flush=True)
-    return {"value": round(total_flop / total_s / 1e12, 6), "unit": "TFLOP/s", "cores": O.num_threads(),
-            "kind": "oracle",
-            "sample": "plain-loop float64 oracle timed on bounded samples, scaled to the whole step: " +
-                      "; ".join(parts)}
+        print(f"[bench] cpu oracle {desc}: {dt:.2f}s -> {t_full:.1f}s for the whole workload; {errs[key]}",
+              file=sys.stderr, flush=True)
+    cpu = {"value": round(total_flop / total_s / 1e12, 6), "unit": "TFLOP/s", "cores": O.num_threads(),
+           "kind": "oracle",
+           "sample": "plain-loop float64 oracle timed on bounded samples, scaled to the whole step: " +
+                     "; ".join(parts)}
+    return cpu, errs
 
 
 if __name__ == "__main__":

@@ -359,7 +359,8 @@ def test_variant_override_is_per_thread():
 ALGO_CASES = [
     # (op, x_shape, cout, kernel, stride, pad, dilation, output_pad, groups, variant, expected)
     ("conv3d", (16, 3, 256, 256, 10), 64, (3, 3, 1), 1, 0, 1, 0, 1, 0, "k1last"),       # c2
-    ("conv3d", (1, 4, 8, 8, 8), 8, 3, 1, 1, 1, 0, 1, 0, "mfma333"),                     # c1
+    ("conv3d", (1, 4, 8, 8, 8), 8, 3, 1, 1, 1, 0, 1, 0, "direct"),                      # c1: below 2^19 MAC
+    ("conv3d", (1, 4, 8, 8, 16), 8, 3, 1, 1, 1, 0, 1, 0, "mfma333"),                    # 884,736 MAC
     ("conv3d", (1, 2, 8, 8, 8), 8, 3, 1, 1, 1, 0, 1, 0, "direct"),                      # too few channels
     ("conv3d", (1, 8, 8, 8, 8), 8, 3, 2, 1, 1, 0, 1, 0, "direct"),                      # strided
     ("conv3d", (16, 3, 256, 256, 10), 64, (3, 3, 1), 1, 0, 1, 0, 1, 1, "direct"),       # forced generic

@@ -4,7 +4,7 @@ bench.py's effective TFLOP/s is 2 * MAC / time with MAC the algorithmic work:
 the dense GEMM count N * Cout * prod(O) * Cin/groups * kvol for direct convs,
 and the valid-tap count N * Cout * Cin/groups * prod_j #{(i_j, k_j) landing
 inside the output} for transposed convs.  Here those counts are checked
-against closed forms worked out by hand for the four full-size workloads, so
+against closed forms worked out by hand for the five workloads, so
 a slip in the benchmark's accounting (a wrong output size, dense instead of
 valid taps, a dropped factor) cannot inflate or deflate the reported rate.
 """
@@ -18,6 +18,15 @@ def _conv_out(S, k, s, p, d):
 
 def _convT_out(S, k, s, p, d, op=0):
     return (S - 1) * s - 2 * p + d * (k - 1) + op + 1
+
+
+def test_c1_dense_gemm_count():
+    # x[1,4,8,8,8], kernel 3, padding 1: output 8^3 x 8 channels, 4 * 27 taps each (padding taps count)
+    wl = W.CONFIGS["c1"]
+    O = tuple(_conv_out(8, 3, 1, 1, 1) for _ in range(3))
+    assert O == (8, 8, 8)
+    mac, _, _ = bench.work(wl, (1, 8) + O)
+    assert mac == 8 * 512 * 4 * 27 == 442_368
 
 
 def test_c2_dense_gemm_count():

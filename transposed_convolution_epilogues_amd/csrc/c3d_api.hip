@@ -127,9 +127,19 @@ c3d_status scratch_on_device(int dev, void** out) {
 // compared with them; variants 3 and 4 select the second algorithms of the
 // ConvT -> BatchNorm -> AvgPool module (swapped sums) and of the transposed
 // conv (LDS scatter).
+//
+// A convolution below 2^19 MAC (the 4->8 channel, 8^3 layer: 442,368) takes
+// the one-thread-per-output kernel: the matrix-core engines' workgroup tiles
+// (4 x 4 x 32 voxels x 64 channels) would put it on a handful of CUs (that
+// layer: 4 workgroups, 31 us), the direct kernel spreads it over all of them.
+constexpr double kSmallConvMac = 524288.0;
+
 int conv3d_algo(const Geom& g) {
     const int v = t_variant;
     if (v == 1) return C3D_ALGO_DIRECT;
+    const double mac = (double)g.N * (double)g.Cout * (double)g.O[0] * (double)g.O[1] * (double)g.O[2] *
+                       (double)g.cin_g * g.k[0] * g.k[1] * g.k[2];
+    if (mac < kSmallConvMac) return C3D_ALGO_DIRECT;
     if (v != 2 && c3d::conv_k1last_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_K1LAST;
     if (c3d::conv3x3x3_mfma_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_MFMA333;
     return C3D_ALGO_DIRECT;
