@@ -26,6 +26,8 @@
 // The workgroup writes the pooled pre-normalisation means (or, in eval mode,
 // the final outputs) and one float64 (sum, sum of squares) pair per channel,
 // which phase 2 merges.
+#include <type_traits>
+
 #include "c3d_internal.h"
 
 namespace c3d {
@@ -65,6 +67,69 @@ __host__ __device__ constexpr int total_steps() {
     for (int c = 0; c < 8; ++c) s += class_steps<CIN>(c);
     return s;
 }
+
+// lanes l and l ^ 16 exchange a value (ds_swizzle in bit-mask mode: no lane
+// arithmetic, unlike a generic shuffle)
+__device__ __forceinline__ float swizzle_xor16(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+
+// The staged input box: every input channel, dim-0 row a and dim-1 row b.
+// load() issues the global loads into registers, store() writes them to LDS
+// with the zero padding.  VEC (S2 % 4 == 0, x 16-byte aligned): a staged row
+// of R2 = 17 inputs from j2, a multiple of 16, is five aligned 16-byte
+// chunks, of which the last contributes its first element; with S2 % 4 == 0
+// a chunk lies wholly inside or wholly outside the row.
+template <int CIN, bool VEC>
+struct StageBox {
+    static constexpr int B = 0;
+    static constexpr int NB = R1;
+    static constexpr int kW = VEC ? (R2 + 3) / 4 : R2;  // items per staged row
+    static constexpr int kItems = CIN * R0 * NB * kW;
+    static constexpr int kIter = (kItems + kThreads - 1) / kThreads;
+    static_assert(kIter <= 64, "one mask bit per staging load");
+    typedef typename std::conditional<VEC, f32x4, float>::type V;
+    V v[kIter];
+    uint64_t inside = 0;
+
+    __device__ __forceinline__ void load(const float* xn, int S0, int S1, int S2, int j0, int j1, int j2) {
+#pragma unroll
+        for (int q = 0; q < kIter; ++q) {
+            const int e = q * kThreads + (int)threadIdx.x;
+            const int ec = e < kItems ? e : kItems - 1;
+            const int row = ec / kW, c = ec - row * kW;
+            const int ic = row / (R0 * NB), r = row - ic * (R0 * NB);
+            const int a = r / NB, b = B + (r - a * NB);
+            const int i0 = j0 + a, i1 = j1 + b, i2 = j2 + (VEC ? 4 * c : c);
+            inside |= (uint64_t)(i0 < S0 && i1 < S1 && i2 < S2) << q;
+            const int k0 = i0 < S0 ? i0 : S0 - 1, k1 = i1 < S1 ? i1 : S1 - 1;
+            const int k2 = i2 < S2 ? i2 : S2 - (VEC ? 4 : 1);
+            const float* src = xn + (int64_t)ic * S0 * S1 * S2 + (k0 * S1 + k1) * S2 + k2;
+            if constexpr (VEC) v[q] = *reinterpret_cast<const f32x4*>(src);
+            else v[q] = *src;
+        }
+    }
+    __device__ __forceinline__ void store(float* xs) const {
+#pragma unroll
+        for (int q = 0; q < kIter; ++q) {
+            const int e = q * kThreads + (int)threadIdx.x;
+            if (e < kItems) {
+                const int row = e / kW, c = e - row * kW;
+                const int ic = row / (R0 * NB), r = row - ic * (R0 * NB);
+                const int a = r / NB, b = B + (r - a * NB);
+                const bool ok = (inside >> q) & 1;
+                if constexpr (VEC) {
+                    float* dst = xs + ((ic * R0 + a) * R1 + b) * R2 + 4 * c;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (4 * c + u < R2) dst[u] = ok ? v[q][u] : 0.f;
+                } else {
+                    xs[((ic * R0 + a) * R1 + b) * R2 + c] = ok ? v[q] : 0.f;
+                }
+            }
+        }
+    }
+};
 
 // VEC: S2 % 4 == 0 and x 16-byte aligned, so the input box is staged with
 // 16-byte loads
@@ -125,86 +190,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CIN ==
             }
         }
     }
-    // stage inputs 2 cb + [0, R) per dim of every input channel, zero outside
+    // Stage inputs 2 cb + [0, R) per dim of every input channel, zero outside
     // x.  The loads are unconditional, from addresses clamped into x, and the
     // zero padding is applied when the registers are written to LDS: a
     // conditional load would be a branch, and the compiler waits for every
     // earlier load before one (their destination registers get reused), which
-    // serialises the whole staging.  All of a thread's loads are issued before
-    // its first LDS write, so their latencies overlap.
-    {
-        const int S0 = (int)g.S[0], S1 = (int)g.S[1], S2 = (int)g.S[2];
-        const float* xn = x + n * CIN * (int64_t)S0 * S1 * S2;
-        const int j0 = 2 * (int)cb0, j1 = 2 * (int)cb1, j2 = 2 * (int)cb2;
-        if constexpr (VEC) {
-            // A staged row holds R2 = 17 inputs along S2 from j2, a multiple
-            // of 16: five aligned 16-byte chunks, of which the last one
-            // contributes its first element.  With S2 % 4 == 0 a chunk lies
-            // wholly inside or wholly outside the row.
-            constexpr int kChunks = (R2 + 3) / 4;
-            constexpr int kItems = CIN * R0 * R1 * kChunks;
-            constexpr int kIter = (kItems + kThreads - 1) / kThreads;
-            static_assert(kIter <= 64, "one mask bit per staging load");
-            f32x4 v[kIter];
-            uint64_t inside = 0;
-#pragma unroll
-            for (int q = 0; q < kIter; ++q) {
-                const int e = q * kThreads + (int)threadIdx.x;
-                const int ec = e < kItems ? e : kItems - 1;
-                const int row = ec / kChunks, ch = ec - row * kChunks;
-                const int ic = row / (R0 * R1), r = row - ic * (R0 * R1);
-                const int a = r / R1, b = r - a * R1;
-                const int i0 = j0 + a, i1 = j1 + b, i2 = j2 + 4 * ch;
-                inside |= (uint64_t)(i0 < S0 && i1 < S1 && i2 < S2) << q;
-                const int k0 = i0 < S0 ? i0 : S0 - 1, k1 = i1 < S1 ? i1 : S1 - 1, k2 = i2 < S2 ? i2 : S2 - 4;
-                v[q] = *reinterpret_cast<const f32x4*>(xn + (int64_t)ic * S0 * S1 * S2 + (k0 * S1 + k1) * S2 + k2);
-            }
-#pragma unroll
-            for (int q = 0; q < kIter; ++q) {
-                const int e = q * kThreads + (int)threadIdx.x;
-                if (e < kItems) {
-                    const int row = e / kChunks, ch = e - row * kChunks;
-                    float* dst = xs + row * R2 + 4 * ch;  // row = (ic R0 + a) R1 + b
-                    const bool ok = (inside >> q) & 1;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (4 * ch + u < R2) dst[u] = ok ? v[q][u] : 0.f;
-                }
-            }
-        } else {
-            constexpr int kIter = (CIN * kRegion + kThreads - 1) / kThreads;
-            static_assert(kIter <= 64, "one mask bit per staging load");
-            float v[kIter];
-            uint64_t inside = 0;
-#pragma unroll
-            for (int q = 0; q < kIter; ++q) {
-                const int e = q * kThreads + (int)threadIdx.x;
-                const int ec = e < CIN * kRegion ? e : CIN * kRegion - 1;
-                const int ic = ec / kRegion;
-                int rem = ec - ic * kRegion;
-                const int a = rem / (R1 * R2);
-                rem -= a * (R1 * R2);
-                const int b = rem / R2;
-                const int c = rem - b * R2;
-                const int i0 = j0 + a, i1 = j1 + b, i2 = j2 + c;
-                inside |= (uint64_t)(i0 < S0 && i1 < S1 && i2 < S2) << q;
-                const int k0 = i0 < S0 ? i0 : S0 - 1, k1 = i1 < S1 ? i1 : S1 - 1, k2 = i2 < S2 ? i2 : S2 - 1;
-                v[q] = xn[(int64_t)ic * S0 * S1 * S2 + (k0 * S1 + k1) * S2 + k2];
-            }
-#pragma unroll
-            for (int q = 0; q < kIter; ++q) {
-                const int e = q * kThreads + (int)threadIdx.x;
-                if (e < CIN * kRegion) xs[e] = (inside >> q) & 1 ? v[q] : 0.f;
-            }
-        }
-    }
-
-    // Wait here for the weight loads: otherwise the first tile that uses
-    // them waits, and since any tile may be skipped, so does every later
-    // tile, and that wait also drains the earlier tiles' output stores
-    // (loads and stores share one in-order counter on this chip).
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();  // xs staged
+    // serialises the staging.  All of a thread's loads are issued before its
+    // first LDS write, so their latencies overlap.  (Staging the box in two
+    // parts, so that the first tile rows start before the rest arrives, needs
+    // the second part's registers during those rows: 129 VGPRs for 3 input
+    // channels, past the 128 that four waves per SIMD allow.)
+    const int S0 = (int)g.S[0], S1 = (int)g.S[1], S2 = (int)g.S[2];
+    const float* xn = x + n * CIN * (int64_t)S0 * S1 * S2;
+    StageBox<CIN, VEC> box;
+    box.load(xn, S0, S1, S2, 2 * (int)cb0, 2 * (int)cb1, 2 * (int)cb2);
+    box.store(xs);
+    __syncthreads();  // input box staged
 
     const int64_t c0 = cb0 + wv;                        // this wave's cell plane
     const int dcell = kq >> 1, de0 = kq & 1;            // D rows: cell kq / 2 of the tile, e0 = kq % 2
@@ -215,26 +216,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CIN ==
         sc *= 1.f / 64.f;
     }
     double st = 0.0, sq = 0.0;
-    if (c0 < pg.C[0]) {
-        // 32-bit cell coordinates (the supported shapes keep every output index below 2^31)
-        const int C1 = (int)pg.C[1], C2 = (int)pg.C[2], P1 = (int)pg.P[1], P2 = (int)pg.P[2];
-        const int lim0 = (int)(g.O[0] - 4 * c0);  // o0 - 4 c0 of this plane's outputs stays below lim0
-        const int b1 = (int)cb1, b2 = (int)cb2 + dcell;
-        const bool row_ok = oc_ok && c0 < pg.P[0];
-        float* yl = y + ((n * g.Cout + oc) * pg.P[0] + c0) * (int64_t)P1 * P2;  // this lane's pooled plane
-        // The tiles of a box row share one A offset per K step: each row
-        // adds its offset to them once, and the row's four tiles read at
-        // this offset plus an immediate.  A loop over the rows (not unrolled)
-        // keeps the kernel small enough for the instruction cache.
+    const bool plane_ok = c0 < pg.C[0];  // wave-uniform
+    // 32-bit cell coordinates (the supported shapes keep every output index below 2^31)
+    const int C1 = (int)pg.C[1], C2 = (int)pg.C[2], P1 = (int)pg.P[1], P2 = (int)pg.P[2];
+    const int lim0 = (int)(g.O[0] - 4 * c0);  // o0 - 4 c0 of this plane's outputs stays below lim0
+    const int b1 = (int)cb1, b2 = (int)cb2 + dcell;
+    const bool row_ok = oc_ok && c0 < pg.P[0];
+    float* yl = y + ((n * g.Cout + oc) * pg.P[0] + c0) * (int64_t)P1 * P2;  // this lane's pooled plane
+
+    // Tile rows [jr0, jr1) of the box, starting at row 0.  The tiles of a
+    // row share one A offset per K step, which each row
+    // advances in place (aoff holds the current row's offsets), and the
+    // row's four tiles read at this offset plus an immediate.  A loop over
+    // the rows (not unrolled) keeps the kernel small for the instruction
+    // cache.
+    auto rows = [&](int jr0, int jr1) __attribute__((always_inline)) {
 #pragma unroll 1
-        for (int jr = 0; jr < B1; ++jr) {
+        for (int jr = jr0; jr < jr1; ++jr) {
             const int c1 = b1 + jr;
-            if (c1 >= C1) break;  // wave-uniform: the rows below lie past the output
+            if (c1 >= C1) break;  // wave-uniform: the rows below (and their offsets) are not needed
             const int lim1 = (int)g.O[1] - 4 * c1;
-            const float* xr = xs + 2 * jr * R2;
-            int arow[total_steps<CIN>()];
-#pragma unroll
-            for (int q = 0; q < total_steps<CIN>(); ++q) arow[q] = aoff[q] + 2 * jr * R2;
+            float stf = 0.f, sqf = 0.f;  // the row's sums, in float over its four tiles
 #pragma unroll
             for (int jc = 0; jc < 4; ++jc) {
                 const int c2a = (int)cb2 + 2 * jc;  // first cell of the tile
@@ -250,10 +252,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CIN ==
                         acc[cls] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int s = 0; s < class_steps<CIN>(cls); ++s, ++q)
-                            acc[cls] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[arow[q]], bw[q], acc[cls], 0, 0, 0);
+                            acc[cls] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[aoff[q]], bw[q], acc[cls], 0, 0, 0);
                     }
                 }
-                (void)xr;
                 // two partial sums each, to halve the dependent chains
                 float win[2] = {0.f, 0.f}, s2[2] = {0.f, 0.f};
                 const int lim2 = (int)g.O[2] - 4 * c2;
@@ -280,16 +281,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(CIN ==
                         }
                     }
                 }
-                sq += (double)(s2[0] + s2[1]);
+                sqf += s2[0] + s2[1];
                 float wsum = win[0] + win[1];
-                wsum += __shfl_xor(wsum, 16, 64);  // the other half (e0) of the cell's window
+                wsum += swizzle_xor16(wsum);  // the other half (e0) of the cell's window
                 if (de0 == 0) {
-                    st += (double)wsum;
+                    stf += wsum;
                     if (row_ok && c1 < P1 && c2 < P2) yl[c1 * P2 + c2] = fmaf(wsum, sc, sh);
                 }
             }
+            st += (double)stf;
+            sq += (double)sqf;
+#pragma unroll
+            for (int q = 0; q < total_steps<CIN>(); ++q) aoff[q] += 2 * R2;  // next tile row
         }
-    }
+    };
+    if (plane_ok) rows(0, B1);
     if (eval) return;  // workgroup-uniform; no barrier follows in eval mode
 
     // per channel: lanes m, m + 16, m + 32, m + 48 hold its partials

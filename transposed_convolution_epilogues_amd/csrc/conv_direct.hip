@@ -247,7 +247,10 @@ __global__ __launch_bounds__(kBlock) void convT_bn_pool_phase1_direct_kernel(con
 
 // Phase 2: each block merges its channel's partials in float64 (redundantly
 // across the blocks of that channel), forms mean and biased variance, and
-// applies gamma*(v - mean)/sqrt(var + eps) + beta to a chunk of pooled values.
+// applies gamma*(v - mean)/sqrt(var + eps) + beta to the pooled values of a
+// run of samples.  A sample's pooled values of one channel are one contiguous
+// plane, so a block reads and writes whole planes with coalesced accesses,
+// issuing a batch of loads before their stores.
 __global__ __launch_bounds__(kBlock) void bn_pool_phase2_kernel(float* __restrict__ y,
                                                                 const double* __restrict__ ws,
                                                                 int64_t parts, const float* __restrict__ conv_bias,
@@ -288,23 +291,24 @@ __global__ __launch_bounds__(kBlock) void bn_pool_phase2_kernel(float* __restric
     }
     __syncthreads();
     const float sc = s_scale, sh = s_shift;
-    // this block's slice [lo, hi) of the pooled positions, in every sample: a
-    // thread owns a position and loads it from 8 samples before storing any
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 16;
     const int64_t pp = pg.P[0] * pg.P[1] * pg.P[2];
-    const int64_t per_block = ceil_div(pp, blocks_per_channel);
-    const int64_t lo = q * per_block, hi = lo + per_block < pp ? lo + per_block : pp;
-    const int64_t nstride = g.Cout * pp;
-    for (int64_t j = lo + threadIdx.x; j < hi; j += blockDim.x) {
-        float* yj = y + c * pp + j;
-        for (int64_t n0 = 0; n0 < g.N; n0 += kBatch) {
+    const int64_t spb = ceil_div(g.N, blocks_per_channel);
+    const int64_t n0 = q * spb, n1 = n0 + spb < g.N ? n0 + spb : g.N;
+    for (int64_t n = n0; n < n1; ++n) {
+        float* yp = y + (n * g.Cout + c) * pp;  // this sample's plane of channel c
+        for (int64_t j0 = 0; j0 < pp; j0 += (int64_t)kBatch * kBlock) {
             float v[kBatch];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u)
-                if (n0 + u < g.N) v[u] = yj[(n0 + u) * nstride];
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t j = j0 + u * kBlock + threadIdx.x;
+                if (j < pp) v[u] = yp[j];
+            }
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u)
-                if (n0 + u < g.N) yj[(n0 + u) * nstride] = fmaf(v[u], sc, sh);
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t j = j0 + u * kBlock + threadIdx.x;
+                if (j < pp) yp[j] = fmaf(v[u], sc, sh);
+            }
         }
     }
 }
@@ -360,12 +364,11 @@ hipError_t launch_convT_bn_pool_phase1_direct(const float* x, const float* w, fl
 hipError_t launch_bn_pool_phase2(float* y, const double* ws, int64_t parts_per_channel, const float* conv_bias,
                                  const float* gamma, const float* beta, float eps, float* mean_out,
                                  float* var_out, const BnRunning& run, const PoolGeom& pg, hipStream_t st) {
-    // slices of at least kBlock pooled positions of one channel, at most
-    // about 1024 blocks in all (every block also merges its channel's partials)
-    const int64_t pp = pg.P[0] * pg.P[1] * pg.P[2];
-    int64_t bpc = ceil_div(pp, kBlock);
-    if (bpc > ceil_div(1024, pg.g.Cout)) bpc = ceil_div(1024, pg.g.Cout);
-    if (bpc < 1) bpc = 1;
+    // runs of samples of one channel, about 1024 blocks in all (every block
+    // also merges its channel's partials)
+    int64_t bpc = ceil_div(1024, pg.g.Cout);
+    if (bpc > pg.g.N) bpc = pg.g.N;
+    bpc = ceil_div(pg.g.N, ceil_div(pg.g.N, bpc));  // no block without a sample
     const int64_t count = pg.g.N * pg.g.O[0] * pg.g.O[1] * pg.g.O[2];
     hipLaunchKernelGGL(bn_pool_phase2_kernel, dim3((unsigned)(bpc * pg.g.Cout)), dim3(kBlock), 0, st, y, ws,
                        parts_per_channel, conv_bias, gamma, beta, eps, mean_out, var_out, run, pg, bpc, count);
