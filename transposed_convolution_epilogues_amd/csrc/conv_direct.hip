@@ -264,6 +264,22 @@ __global__ __launch_bounds__(kBlock) void bn_pool_phase2_kernel(float* __restric
     const Geom& g = pg.g;
     const int64_t c = blockIdx.x / blocks_per_channel;
     const int64_t q = blockIdx.x % blocks_per_channel;
+    constexpr int kBatch = 16;
+    const int64_t pp = pg.P[0] * pg.P[1] * pg.P[2];
+    const int64_t spb = ceil_div(g.N, blocks_per_channel);
+    const int64_t n0 = q * spb, n1 = n0 + spb < g.N ? n0 + spb : g.N;
+    // the first batch of this block's pooled values does not depend on the
+    // statistics: its loads are issued before the partials are merged, so the
+    // two round trips overlap
+    float v0[kBatch];
+    if (n0 < n1) {
+        const float* yp = y + (n0 * g.Cout + c) * pp;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t j = u * kBlock + threadIdx.x;
+            if (j < pp) v0[u] = yp[j];
+        }
+    }
     double a = 0.0, b2 = 0.0;
     const double* pc = ws + 2 * c * parts;
     for (int64_t i = threadIdx.x; i < parts; i += blockDim.x) {
@@ -291,18 +307,19 @@ __global__ __launch_bounds__(kBlock) void bn_pool_phase2_kernel(float* __restric
     }
     __syncthreads();
     const float sc = s_scale, sh = s_shift;
-    constexpr int kBatch = 16;
-    const int64_t pp = pg.P[0] * pg.P[1] * pg.P[2];
-    const int64_t spb = ceil_div(g.N, blocks_per_channel);
-    const int64_t n0 = q * spb, n1 = n0 + spb < g.N ? n0 + spb : g.N;
     for (int64_t n = n0; n < n1; ++n) {
         float* yp = y + (n * g.Cout + c) * pp;  // this sample's plane of channel c
         for (int64_t j0 = 0; j0 < pp; j0 += (int64_t)kBatch * kBlock) {
             float v[kBatch];
+            if (n == n0 && j0 == 0) {
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int64_t j = j0 + u * kBlock + threadIdx.x;
-                if (j < pp) v[u] = yp[j];
+                for (int u = 0; u < kBatch; ++u) v[u] = v0[u];
+            } else {
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int64_t j = j0 + u * kBlock + threadIdx.x;
+                    if (j < pp) v[u] = yp[j];
+                }
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
