@@ -281,15 +281,22 @@ def probe_mfma(torch):
 
 
 def gpu_clocks():
-    """Current and maximum shader clock from rocm-smi (None where it is not available)."""
+    """Current shader clock (MHz) from the driver's sysfs table of sclk levels
+    (the active level is marked '*'), or None.  A file read: no other program
+    is started from this process, which has initialised the GPU."""
+    import glob
     import re
-    import subprocess
-    try:
-        txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
-    except (OSError, subprocess.SubprocessError):
-        return None
-    m = re.search(r"sclk clock level:\s*\d+:\s*\(?(\d+)\s*Mhz", txt, re.I)
-    return int(m.group(1)) if m else None
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                        if m:
+                            return int(m.group(1))
+        except OSError:
+            continue
+    return None
 
 
 def hardware(torch):
