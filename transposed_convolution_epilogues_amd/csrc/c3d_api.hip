@@ -390,14 +390,18 @@ c3d_status convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const f
     const size_t need = bn_training_bytes(pg, algo);
     if (!ws || ws_bytes < need) return C3D_ERR_WORKSPACE;
     if (((uintptr_t)ws & 7u) != 0) return C3D_ERR_ALIGN;
+    const c3d::BnRunning run{update ? running_mean : nullptr, update ? running_var : nullptr, momentum};
+    if (algo == C3D_ALGO_BN_SWAP) {
+        // the whole module, statistics first, then the normalised pooled sums
+        const c3d::BnEval none{nullptr, nullptr, nullptr, nullptr, nullptr, 0.f};
+        const c3d::BnSwapTrain tr{conv_bias, gamma, beta, eps, batch_mean, batch_var, run};
+        return hip_status(c3d::launch_convT_bn_swap(x, w, y, ws, pg, none, &tr, s));
+    }
     double* part = (double*)ws;
-    int64_t nparts = (int64_t)parts;
+    const int64_t nparts = (int64_t)parts;
     const c3d::BnEval none{nullptr, nullptr, nullptr, nullptr, nullptr, 0.f};
     hipError_t e;
-    if (algo == C3D_ALGO_BN_SWAP) {
-        e = c3d::launch_convT_bn_swap(x, w, y, part, pg, none, &part, s);  // part -> the per-channel finals
-        nparts = 1;
-    } else if (algo == C3D_ALGO_BN_MFMA) {
+    if (algo == C3D_ALGO_BN_MFMA) {
         e = c3d::launch_convT_bn_pool_phase1_mfma(x, w, y, part, pg, none, s);
     } else if (algo == C3D_ALGO_BN_CELLS) {
         e = c3d::launch_convT_bn_pool_phase1_fast(x, w, y, part, pg, none, s);
@@ -405,7 +409,6 @@ c3d_status convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const f
         e = c3d::launch_convT_bn_pool_phase1_direct(x, w, y, part, pg, none, s);
     }
     if (e != hipSuccess) return C3D_ERR_HIP;
-    const c3d::BnRunning run{update ? running_mean : nullptr, update ? running_var : nullptr, momentum};
     return hip_status(c3d::launch_bn_pool_phase2(y, part, nparts, conv_bias, gamma, beta, eps, batch_mean,
                                                  batch_var, run, pg, s));
 }

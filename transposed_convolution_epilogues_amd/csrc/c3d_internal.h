@@ -101,14 +101,25 @@ bool conv_k1last_supported(const Geom& g, const void* x, const void* w, const vo
 hipError_t launch_conv_k1last(const float* x, const float* w, const float* bias, float* y, const Geom& g,
                               hipStream_t st);
 // The page's module (k3 s2 p1, pool 4, Cin <= 3, Cout <= 32) with the sums
-// swapped: pooled sums from summed weights, batch statistics from lag
-// correlations of the input.  Training mode leaves one (sum, sum of squares)
-// part per channel at *stats_out (inside ws) for phase 2; eval mode (ev set)
-// writes the final output and uses no workspace.
+// swapped: pooled sums from summed weights on the matrix cores, batch
+// statistics from lag correlations of the input and Gram matrices of its
+// boundary.  Training mode (tr set) runs the whole module: it writes the
+// normalised y, the batch statistics and the running update, using ws
+// (convT_bn_swap_workspace_bytes, 8-byte aligned); eval mode (ev.gamma set)
+// writes y with the running statistics and uses no workspace.
+struct BnSwapTrain {
+    const float* bias;
+    const float* gamma;
+    const float* beta;
+    float eps;
+    float* mean_out;
+    float* var_out;
+    BnRunning run;
+};
 bool convT_bn_swap_supported(const PoolGeom& pg, const void* x);
 size_t convT_bn_swap_workspace_bytes(const PoolGeom& pg);
-hipError_t launch_convT_bn_swap(const float* x, const float* w, float* y, double* ws, const PoolGeom& pg,
-                                const BnEval& ev, double** stats_out, hipStream_t st);
+hipError_t launch_convT_bn_swap(const float* x, const float* w, float* y, void* ws, const PoolGeom& pg,
+                                const BnEval& ev, const BnSwapTrain* tr, hipStream_t st);
 bool convT_bn_pool_fast_supported(const PoolGeom& pg, const void* x);
 bool convT_bn_pool_mfma_supported(const PoolGeom& pg, const void* x);
 size_t convT_bn_pool_mfma_partials(const PoolGeom& pg);
