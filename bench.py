@@ -40,7 +40,7 @@ KERNELS = {
     "c1": ("conv3d_direct_kernel", [CSRC + "conv_direct.hip"]),
     "c2": ("conv_k1last_kernel", [CSRC + "conv_k1last.hip"]),
     "c3": ("conv333_store_kernel", [CSRC + "convT_sublattice.hip", CSRC + "conv333_mfma.h"]),
-    "c4": ("convT_bn_pool_mfma_kernel", [CSRC + "convT_bn_pool_mfma.hip"]),
+    "c4": ("swap_pool_kernel", [CSRC + "convT_bn_swap.hip"]),
     "c5": ("conv_pool_lse_mfma_kernel", [CSRC + "conv_pool_lse.hip", CSRC + "conv333_mfma.h"]),
 }
 
@@ -240,7 +240,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded U[-1,1] inputs, PyTorch-default uniform weights)",
         "config": {
-            "workload": "fused 3D conv suite, one pass of c2+c3+c4+c5 at full size: " +
+            "workload": "fused 3D conv suite, one pass of c1+c2+c3+c4+c5 at full size: " +
                         "; ".join(f"{k}: {runs[k]['wl'].description}" for k in runs),
             "per_config": per,
             "frac_fp32_peak_step": round(value / FP32_PEAK_TFLOPS, 4),
@@ -350,7 +350,7 @@ def widen(torch, args):
         through the LDS-scatter algorithm;
       - the c4 module with BatchNorm in eval mode (running statistics), in
         training mode with the running-statistics update, and through its
-        swapped-sums algorithm."""
+        second algorithm (the output-phase classes on the matrix cores)."""
     from transposed_convolution_epilogues_amd import binding as B
     from transposed_convolution_epilogues_amd import workloads as W
 
@@ -361,7 +361,7 @@ def widen(torch, args):
     cases = ([(k, wl, 0, "convT") for k, wl in W.WIDEN.items()] + [("c3_phase", W.CONFIGS["c3"], 2, "convT")] +
              [("t1_scatter", W.WIDEN["t1"], 4, "convT"), ("c3_scatter", W.CONFIGS["c3"], 4, "convT")] +
              [("c4_eval", c4, 0, "bn_eval"), ("c4_train_running", c4, 0, "bn_running"),
-              ("c4_swapped_sums", c4, 3, "bn_swap")])
+              ("c4_phase_classes", c4, 3, "bn_second")])
     out = {}
     for key, wl, variant, kind in cases:
         inp = W.make_inputs(wl)
@@ -382,7 +382,7 @@ def widen(torch, args):
             rm, rv = t(rm0), t(rv0)
             ws = torch.empty(B.convT_bn_avgpool_workspace_bytes(wl.x_shape, wl.cout, p, wl.pool), dtype=torch.uint8,
                              device=dev)
-            if kind == "bn_swap":  # the module's second algorithm, batch statistics only
+            if kind == "bn_second":  # the module's second algorithm, batch statistics only
                 fn = lambda: B.convT_bn_avgpool(x, w, b, gm, bt, wl.eps, wl.pool, out=y, workspace=ws, **kw)
             else:
                 train = kind == "bn_running"
@@ -392,7 +392,7 @@ def widen(torch, args):
         nbytes = xb + wb + 4 * y.numel()
         row = dict(workload=wl.description + {"convT": "", "bn_eval": "; BN in eval mode",
                                               "bn_running": "; training mode + running-statistics update",
-                                              "bn_swap": "; swapped-sums algorithm"}[kind],
+                                              "bn_second": "; output-phase classes on the matrix cores"}[kind],
                    mac=mac, algo_bytes=nbytes)
         for label, v, reps in (("fast", variant, args.steps), ("generic", 1, 3)):
             old = B.set_variant(v)

@@ -225,14 +225,16 @@ const char* c3d_status_str(c3d_status status);
  * the generic direct kernels, 2 = skip the shape-specialised kernels (the
  * flattened-row conv for (k,k,1) kernels and the stride-2/dilation-2
  * sub-lattice transposed conv) so that the general MFMA paths run where
- * they apply, 3 = as 0 but with the swapped-sums algorithm for
- * convT_bn_avgpool where it applies (see c3d_convT_bn_avgpool_algo), 4 = as
+ * they apply (for convT_bn_avgpool: the output-phase classes on the matrix
+ * cores instead of the swapped sums), 3 = as 0 but with the second algorithm
+ * of convT_bn_avgpool where the swapped sums apply, the output-phase classes
+ * on the matrix cores (see c3d_convT_bn_avgpool_algo), 4 = as
  * 0 but conv_transpose3d_fwd scatters into an LDS output tile
  * (C3D_ALGO_SCATTER: "Kimi-K2.6 l1_p77", the scatter form, which needs no
  * atomics within one tap offset because the input-to-output map is
  * injective there; LDS-bound, the second algorithm to compare against),
  * 5 = as 0 but convT_bn_avgpool uses its one-thread-per-cell fp32 kernel
- * (C3D_ALGO_BN_CELLS) instead of the matrix-core one.
+ * (C3D_ALGO_BN_CELLS).
  * Returns the previous value.  The setting belongs to the calling thread
  * (thread-local): other threads keep their own, starting at 0. */
 int c3d_set_variant(int variant);
@@ -273,17 +275,18 @@ c3d_status c3d_conv3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_con
  * Cin/groups >= 4, Cout/groups >= 8. */
 c3d_status c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo);
 
-/* The same for convT_bn_avgpool and convT_bn_avgpool_ex.  The swapped-sums
- * path ("Kimi-K2.6 l2_p72", the proposal to swap the pooled sum and the conv
- * sum) takes the page's module (kernel 3, stride 2, padding 1, dilation 1,
- * no output padding, pool 4, groups 1) with Cin <= 3 and Cout <= 32: pooled
- * sums from 3x3x3 summed weights, batch statistics from lag correlations of
- * the input.  It is the second algorithm for the module, selected by
- * variant 3.  The default for Cin <= 4 and Cout <= 16 is C3D_ALGO_BN_MFMA
- * (the 8 output-phase classes of [p72]'s parity tables, each a GEMM over
- * Cin x taps on the matrix cores, pooled and squared in registers); other
- * Cin <= 4 shapes, or variant 5, take the one-thread-per-cell fp32 kernel
- * (C3D_ALGO_BN_CELLS). */
+/* The same for convT_bn_avgpool and convT_bn_avgpool_ex.  The default for
+ * the page's module (kernel 3, stride 2, padding 1, dilation 1, no output
+ * padding, pool 4, groups 1) with Cin <= 3 and Cout <= 32 is the swapped-sums
+ * path C3D_ALGO_BN_SWAP ("Kimi-K2.6 l2_p72", the proposal to swap the pooled
+ * sum and the conv sum): pooled sums from 3x3x3 summed weights on the matrix
+ * cores, batch statistics from lag correlations of the input and Gram
+ * matrices of its boundary; no transposed-conv output is formed.  The second
+ * algorithm (variant 3, and the default for the other Cin <= 4, Cout <= 16
+ * shapes) is C3D_ALGO_BN_MFMA: the 8 output-phase classes of [p72]'s parity
+ * tables, each a GEMM over Cin x taps on the matrix cores, pooled and squared
+ * in registers.  Other Cin <= 4 shapes, or variant 5, take the
+ * one-thread-per-cell fp32 kernel (C3D_ALGO_BN_CELLS). */
 c3d_status c3d_convT_bn_avgpool_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t pool,
                               int32_t* algo);
 

@@ -402,14 +402,17 @@ def test_kernel_choice(case):
 
 BN_ALGO_CASES = [
     # (x_shape, cout, kernel, stride, pad, pool, variant, expected)
-    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 0, "bn_mfma"),    # c4
-    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 3, "bn_swap"),
+    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 0, "bn_swap"),    # c4: swapped sums
+    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 4, "bn_swap"),
+    ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 3, "bn_mfma"),    # the module's second algorithm
     ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 2, "bn_mfma"),
     ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 5, "bn_cells"),   # per-cell fp32 kernel on request
     ((64, 3, 32, 32, 32), 16, 3, 2, 1, 4, 1, "direct"),
     ((2, 4, 8, 8, 8), 16, 3, 2, 1, 4, 3, "bn_mfma"),       # Cin 4: outside the swapped-sums path
     ((2, 3, 8, 8, 8), 40, 3, 2, 1, 4, 3, "bn_cells"),      # Cout 40: outside both
-    ((2, 3, 8, 8, 8), 17, 3, 2, 1, 4, 0, "bn_cells"),      # Cout 17: more than one MFMA N tile
+    ((2, 3, 8, 8, 8), 17, 3, 2, 1, 4, 0, "bn_swap"),       # Cout 17: two N tiles on the swapped sums
+    ((2, 3, 8, 8, 8), 17, 3, 2, 1, 4, 3, "bn_cells"),      # outside the phase-class kernel (Cout > 16)
+    ((2, 4, 8, 8, 8), 16, 3, 2, 1, 4, 0, "bn_mfma"),       # Cin 4: default outside the swapped sums
     ((2, 5, 8, 8, 8), 16, 3, 2, 1, 4, 0, "direct"),        # Cin 5
     ((2, 3, 8, 8, 8), 16, 3, 2, 1, 2, 3, "direct"),        # pool 2
     ((2, 3, 8, 8, 8), 16, 3, 1, 1, 4, 0, "direct"),        # stride 1

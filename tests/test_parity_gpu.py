@@ -38,9 +38,10 @@ def variant(request):
     B.set_variant(old)
 
 
-@pytest.fixture(params=[0, 1, 3, 5], ids=["auto", "generic", "swapped_sums", "per_cell"])
+@pytest.fixture(params=[0, 1, 3, 5], ids=["swapped_sums", "generic", "matrix_cores", "per_cell"])
 def bn_variant(request):
-    """Kernel choices of the c4 module: per-cell (default), generic, swapped sums."""
+    """Kernel choices of the c4 module: swapped sums (default), generic, output-phase
+    classes on the matrix cores (the second algorithm), per-cell."""
     old = B.set_variant(request.param)
     yield request.param
     B.set_variant(old)
@@ -357,14 +358,14 @@ def test_c3_full_size_sampled_and_checkerboard():
     assert torch.equal(y, y2)
 
 
-@pytest.mark.parametrize("v", [0, 5, 3], ids=["matrix_cores", "per_cell", "swapped_sums"])
+@pytest.mark.parametrize("v", [0, 5, 3], ids=["swapped_sums", "per_cell", "matrix_cores"])
 def test_c4_full_size(v):
     old = B.set_variant(v)
     try:
         wl = W.CONFIGS["c4"]
         p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
-        assert B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool) == {0: "bn_mfma", 5: "bn_cells",
-                                                                             3: "bn_swap"}[v]
+        assert B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool) == {0: "bn_swap", 5: "bn_cells",
+                                                                             3: "bn_mfma"}[v]
         inp = W.make_inputs(wl)
         y = check_full(wl, inp, "c4")
         # repeat (the workspace is reused) and compare bit for bit
@@ -375,7 +376,7 @@ def test_c4_full_size(v):
 
 
 @pytest.mark.parametrize("dist", ["unit", "offset4"])
-@pytest.mark.parametrize("v", [0, 5, 3], ids=["matrix_cores", "per_cell", "swapped_sums"])
+@pytest.mark.parametrize("v", [0, 5, 3], ids=["swapped_sums", "per_cell", "matrix_cores"])
 def test_c4_full_size_offset_inputs(v, dist):
     """The module at full size with inputs whose mean is far from zero: U[0,1)
     (the pages' torch.rand) and 4 + U[-1,1].  The batch variance is then a
@@ -415,16 +416,23 @@ MFMA_MEDIUM = {
 @pytest.mark.parametrize("name", list(MFMA_MEDIUM))
 def test_c4_matrix_core_medium(name):
     wl = MFMA_MEDIUM[name]
-    p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
-    assert B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool) == "bn_mfma"
-    print(f"[c4 matrix cores {name}] {wl}", flush=True)
-    check_full(wl, W.make_inputs(wl), name)
+    old = B.set_variant(3)  # the module's second algorithm where the swapped sums would apply
+    try:
+        p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+        assert B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool) == "bn_mfma"
+        print(f"[c4 matrix cores {name}] {wl}", flush=True)
+        check_full(wl, W.make_inputs(wl), name)
+    finally:
+        B.set_variant(old)
 
 
-def test_c4_matrix_core_unaligned_input():
-    """x 4 bytes off a 16-byte boundary: the matrix-core path stages the input
-    box with scalar loads instead of 16-byte ones (S2 % 4 == 0 here)."""
-    wl = W.CONFIGS["c4"].with_(x_shape=(2, 3, 9, 10, 20))
+@pytest.mark.parametrize("v,shape", [(3, (2, 3, 9, 10, 20)), (0, (2, 3, 9, 10, 20)), (0, (64, 3, 32, 32, 32))],
+                         ids=["matrix_cores", "swapped_sums", "swapped_sums_full"])
+def test_c4_unaligned_input(v, shape):
+    """x 4 bytes off a 16-byte boundary: both algorithms stage the input with
+    scalar loads instead of 16-byte ones (the swapped sums at full size then
+    take their general statistics and pooled kernels)."""
+    wl = W.CONFIGS["c4"].with_(x_shape=shape)
     inp = W.make_inputs(wl)
     ref, ref_mean, ref_var = O.run_workload(wl, inp)
     flat = torch.empty(int(np.prod(wl.x_shape)) + 1, dtype=torch.float32, device="cuda")
@@ -432,8 +440,15 @@ def test_c4_matrix_core_unaligned_input():
     x.copy_(dev(inp.x))
     assert x.data_ptr() % 16 == 4
     out, mean, var = poisoned(ref.shape), poisoned((wl.cout,)), poisoned((wl.cout,))
-    B.convT_bn_avgpool(x, dev(inp.w), dev(inp.b), dev(inp.gamma), dev(inp.beta), wl.eps, wl.pool, wl.stride,
-                       wl.pad, wl.dilation, out=out, batch_mean=mean, batch_var=var)
+    old = B.set_variant(v)
+    try:
+        p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+        assert B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool) == {0: "bn_swap", 3: "bn_mfma"}[v]
+        print(f"[c4 unaligned v{v}] {shape}", flush=True)
+        B.convT_bn_avgpool(x, dev(inp.w), dev(inp.b), dev(inp.gamma), dev(inp.beta), wl.eps, wl.pool, wl.stride,
+                           wl.pad, wl.dilation, out=out, batch_mean=mean, batch_var=var)
+    finally:
+        B.set_variant(old)
     assert_close("c4 unaligned out", out.cpu().numpy(), ref)
     assert_close("c4 unaligned mean", mean.cpu().numpy(), ref_mean)
     assert_close("c4 unaligned var", var.cpu().numpy(), ref_var)
@@ -452,7 +467,7 @@ SWAP_MEDIUM = {
 @pytest.mark.parametrize("name", list(SWAP_MEDIUM))
 def test_c4_swapped_sums_medium(name):
     wl = SWAP_MEDIUM[name]
-    old = B.set_variant(3)
+    old = B.set_variant(0)
     try:
         p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
         assert B.convT_bn_avgpool_algo(wl.x_shape, wl.cout, p, wl.pool) == "bn_swap"

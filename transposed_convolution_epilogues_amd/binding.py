@@ -261,7 +261,8 @@ def probe_mfma_f32(iters: int, out: torch.Tensor, stream=None) -> int:
 def set_variant(variant: int) -> int:
     """0 = automatic kernel choice, 1 = force the generic direct kernels,
     2 = skip the shape-specialised kernels (general MFMA paths where they apply),
-    3 = automatic, but the swapped-sums algorithm for convT_bn_avgpool where it applies,
+    3 = automatic, but convT_bn_avgpool's second algorithm (the output-phase classes on
+        the matrix cores) where the swapped sums would apply,
     4 = automatic, but conv_transpose3d_fwd scatters into an LDS output tile,
     5 = automatic, but convT_bn_avgpool runs its one-thread-per-cell fp32 kernel.
     The setting is the calling thread's own (the library keeps it thread-local)."""

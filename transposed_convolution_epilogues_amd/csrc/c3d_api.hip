@@ -126,7 +126,8 @@ c3d_status scratch_on_device(int dev, void** out) {
 // stride-2 dilation-2 transposed conv) so the general fast paths can be
 // compared with them; variants 3 and 4 select the second algorithms of the
 // ConvT -> BatchNorm -> AvgPool module (swapped sums) and of the transposed
-// conv (LDS scatter).
+// conv (LDS scatter); for the module the swapped sums are the default and
+// variant 3 selects the output-phase classes.
 //
 // A convolution below 2^19 MAC (the 4->8 channel, 8^3 layer: 442,368) takes
 // the one-thread-per-output kernel: the matrix-core engines' workgroup tiles
@@ -145,14 +146,15 @@ int conv3d_algo(const Geom& g) {
     return C3D_ALGO_DIRECT;
 }
 
-// ConvT -> BatchNorm -> AvgPool module: the output-phase classes on the
-// matrix cores where they apply (variants 0, 2 and 4), one thread per 4x4x4
-// cell otherwise or with variant 5, the swapped sums (variant 3; measured
-// slower on MI355X, kept as the second algorithm), generic (variant 1)
+// ConvT -> BatchNorm -> AvgPool module: the swapped sums where they apply
+// (variants 0 and 4), else the output-phase classes on the matrix cores
+// (also variant 2, which skips the shape-specialised path, and variant 3, the
+// module's second algorithm), one thread per 4x4x4 cell otherwise or with
+// variant 5, generic (variant 1)
 int bn_algo(const PoolGeom& pg) {
     const int v = t_variant;
     if (v == 1) return C3D_ALGO_DIRECT;
-    if (v == 3 && c3d::convT_bn_swap_supported(pg, nullptr)) return C3D_ALGO_BN_SWAP;
+    if (v != 2 && v != 3 && v != 5 && c3d::convT_bn_swap_supported(pg, nullptr)) return C3D_ALGO_BN_SWAP;
     if (v != 5 && c3d::convT_bn_pool_mfma_supported(pg, nullptr)) return C3D_ALGO_BN_MFMA;
     if (c3d::convT_bn_pool_fast_supported(pg, nullptr)) return C3D_ALGO_BN_CELLS;
     return C3D_ALGO_DIRECT;

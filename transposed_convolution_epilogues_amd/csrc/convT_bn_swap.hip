@@ -307,21 +307,22 @@ __global__ __launch_bounds__(kThreads) void swap_stats_kernel(StatArgs a) {
     const float* xn = a.x + n * CIN * (int64_t)S0 * a.S[1] * a.S[2];
     const int r0 = t1 * kTile - 1, c0 = t2 * kTile - 1;
 
+    // Plane P is stored before the loop; plane p + 1 is stored at the top of
+    // the iteration of plane p, before its barrier, so the loads fetched one
+    // iteration earlier had a whole iteration of products to arrive.
     float4 pre[CIN];
     if constexpr (FAST) {
         // halos are zero and never written again; the interiors are fetched
         for (int i = tid; i < 3 * kSlot / 4; i += kThreads)
             reinterpret_cast<float4*>(lds)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        fast_fetch<CIN>(xn, P, S0, pre);
-        __syncthreads();
-        fast_put<CIN>(lds, pre);
+        float4 pre0[CIN];
+        fast_fetch<CIN>(xn, P, S0, pre0);
         fast_fetch<CIN>(xn, P + 1, S0, pre);
-        fast_put<CIN>(lds + kSlot, pre);
+        __syncthreads();
+        fast_put<CIN>(lds, pre0);
     } else {
         box_stage<CIN>(xn, P, a, r0, c0, lds);
-        box_stage<CIN>(xn, P + 1, a, r0, c0, lds + kSlot);
     }
-    __syncthreads();
 
     float acc[NA];
 #pragma unroll
@@ -330,19 +331,18 @@ __global__ __launch_bounds__(kThreads) void swap_stats_kernel(StatArgs a) {
     const int lane_base = (4 * g + 1) * kRS + 4 + (lane & 31);
     for (int p = P; p < Pend; ++p) {
         const int i = p - P;
-        const bool more = p + 2 <= Pend;  // plane p + 2 is read by the next plane
+        // plane p + 1 (zero beyond the input) into the slot after plane p's
+        if constexpr (FAST)
+            fast_put<CIN>(lds + ((i + 1) % 3) * kSlot, pre);
+        else
+            box_stage<CIN>(xn, p + 1, a, r0, c0, lds + ((i + 1) % 3) * kSlot);
+        __syncthreads();
         if constexpr (FAST) {
-            if (more) fast_fetch<CIN>(xn, p + 2, S0, pre);
+            if (p + 1 < Pend) fast_fetch<CIN>(xn, p + 2, S0, pre);  // read by the next plane
         }
         stat_rows<CIN>(lds + (i % 3) * kSlot + lane_base, lds + ((i + 1) % 3) * kSlot + lane_base, acc);
-        if (more) {
-            if constexpr (FAST)
-                fast_put<CIN>(lds + ((i + 2) % 3) * kSlot, pre);
-            else
-                box_stage<CIN>(xn, p + 2, a, r0, c0, lds + ((i + 2) % 3) * kSlot);
-        }
-        __syncthreads();
     }
+    __syncthreads();
     // every LDS read is done: the first slot takes the four waves' totals
     wave_reduce_to<NA>(acc, lds + wv * NA, lane);
     __syncthreads();
@@ -401,13 +401,15 @@ __host__ __device__ inline int shell_lds_floats(int C, int Sa, int Sb) {
     return z + 2 * (shell_rs(Sb) + 8) + 128;
 }
 constexpr int kShellLds = 12288;  // floats of the staged planes
+constexpr int kShellThreads = 1024;
 
 template <int CIN>
-__global__ __launch_bounds__(kThreads) void swap_shell_lds_kernel(ShellArgs a) {
+__global__ __launch_bounds__(kShellThreads) void swap_shell_lds_kernel(ShellArgs a) {
     __shared__ __attribute__((aligned(16))) float pl[kShellLds];
-    __shared__ float red[18][kThreads / 64][256];  // up to 18 types per face axis
+    __shared__ float red[18][4][256];  // up to 18 types per face axis, four waves each
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wv = wave & 3;  // four groups of four waves
     const int64_t n = blockIdx.x / 3;
     const int fi = blockIdx.x % 3;
     const int ad = fi == 0 ? 1 : 0, bd = fi == 2 ? 1 : 2;
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void swap_shell_lds_kernel(ShellArgs a) {
     zoff += ((24 - zoff) % 64 + 64) % 64;
     int ooff = zoff + RS + 8;
     ooff += ((28 - ooff) % 64 + 64) % 64;
-    for (int i = tid; i < RS + 8; i += kThreads) {
+    for (int i = tid; i < RS + 8; i += kShellThreads) {
         pl[zoff + i] = 0.f;
         pl[ooff + i] = 1.f;
     }
@@ -430,12 +432,12 @@ __global__ __launch_bounds__(kThreads) void swap_shell_lds_kernel(ShellArgs a) {
     // index splits use float reciprocals (exact below 2^22)
     const int total = 2 * CIN * face;
     const float rface = 1.f / (float)face, rsb = 1.f / (float)Sb;
-    for (int e0 = 0; e0 < total; e0 += 12 * kThreads) {
+    for (int e0 = 0; e0 < total; e0 += 12 * kShellThreads) {
         float v[12];
         int dst[12];
 #pragma unroll
         for (int u = 0; u < 12; ++u) {
-            const int e = e0 + u * kThreads + tid;
+            const int e = e0 + u * kShellThreads + tid;
             const int ec = e < total ? e : total - 1;
             const int sc = (int)(((float)ec + 0.5f) * rface), idx = ec - sc * face;
             const int ia = (int)(((float)idx + 0.5f) * rsb), ib = idx - ia * Sb;
@@ -452,13 +454,15 @@ __global__ __launch_bounds__(kThreads) void swap_shell_lds_kernel(ShellArgs a) {
     // types: side (L or H on axis fi), classes of a and b (only M below the
     // face axis).  A type's positions form an na x nb grid; a step takes 4
     // rows (lane group kq = row within the group) at one column, so within a
-    // row group the LDS reads are immediate offsets.  The waves take the row
-    // groups of every type in turn, the first wave rotating per type; each
-    // wave leaves its partial of each type in LDS: one barrier, then the sums.
+    // row group the LDS reads are immediate offsets.  Type slot s goes to wave
+    // group s % 4, whose four waves take its row groups in turn, the first
+    // rotating per type; each wave leaves its partial in LDS: one barrier,
+    // then the sums.
     int slot = 0;
     for (int side = 0; side < 2; ++side)
         for (int ta = (ad < fi ? 1 : 0); ta <= (ad < fi ? 1 : 2); ++ta)
             for (int tb = (bd < fi ? 1 : 0); tb <= (bd < fi ? 1 : 2); ++tb, ++slot) {
+                if ((slot & 3) != grp) continue;  // uniform per wave
                 const int nM = (ta == 1) + (tb == 1);
                 const int na = ta == 1 ? Sa - 1 : 1, nb = tb == 1 ? Sb - 1 : 1;
                 const bool real = m < (CIN << nM);
@@ -474,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void swap_shell_lds_kernel(ShellArgs a) {
                 }
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 const int groups = na > 0 && nb > 0 ? (na + 3) >> 2 : 0;
-                for (int g = (wv - slot) & 3; g < groups; g += kThreads / 64) {
+                for (int g = (wv - (slot >> 2)) & 3; g < groups; g += 4) {
                     const int row = 4 * g + kq;
                     const bool rok = row < na;
                     const float* src = pl + (real && rok ? base + row * RS : (one_lane(m) && rok ? ooff : zoff));
@@ -499,10 +503,12 @@ __global__ __launch_bounds__(kThreads) void swap_shell_lds_kernel(ShellArgs a) {
                 tau[fi] = side ? 2 : 0;
                 tau[ad] = ta;
                 tau[bd] = tb;
-                float sum = red[slot][0][tid];
+                if ((slot & 3) != (tid >> 8)) continue;  // thread group s % 4 writes slot s
+                const int e = tid & 255;
+                float sum = red[slot][0][e];
 #pragma unroll
-                for (int w = 1; w < kThreads / 64; ++w) sum += red[slot][w][tid];
-                a.part[((int64_t)n * kTypes + type_index(tau[0], tau[1], tau[2])) * 256 + tid] = sum;
+                for (int w = 1; w < 4; ++w) sum += red[slot][w][e];
+                a.part[((int64_t)n * kTypes + type_index(tau[0], tau[1], tau[2])) * 256 + e] = sum;
             }
 }
 
@@ -735,8 +741,9 @@ __device__ void entry_index(int e, int C, int* out) {
 
 // Block v < NS sums statistic v over the statistics workgroups; block NS + t
 // sums the Gram matrix of type t over its partial rows (entry tid % 256, four
-// groups of rows, eight loads in flight each).  Every block also builds its
-// slice of the contraction's index table, and block 0 the summed weights.
+// groups of rows); block NS + 26 builds the summed weights.  Each block
+// issues its loads (sixteen in flight per thread) before it computes its
+// slice of the contraction's index table.
 __global__ __launch_bounds__(kFinThreads) void swap_reduce_kernel(FinArgs a) {
     __shared__ double red[kFinThreads];
     __shared__ float wl[kMaxCin * kMaxCout * 27];
@@ -744,17 +751,29 @@ __global__ __launch_bounds__(kFinThreads) void swap_reduce_kernel(FinArgs a) {
     const int C = a.Cin, NS = n_stat(C);
     const int v = blockIdx.x;
     const int E = C * C * 125 + C * 27;  // contraction entries: sums over classes of (C 2^|r|)^2 and C 2^|r|
-    {
+    auto table_slice = [&]() {
         const int chunk = (E + (int)gridDim.x - 1) / (int)gridDim.x, e = v * chunk + tid;
         if (tid < chunk && e < E) {
             int o[9];
             entry_index(e, C, o);
             for (int k = 0; k < 9; ++k) a.tab[e * 9 + k] = o[k];
         }
-    }
+    };
     if (v < NS) {
+        // parts b = tid, tid + 1024, ... of statistic v, in order
         double s = 0.0;
-        for (int b = tid; b < a.stat_blocks; b += kFinThreads) s += (double)a.stat_part[(int64_t)b * kStatRow + v];
+        for (int b0 = 0; b0 < a.stat_blocks; b0 += 16 * kFinThreads) {
+            float vals[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int bb = b0 + u * kFinThreads + tid;
+                vals[u] = a.stat_part[(int64_t)(bb < a.stat_blocks ? bb : 0) * kStatRow + v];
+            }
+            if (b0 == 0) table_slice();
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (b0 + u * kFinThreads + tid < a.stat_blocks) s += (double)vals[u];
+        }
         red[tid] = s;
         __syncthreads();
         for (int h = kFinThreads / 2; h > 0; h >>= 1) {
@@ -762,29 +781,32 @@ __global__ __launch_bounds__(kFinThreads) void swap_reduce_kernel(FinArgs a) {
             __syncthreads();
         }
         if (tid == 0) a.tot[v] = red[0];
-    } else {
+    } else if (v < NS + kTypes) {
+        // rows gq, gq + 4, ... of type t, entry e
         const int t = v - NS, e = tid & 255, gq = tid >> 8;
         const int cnt = a.shell_count[t];
         const float* src = a.shell_part + (int64_t)a.shell_first[t] * 256 + e;
         const int64_t step = (int64_t)a.shell_stride * 256;
         double s = 0.0;
-        for (int j0 = gq; j0 < cnt; j0 += 4 * 8) {
-            float vals[8];
+        for (int j0 = gq; j0 < cnt; j0 += 4 * 16) {
+            float vals[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 16; ++u) {
                 const int j = j0 + 4 * u;
                 vals[u] = src[(j < cnt ? j : 0) * step];
             }
+            if (j0 == gq) table_slice();
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < 16; ++u)
                 if (j0 + 4 * u < cnt) s += (double)vals[u];
         }
+        if (gq >= cnt) table_slice();
         red[tid] = s;
         __syncthreads();
         if (tid < 256) a.tot[NS + t * 256 + tid] = ((red[tid] + red[tid + 256]) + red[tid + 512]) + red[tid + 768];
-    }
-    if (v == 0) {
+    } else {
         copy_batched(wl, a.w, C * a.Cout * 27, tid, kFinThreads);
+        table_slice();
         __syncthreads();
         build_wp(wl, a.Cin, a.Cout, a.Kp, a.Np, a.wp, tid, kFinThreads);
     }
@@ -800,20 +822,52 @@ __global__ __launch_bounds__(kFinThreads) void swap_contract_kernel(FinArgs a) {
     __shared__ double mr[kMaxM];
     __shared__ double sr[kMaxS];
     __shared__ int tw[kMaxS], ecls[kMaxS], eidx[kMaxS], mf[kMaxS];
+    __shared__ double wd[kMaxCout][kMaxS];  // weight of class entry e for output channel oc
     __shared__ double tl[n_stat(kMaxCin) + kTypes * 256];
     const int tid = threadIdx.x;
     const int C = a.Cin, NS = n_stat(C);
     const int Mtot = C * C * 125, Stot = C * 27, E = Mtot + Stot;
     const int Cout = a.Cout;
-    copy_batched(wl, a.w, C * Cout * 27, tid, kFinThreads);
-    copy_batched(tl, a.tot, NS + kTypes * 256, tid, kFinThreads);
+    // every global load of the kernel at once: weights, totals and this
+    // thread's (at most two) rows of the index table
+    constexpr int kWPer = (kMaxCin * kMaxCout * 27 + kFinThreads - 1) / kFinThreads;
+    constexpr int kTPer = (n_stat(kMaxCin) + kTypes * 256 + kFinThreads - 1) / kFinThreads;
+    static_assert(kMaxM + kMaxS <= 2 * kFinThreads, "two table rows per thread");
+    const int nw = C * Cout * 27, nt = NS + kTypes * 256;
+    float wv[kWPer];
+    double tv[kTPer];
+    int t9[2][9];
+#pragma unroll
+    for (int u = 0; u < kWPer; ++u) {
+        const int i = u * kFinThreads + tid;
+        wv[u] = a.w[i < nw ? i : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kTPer; ++u) {
+        const int i = u * kFinThreads + tid;
+        tv[u] = a.tot[i < nt ? i : 0];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int e = h * kFinThreads + tid;
+#pragma unroll
+        for (int k = 0; k < 9; ++k) t9[h][k] = a.tab[(e < E ? e : 0) * 9 + k];
+    }
+#pragma unroll
+    for (int u = 0; u < kWPer; ++u)
+        if (u * kFinThreads + tid < nw) wl[u * kFinThreads + tid] = wv[u];
+#pragma unroll
+    for (int u = 0; u < kTPer; ++u)
+        if (u * kFinThreads + tid < nt) tl[u * kFinThreads + tid] = tv[u];
     __syncthreads();
-    for (int e = tid; e < E; e += kFinThreads) {
-        const int* t9 = a.tab + e * 9;
-        double val = tl[t9[0]];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int e = h * kFinThreads + tid;
+        if (e >= E) continue;
+        double val = tl[t9[h][0]];
 #pragma unroll
         for (int k = 1; k < 9; ++k) {
-            const int q = t9[k];
+            const int q = t9[h][k];
             if (q >= 0) val -= tl[q];
         }
         if (e < Mtot) {
@@ -846,11 +900,18 @@ __global__ __launch_bounds__(kFinThreads) void swap_contract_kernel(FinArgs a) {
     // the output channel, mf[e] the first M entry of its row
     for (int it = tid; it < Cout * Stot; it += kFinThreads) {
         const int oc = it / Stot, e = it % Stot;
+        wd[oc][e] = (double)wl[tw[e] + oc * 27];
+    }
+    __syncthreads();
+    for (int it = tid; it < Cout * Stot; it += kFinThreads) {
+        const int oc = it / Stot, e = it % Stot;
         const int r = ecls[e], nr = C << __popc(r), i = eidx[e];
-        const double wi = (double)wl[tw[e] + oc * 27];
         const int e0 = e - i;  // first entry of the class
+        const double* wrow = wd[oc] + e0;
+        const double* mrow = mr + mf[e0] + i * nr;
         double acc = 0.0;
-        for (int j = 0; j < nr; ++j) acc += (double)wl[tw[e0 + j] + oc * 27] * mr[mf[e0] + i * nr + j];
+        for (int j = 0; j < nr; ++j) acc += wrow[j] * mrow[j];
+        const double wi = wd[oc][e];
         part[oc][e][0] = wi * sr[e];
         part[oc][e][1] = wi * acc;
     }
@@ -1155,7 +1216,7 @@ SwapPlan plan_swap(const PoolGeom& pg, const void* x, bool eval) {
     const size_t shell_rows = sp.shell_lds ? (size_t)g.N * kTypes : (size_t)nb;
     // finalize
     fn.stat_blocks = sp.stat_blocks;
-    sp.fin_blocks = n_stat(C) + kTypes;
+    sp.fin_blocks = n_stat(C) + kTypes + 1;
     fn.Cin = C;
     fn.Cout = Cout;
     for (int j = 0; j < 3; ++j) fn.S[j] = S[j];
@@ -1186,7 +1247,7 @@ void launch_training(const SwapPlan& sp, hipStream_t s) {
     else
         hipLaunchKernelGGL((swap_stats_kernel<CIN, false>), dim3((unsigned)sp.stat_blocks), dim3(kThreads), 0, s, sp.st);
     if (sp.shell_lds)
-        hipLaunchKernelGGL(swap_shell_lds_kernel<CIN>, dim3((unsigned)sp.shell_blocks), dim3(kThreads), 0, s, sp.sh);
+        hipLaunchKernelGGL(swap_shell_lds_kernel<CIN>, dim3((unsigned)sp.shell_blocks), dim3(kShellThreads), 0, s, sp.sh);
     else
         hipLaunchKernelGGL(swap_shell_global_kernel<CIN>, dim3((unsigned)sp.shell_blocks), dim3(kThreads), 0, s, sp.sh);
     hipLaunchKernelGGL(swap_reduce_kernel, dim3((unsigned)sp.fin_blocks), dim3(kFinThreads), 0, s, sp.fin);
