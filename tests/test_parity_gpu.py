@@ -461,6 +461,8 @@ SWAP_MEDIUM = {
     "cin2_cout32": W.CONFIGS["c4"].with_(x_shape=(2, 2, 5, 7, 11), cout=32),
     "exact_windows": W.CONFIGS["c4"].with_(x_shape=(2, 3, 16, 16, 16)),
     "tiny": W.CONFIGS["c4"].with_(x_shape=(1, 3, 3, 3, 4), cout=7),
+    # faces too large for LDS: the boundary Gram matrices read x directly
+    "wide_faces": W.CONFIGS["c4"].with_(x_shape=(1, 3, 3, 70, 66), cout=9),
 }
 
 

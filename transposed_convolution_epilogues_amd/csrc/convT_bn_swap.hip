@@ -288,13 +288,12 @@ __device__ __forceinline__ void stat_rows(const float* A, const float* B, float*
 }
 
 template <int CIN, bool FAST>
-__global__ __launch_bounds__(kThreads) void swap_stats_kernel(StatArgs a) {
+__device__ __forceinline__ void stats_block(const StatArgs& a, float* lds, int blk) {
     constexpr int NS = n_stat(CIN);
     constexpr int NA = reduce_width<CIN>();
     constexpr int kSlot = CIN * kChS;
-    __shared__ __attribute__((aligned(16))) float lds[3 * kSlot];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int b = blockIdx.x;
+    int b = blk;
     if ((a.blocks & 7) == 0) b = (b & 7) * (a.blocks >> 3) + (b >> 3);  // neighbouring slabs on one XCD
     const int t2 = b % a.T2;
     b /= a.T2;
@@ -350,8 +349,14 @@ __global__ __launch_bounds__(kThreads) void swap_stats_kernel(StatArgs a) {
         float s = lds[tid];
 #pragma unroll
         for (int w = 1; w < kThreads / 64; ++w) s += lds[w * NA + tid];
-        a.part[(int64_t)blockIdx.x * kStatRow + tid] = s;
+        a.part[(int64_t)blk * kStatRow + tid] = s;
     }
+}
+
+template <int CIN, bool FAST>
+__global__ __launch_bounds__(kThreads) void swap_stats_kernel(StatArgs a) {
+    __shared__ __attribute__((aligned(16))) float lds[3 * CIN * kChS];
+    stats_block<CIN, FAST>(a, lds, (int)blockIdx.x);
 }
 
 // ----------------------------------------------------------------- shell
@@ -359,15 +364,13 @@ __global__ __launch_bounds__(kThreads) void swap_stats_kernel(StatArgs a) {
 // positions of one type (lane group kq = lane / 16); lane m = lane % 16
 // supplies entry m of the position's patch vector, and the same value serves
 // as both operands, so D accumulates the 16 x 16 Gram matrix.  Every type's
-// partial goes to its own 256-float row; the finalize kernel adds the rows of
+// partial goes to its own 256-float row; the reduce kernel adds the rows of
 // a type (count rows, stride apart).
 //
-// LDS form: one workgroup per (sample, face axis i).  It stages the two input
-// planes x_i = 0 and x_i = S_i - 1 and takes the types whose first non-M
-// coordinate is i (18, 6 and 2 types for i = 0, 1, 2: a partition of the
-// boundary), one type at a time, rows of the type split over the waves.
-// Global form (faces too large for LDS): a wave takes a run of rows of one
-// type and reads x directly.
+// LDS form (workgroups of the statistics kernel, below): the boundary planes
+// staged in LDS, one (sample, face axis, side) per workgroup.  Global form
+// (faces too large for LDS, a kernel of its own): a wave takes a run of rows
+// of one type and reads x directly.
 
 struct ShellArgs {
     const float* x;
@@ -385,7 +388,7 @@ __host__ __device__ inline int type_index(int t0, int t1, int t2) {
     return c < 13 ? c : c - 1;
 }
 
-// LDS layout of the LDS form: slice (side, channel) holds the face plane with
+// LDS layout of the LDS form: slice (channel) holds the face plane with
 // row stride Sb + 1 and slice stride = 8 (mod 64) banks, so the 16 entries x
 // 4 rows of a step fall in distinct banks or on the same word; a row of
 // zeros and a row of ones follow (the lanes of padding entries, of the
@@ -395,23 +398,27 @@ __host__ __device__ inline int shell_cs(int Sa, int Sb) {
     const int sl = Sa * shell_rs(Sb);
     return sl + ((8 - sl) % 64 + 64) % 64;
 }
+
+// The LDS form inside the statistics kernel: a 256-thread workgroup takes
+// one (sample, face axis i): it stages the input planes x_i = 0 and
+// x_i = S_i - 1 and takes the types whose first non-M coordinate is i (18, 6
+// and 2 types for i = 0, 1, 2: a partition of the boundary).  One wave per
+// type, no reduction across waves: the two face types (M, M) on waves 0 and
+// 1, the small types alternating on waves 2 and 3; every wave writes its own
+// partial rows.  (Measured against splitting each face's rows over the four
+// waves, with one workgroup per side: slower.)
 __host__ __device__ inline int shell_lds_floats(int C, int Sa, int Sb) {
-    // slices, 8 words of slack (reads past a row end are discarded), two rows of Sb + 9
-    const int z = 2 * C * shell_cs(Sa, Sb) + 8;
-    return z + 2 * (shell_rs(Sb) + 8) + 128;
+    // slices of both sides, 8 words of slack (reads past a row end are
+    // discarded), zero and ones rows of Sb + 9 with their bank alignment
+    return 2 * C * shell_cs(Sa, Sb) + 8 + 2 * (shell_rs(Sb) + 8) + 128;
 }
-constexpr int kShellLds = 12288;  // floats of the staged planes
-constexpr int kShellThreads = 1024;
 
 template <int CIN>
-__global__ __launch_bounds__(kShellThreads) void swap_shell_lds_kernel(ShellArgs a) {
-    __shared__ __attribute__((aligned(16))) float pl[kShellLds];
-    __shared__ float red[18][4][256];  // up to 18 types per face axis, four waves each
+__device__ void shell_block(const ShellArgs& a, int blk, float* pl) {
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2, wv = wave & 3;  // four groups of four waves
-    const int64_t n = blockIdx.x / 3;
-    const int fi = blockIdx.x % 3;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t n = blk / 3;
+    const int fi = blk % 3;
     const int ad = fi == 0 ? 1 : 0, bd = fi == 2 ? 1 : 2;
     const int S[3] = {a.S[0], a.S[1], a.S[2]};
     const int Sa = S[ad], Sb = S[bd], Si = S[fi];
@@ -419,25 +426,24 @@ __global__ __launch_bounds__(kShellThreads) void swap_shell_lds_kernel(ShellArgs
     const int plane3 = S[0] * S[1] * S[2];
     const float* xn = a.x + n * CIN * (int64_t)plane3;
     const int face = Sa * Sb, RS = shell_rs(Sb), CS = shell_cs(Sa, Sb);
-    // zero and ones rows, placed at banks 24 and 28 (mod 64)
     int zoff = 2 * CIN * CS + 8;
     zoff += ((24 - zoff) % 64 + 64) % 64;
     int ooff = zoff + RS + 8;
     ooff += ((28 - ooff) % 64 + 64) % 64;
-    for (int i = tid; i < RS + 8; i += kShellThreads) {
+    for (int i = tid; i < RS + 8; i += kThreads) {
         pl[zoff + i] = 0.f;
         pl[ooff + i] = 1.f;
     }
-    // stage the slices, twelve independent loads per thread at a time; the
-    // index splits use float reciprocals (exact below 2^22)
+    // stage slices (side, channel), twelve independent loads per thread at a
+    // time; the index splits use float reciprocals (exact below 2^22)
     const int total = 2 * CIN * face;
     const float rface = 1.f / (float)face, rsb = 1.f / (float)Sb;
-    for (int e0 = 0; e0 < total; e0 += 12 * kShellThreads) {
+    for (int e0 = 0; e0 < total; e0 += 12 * kThreads) {
         float v[12];
         int dst[12];
 #pragma unroll
         for (int u = 0; u < 12; ++u) {
-            const int e = e0 + u * kShellThreads + tid;
+            const int e = e0 + u * kThreads + tid;
             const int ec = e < total ? e : total - 1;
             const int sc = (int)(((float)ec + 0.5f) * rface), idx = ec - sc * face;
             const int ia = (int)(((float)idx + 0.5f) * rsb), ib = idx - ia * Sb;
@@ -450,19 +456,17 @@ __global__ __launch_bounds__(kShellThreads) void swap_shell_lds_kernel(ShellArgs
             if (dst[u] >= 0) pl[dst[u]] = v[u];
     }
     __syncthreads();
+    // a type's positions form an na x nb grid; a step takes 4 rows (lane group
+    // kq = row within the group) at one column, so within a row group the LDS
+    // reads are immediate offsets
     const int m = lane & 15, kq = lane >> 4;
-    // types: side (L or H on axis fi), classes of a and b (only M below the
-    // face axis).  A type's positions form an na x nb grid; a step takes 4
-    // rows (lane group kq = row within the group) at one column, so within a
-    // row group the LDS reads are immediate offsets.  Type slot s goes to wave
-    // group s % 4, whose four waves take its row groups in turn, the first
-    // rotating per type; each wave leaves its partial in LDS: one barrier,
-    // then the sums.
-    int slot = 0;
+    int small = 0;
     for (int side = 0; side < 2; ++side)
         for (int ta = (ad < fi ? 1 : 0); ta <= (ad < fi ? 1 : 2); ++ta)
-            for (int tb = (bd < fi ? 1 : 0); tb <= (bd < fi ? 1 : 2); ++tb, ++slot) {
-                if ((slot & 3) != grp) continue;  // uniform per wave
+            for (int tb = (bd < fi ? 1 : 0); tb <= (bd < fi ? 1 : 2); ++tb) {
+                const bool big = ta == 1 && tb == 1;
+                const int owner = big ? side : 2 + ((small++) & 1);
+                if (owner != wv) continue;  // uniform per wave
                 const int nM = (ta == 1) + (tb == 1);
                 const int na = ta == 1 ? Sa - 1 : 1, nb = tb == 1 ? Sb - 1 : 1;
                 const bool real = m < (CIN << nM);
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(kShellThreads) void swap_shell_lds_kernel(ShellArgs
                 }
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 const int groups = na > 0 && nb > 0 ? (na + 3) >> 2 : 0;
-                for (int g = (wv - (slot >> 2)) & 3; g < groups; g += 4) {
+                for (int g = 0; g < groups; ++g) {
                     const int row = 4 * g + kq;
                     const bool rok = row < na;
                     const float* src = pl + (real && rok ? base + row * RS : (one_lane(m) && rok ? ooff : zoff));
@@ -491,25 +495,29 @@ __global__ __launch_bounds__(kShellThreads) void swap_shell_lds_kernel(ShellArgs
                             if (v0 + u < nb) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(e[u], e[u], acc, 0, 0, 0);
                     }
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) red[slot][wv][(4 * kq + i) * 16 + m] = acc[i];
-            }
-    __syncthreads();
-    slot = 0;
-    for (int side = 0; side < 2; ++side)
-        for (int ta = (ad < fi ? 1 : 0); ta <= (ad < fi ? 1 : 2); ++ta)
-            for (int tb = (bd < fi ? 1 : 0); tb <= (bd < fi ? 1 : 2); ++tb, ++slot) {
                 int tau[3];
                 tau[fi] = side ? 2 : 0;
                 tau[ad] = ta;
                 tau[bd] = tb;
-                if ((slot & 3) != (tid >> 8)) continue;  // thread group s % 4 writes slot s
-                const int e = tid & 255;
-                float sum = red[slot][0][e];
+                float* dst = a.part + ((int64_t)n * kTypes + type_index(tau[0], tau[1], tau[2])) * 256;
 #pragma unroll
-                for (int w = 1; w < 4; ++w) sum += red[slot][w][e];
-                a.part[((int64_t)n * kTypes + type_index(tau[0], tau[1], tau[2])) * 256 + e] = sum;
+                for (int i = 0; i < 4; ++i) dst[(4 * kq + i) * 16 + m] = acc[i];
             }
+}
+
+// The statistics kernel with the LDS-form shell workgroups appended: blocks
+// [0, stat blocks) take statistics, the others one (sample, face axis) each
+// (measured: behind the statistics the shell work fills the tail; in front
+// it delays the statistics workgroups).
+template <int CIN, bool FAST>
+__global__ __launch_bounds__(kThreads) void swap_stats_shell_kernel(StatArgs a, ShellArgs sh) {
+    constexpr int kSlot = CIN * kChS;
+    __shared__ __attribute__((aligned(16))) float lds[3 * kSlot];
+    if ((int)blockIdx.x >= a.blocks) {
+        shell_block<CIN>(sh, (int)blockIdx.x - a.blocks, lds);
+        return;
+    }
+    stats_block<CIN, FAST>(a, lds, (int)blockIdx.x);
 }
 
 template <int CIN>
@@ -1176,10 +1184,10 @@ SwapPlan plan_swap(const PoolGeom& pg, const void* x, bool eval) {
     // shell: the LDS form when every face fits, else runs of rows per wave
     ShellArgs& sh = sp.sh;
     for (int j = 0; j < 3; ++j) sh.S[j] = S[j];
-    sp.shell_lds = true;
+    sp.shell_lds = true;  // the LDS form, merged into the statistics kernel
     for (int i = 0; i < 3; ++i) {
         const int ad = i == 0 ? 1 : 0, bd = i == 2 ? 1 : 2;
-        if ((int64_t)S[ad] * (S[bd] + 1) > kShellLds || shell_lds_floats(C, S[ad], S[bd]) > kShellLds)
+        if ((int64_t)S[ad] * (S[bd] + 1) > 3 * C * kChS || shell_lds_floats(C, S[ad], S[bd]) > 3 * C * kChS)
             sp.shell_lds = false;
     }
     FinArgs& fn = sp.fin;
@@ -1242,13 +1250,18 @@ SwapPlan plan_swap(const PoolGeom& pg, const void* x, bool eval) {
 
 template <int CIN>
 void launch_training(const SwapPlan& sp, hipStream_t s) {
-    if (sp.fast_stats)
+    if (sp.shell_lds) {
+        const unsigned nb = (unsigned)(sp.stat_blocks + sp.shell_blocks);
+        if (sp.fast_stats)
+            hipLaunchKernelGGL((swap_stats_shell_kernel<CIN, true>), dim3(nb), dim3(kThreads), 0, s, sp.st, sp.sh);
+        else
+            hipLaunchKernelGGL((swap_stats_shell_kernel<CIN, false>), dim3(nb), dim3(kThreads), 0, s, sp.st, sp.sh);
+    } else if (sp.fast_stats) {
         hipLaunchKernelGGL((swap_stats_kernel<CIN, true>), dim3((unsigned)sp.stat_blocks), dim3(kThreads), 0, s, sp.st);
-    else
+    } else {
         hipLaunchKernelGGL((swap_stats_kernel<CIN, false>), dim3((unsigned)sp.stat_blocks), dim3(kThreads), 0, s, sp.st);
-    if (sp.shell_lds)
-        hipLaunchKernelGGL(swap_shell_lds_kernel<CIN>, dim3((unsigned)sp.shell_blocks), dim3(kShellThreads), 0, s, sp.sh);
-    else
+    }
+    if (!sp.shell_lds)
         hipLaunchKernelGGL(swap_shell_global_kernel<CIN>, dim3((unsigned)sp.shell_blocks), dim3(kThreads), 0, s, sp.sh);
     hipLaunchKernelGGL(swap_reduce_kernel, dim3((unsigned)sp.fin_blocks), dim3(kFinThreads), 0, s, sp.fin);
     hipLaunchKernelGGL(swap_contract_kernel, dim3(1), dim3(kFinThreads), 0, s, sp.fin);
