@@ -826,7 +826,6 @@ __global__ __launch_bounds__(kFinThreads) void swap_contract_kernel(FinArgs a) {
     constexpr int kMaxM = kMaxCin * kMaxCin * 125;
     constexpr int kMaxS = kMaxCin * 27;
     __shared__ float wl[kMaxCin * kMaxCout * 27];
-    __shared__ double part[kMaxCout][kMaxS][2];
     __shared__ double mr[kMaxM];
     __shared__ double sr[kMaxS];
     __shared__ int tw[kMaxS], ecls[kMaxS], eidx[kMaxS], mf[kMaxS];
@@ -911,29 +910,32 @@ __global__ __launch_bounds__(kFinThreads) void swap_contract_kernel(FinArgs a) {
         wd[oc][e] = (double)wl[tw[e] + oc * 27];
     }
     __syncthreads();
-    for (int it = tid; it < Cout * Stot; it += kFinThreads) {
-        const int oc = it / Stot, e = it % Stot;
-        const int r = ecls[e], nr = C << __popc(r), i = eidx[e];
-        const int e0 = e - i;  // first entry of the class
-        const double* wrow = wd[oc] + e0;
-        const double* mrow = mr + mf[e0] + i * nr;
-        double acc = 0.0;
-        for (int j = 0; j < nr; ++j) acc += wrow[j] * mrow[j];
-        const double wi = wd[oc][e];
-        part[oc][e][0] = wi * sr[e];
-        part[oc][e][1] = wi * acc;
-    }
-    __syncthreads();
-    // a wave per channel adds its items: lane l the items l, l + 64, then a
-    // fixed butterfly
+    // a wave per channel: lane l takes the items l and l + 64 (the inner sum
+    // runs over at most 8 C entries, unrolled with its loads together), then
+    // a fixed butterfly adds the lanes
+    constexpr int kMaxRow = 8 * kMaxCin;
+    static_assert(kMaxS <= 128, "two items per lane");
     for (int oc0 = 0; oc0 < Cout; oc0 += kFinThreads / 64) {
         const int oc = oc0 + (tid >> 6), l = tid & 63;
         double s1 = 0.0, s2 = 0.0;
-        if (oc < Cout)
-            for (int e = l; e < Stot; e += 64) {
-                s1 += part[oc][e][0];
-                s2 += part[oc][e][1];
+        if (oc < Cout) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int e = l + 64 * h;
+                if (e >= Stot) continue;
+                const int r = ecls[e], nr = C << __popc(r), i = eidx[e];
+                const int e0 = e - i;  // first entry of the class
+                const double* wrow = wd[oc] + e0;
+                const double* mrow = mr + mf[e0] + i * nr;
+                double acc = 0.0;
+#pragma unroll
+                for (int j = 0; j < kMaxRow; ++j)
+                    if (j < nr) acc += wrow[j] * mrow[j];
+                const double wi = wd[oc][e];
+                s1 += wi * sr[e];
+                s2 += wi * acc;
             }
+        }
         for (int off = 32; off > 0; off >>= 1) {
             s1 += __shfl_xor(s1, off, 64);
             s2 += __shfl_xor(s2, off, 64);
