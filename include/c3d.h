@@ -194,14 +194,15 @@ c3d_status convT_bn_avgpool_ex(const float* x, const int64_t x_shape[5], const f
  * the first call on a device looks up that device's copy of the array.
  *   stream   must belong to the current device (else C3D_ERR_PARAM).
  *   Errors   as convT_bn_avgpool; C3D_ERR_SCRATCH_LIMIT when the arguments
- *            need more than C3D_NOALLOC_SCRATCH_BYTES of partials (64 x 16
- *            channels x 63^3 outputs need 256 KiB on the default kernel);
+ *            need more than C3D_NOALLOC_SCRATCH_BYTES of partials (the
+ *            module on x[64,3,32,32,32] with 16 channels needs 2.07 MB with
+ *            the sums swapped, 256 KiB on the output-phase kernel);
  *            nothing is launched then.
  * All calls on one GPU share its scratch, which keeps the last call's
  * partials: calls that overlap in time on one GPU (other streams, other
  * threads) race and must be serialised by the caller.  Nothing in the
- * scratch needs to start at zero: phase 1 writes every partial phase 2
- * reads. */
+ * scratch needs to start at zero: every kernel of the call writes each
+ * value that a later one reads. */
 c3d_status convT_bn_avgpool_noalloc(const float* x, const int64_t x_shape[5], const float* w, int64_t cout,
                                     const c3d_conv_params* p, const float* conv_bias, const float* gamma,
                                     const float* beta, float eps, int32_t pool, float* y, float* batch_mean,

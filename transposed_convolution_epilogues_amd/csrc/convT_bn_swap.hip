@@ -21,8 +21,8 @@
 //      sum_E t_r^2 = sum_{a,b} w_a w_b L_{c_a c_b}(delta_b - delta_a)
 //    with L_{cc'}(D) = sum_u x_c(u) x_c'(u + D) the lag correlation over the
 //    natural range.  Lag 0 (pairs c <= c'), the 13 lags of a half-space and
-//    the channel sums are 126 values for 3 channels (swap_stats_kernel, on
-//    the vector ALUs).
+//    the channel sums are 126 values for 3 channels (stats_block, on the
+//    vector ALUs).
 // 3. E holds more than the real outputs of class r: a coordinate at -1, or
 //    at S - 1 in a residue-1 dim, is outside the transposed conv.  Split E by
 //    type tau in {L, M, H}^3 (q_i = -1, 0 <= q_i <= S_i - 2, q_i = S_i - 1).
@@ -31,7 +31,9 @@
 //    vector v(q) (3 channels x 2^(number of M dims) entries).  The Gram
 //    matrix Q_tau = sum v v^T (with a constant entry 1 appended, giving the
 //    sums and the count) over the 26 boundary types is one 16x16 matrix-core
-//    product per type and block of positions (swap_shell_kernel); the
+//    product per type and block of positions (shell_block, run as extra
+//    workgroups of swap_stats_shell_kernel when a sample's faces fit in its
+//    LDS, else swap_shell_global_kernel); the
 //    outputs outside the conv are those of the types with an L only in
 //    residue-1 dims and an L or H in at least one of them, and their sums
 //    are w_r^T Q_tau w_r.
