@@ -235,7 +235,9 @@ const char* c3d_status_str(c3d_status status);
  * atomics within one tap offset because the input-to-output map is
  * injective there; LDS-bound, the second algorithm to compare against),
  * 5 = as 0 but convT_bn_avgpool uses its one-thread-per-cell fp32 kernel
- * (C3D_ALGO_BN_CELLS).
+ * (C3D_ALGO_BN_CELLS), 6 = as 0 but conv_transpose3d_fwd takes the
+ * one-phase-per-workgroup kernel (C3D_ALGO_PHASE) wherever it applies, for
+ * A/B against the kernel that shares a staged halo among the phases.
  * Returns the previous value.  The setting belongs to the calling thread
  * (thread-local): other threads keep their own, starting at 0. */
 int c3d_set_variant(int variant);
@@ -262,18 +264,22 @@ enum {
     C3D_ALGO_BN_CELLS = 5,   /* convT_bn_avgpool, k3 s2 p1 pool 4: a thread per 4^3 cell */
     C3D_ALGO_BN_SWAP = 6,    /* convT_bn_avgpool, k3 s2 p1 pool 4: swapped sums        */
     C3D_ALGO_SCATTER = 7,    /* conv_transpose3d: scatter into an LDS output tile      */
-    C3D_ALGO_BN_MFMA = 8     /* convT_bn_avgpool, k3 s2 p1 pool 4: output phases on MFMA */
+    C3D_ALGO_BN_MFMA = 8,    /* convT_bn_avgpool, k3 s2 p1 pool 4: output phases on MFMA */
+    C3D_ALGO_PHASE_GROUP = 9 /* conv_transpose3d, strided: every output phase of a tile
+                                from one staged halo, on MFMA                          */
 };
 
 /* Writes the C3D_ALGO_* code conv3d_fwd would use to *algo; returns the
  * validation status conv3d_fwd would return (nothing is written on error). */
 c3d_status c3d_conv3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo);
 
-/* The same for conv_transpose3d_fwd.  The phase path ("Kimi-K2.6 l1_p77",
+/* The same for conv_transpose3d_fwd.  The phase paths ("Kimi-K2.6 l1_p77",
  * the residue classes of o mod s, each a stride-1 correlation with its own
- * taps) applies when every stride is at most 4, every residue class has at
- * most 3 taps per dim whose input offsets span at most 3 positions, and
- * Cin/groups >= 4, Cout/groups >= 8. */
+ * taps) apply when every stride is at most 4, every residue class has at
+ * most 3 taps per dim, and Cin/groups >= 4, Cout/groups >= 8.
+ * C3D_ALGO_PHASE_GROUP (the default) needs the input offsets of all residues
+ * of a dim together to span at most 3 positions and at most 64 kernel taps;
+ * C3D_ALGO_PHASE needs the span per residue only. */
 c3d_status c3d_conv_transpose3d_algo(const int64_t x_shape[5], int64_t cout, const c3d_conv_params* p, int32_t* algo);
 
 /* The same for convT_bn_avgpool and convT_bn_avgpool_ex.  The default for

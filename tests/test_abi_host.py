@@ -365,13 +365,16 @@ ALGO_CASES = [
     ("conv3d", (1, 8, 8, 8, 8), 8, 3, 2, 1, 1, 0, 1, 0, "direct"),                      # strided
     ("conv3d", (16, 3, 256, 256, 10), 64, (3, 3, 1), 1, 0, 1, 0, 1, 1, "direct"),       # forced generic
     ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 0, "sublattice"),  # c3
-    ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 2, "phase"),       # c3, general path
-    ("conv_transpose3d", (1, 8, 4, 4, 4), 1025, 3, 2, 1, 2, 0, 1, 0, "phase"),          # bias table limit
+    ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 2, "phase_group"), # c3, general path
+    ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 6, "phase"),       # one phase per workgroup
+    ("conv_transpose3d", (1, 8, 4, 4, 4), 1025, 3, 2, 1, 2, 0, 1, 0, "phase_group"),    # 33 channel blocks
     ("conv_transpose3d", (16, 32, 16, 32, 32), 64, 3, 2, 1, 2, 0, 1, 1, "direct"),
-    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 2, 1, 1, 1, 1, 0, "phase"),           # dense phases
-    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 4, 2, 1, 1, 0, 1, 0, "phase"),
-    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 3, 1, 1, 2, 2, 0, "phase"),           # s3, groups
-    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 1, 1, 1, 0, 1, 0, "phase"),           # stride 1
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 2, 1, 1, 1, 1, 0, "phase_group"),     # dense phases
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 2, 1, 1, 1, 1, 6, "phase"),
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 4, 2, 1, 1, 0, 1, 0, "phase_group"),
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 3, 1, 1, 2, 2, 0, "phase_group"),     # s3, groups
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 1, 1, 1, 0, 1, 0, "phase_group"),     # stride 1
+    ("conv_transpose3d", (2, 16, 8, 8, 8), 32, (5, 5, 3), 2, (2, 2, 1), 1, 0, 1, 0, "phase"),  # 75 taps > 64
     ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 5, 1, 1, 0, 1, 0, "direct"),          # stride > 4
     ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 7, 2, 1, 1, 0, 1, 0, "direct"),          # 4 taps per residue
     ("conv_transpose3d", (2, 16, 8, 8, 8), 32, 3, 1, 1, 2, 0, 1, 0, "direct"),          # offsets span 4

@@ -135,8 +135,9 @@ def test_random_small_shapes(op, variant):
 
 # ------------------------------------- transposed conv, per-phase MFMA path
 def _phase_cases(n, seed):
-    """Random transposed convs that take the per-phase MFMA kernel: strides
-    1..4, kernels 1..5, dilation 1..3, output padding, groups 1/2."""
+    """Random transposed convs that take a phase kernel (the shared-halo one
+    or the per-phase one): strides 1..4, kernels 1..5, dilation 1..3, output
+    padding, groups 1/2."""
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
@@ -152,16 +153,34 @@ def _phase_cases(n, seed):
         if not _valid(wl):
             continue
         if B.conv_transpose3d_algo(wl.x_shape, wl.cout, B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation,
-                                                                      wl.output_pad, wl.groups)) != "phase":
+                                                                      wl.output_pad, wl.groups)) not in PHASE_ALGOS:
             continue
         out.append(wl)
     return out
 
 
-def test_convT_phase_random():
-    for i, wl in enumerate(_phase_cases(30, 71)):
-        print(f"[convT phase] case {i}: {wl}", flush=True)
-        check_full(wl, W.make_inputs(wl), f"convT phase #{i}")
+PHASE_ALGOS = ("phase_group", "phase")
+# variant 0 takes the shared-halo kernel where it applies; variant 6 the
+# one-phase-per-workgroup kernel
+PHASE_VARIANTS = {"shared_halo": 0, "per_phase": 6}
+
+
+@pytest.mark.parametrize("pv", list(PHASE_VARIANTS))
+def test_convT_phase_random(pv):
+    cases = _phase_cases(30, 71)
+    old = B.set_variant(PHASE_VARIANTS[pv])
+    try:
+        seen = set()
+        for i, wl in enumerate(cases):
+            p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+            algo = B.conv_transpose3d_algo(wl.x_shape, wl.cout, p)
+            assert algo in PHASE_ALGOS, algo
+            seen.add(algo)
+            print(f"[convT phase {pv} {algo}] case {i}: {wl}", flush=True)
+            check_full(wl, W.make_inputs(wl), f"convT phase #{i}")
+        assert seen == ({"phase"} if pv == "per_phase" else {"phase_group", "phase"}), seen
+    finally:
+        B.set_variant(old)
 
 
 PHASE_MEDIUM = {
@@ -178,29 +197,40 @@ PHASE_MEDIUM = {
 }
 
 
+@pytest.mark.parametrize("pv", list(PHASE_VARIANTS))
 @pytest.mark.parametrize("name", list(PHASE_MEDIUM))
-def test_convT_phase_medium(name):
-    """Per-phase MFMA path on multi-tile shapes; variant 2 makes the
-    stride-2 dilation-2 case take it instead of the sub-lattice kernel."""
+def test_convT_phase_medium(name, pv):
+    """Both phase kernels on multi-tile shapes; variant 2 makes the stride-2
+    dilation-2 case take the shared-halo kernel instead of the sub-lattice
+    one, variant 6 the per-phase kernel."""
     wl = PHASE_MEDIUM[name]
-    old = B.set_variant(2)
+    old = B.set_variant(2 if pv == "shared_halo" else 6)
     try:
         algo = B.conv_transpose3d_algo(wl.x_shape, wl.cout, B.make_params(wl.kernel, wl.stride, wl.pad,
                                                                            wl.dilation, wl.output_pad, wl.groups))
-        assert algo == "phase", algo
+        assert algo == ("phase_group" if pv == "shared_halo" else "phase"), algo
         print(f"[convT phase medium {name}] {wl}", flush=True)
         check_full(wl, W.make_inputs(wl), name)
     finally:
         B.set_variant(old)
 
 
+@pytest.mark.parametrize("pv", list(PHASE_VARIANTS))
 @pytest.mark.parametrize("key", list(W.WIDEN))
-def test_convT_widen_full_size_sampled(key):
-    """The transposed convs `bench.py --widen` times, at full size through the
-    automatic kernel (the per-phase path), on sampled outputs."""
+def test_convT_widen_full_size_sampled(key, pv):
+    """The transposed convs `bench.py --widen` times, at full size through
+    both phase kernels, on sampled outputs."""
     wl = W.WIDEN[key]
     p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
-    assert B.conv_transpose3d_algo(wl.x_shape, wl.cout, p) == "phase"
+    old = B.set_variant(PHASE_VARIANTS[pv])
+    try:
+        assert B.conv_transpose3d_algo(wl.x_shape, wl.cout, p) == ("phase_group" if pv == "shared_halo" else "phase")
+        _widen_sampled(key, wl)
+    finally:
+        B.set_variant(old)
+
+
+def _widen_sampled(key, wl):
     inp = W.make_inputs(wl)
     print(f"[convT widen {key}] {wl}", flush=True)
     y = run_gpu(wl, inp)

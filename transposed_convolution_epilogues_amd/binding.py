@@ -32,7 +32,7 @@ EXPORTS = ("c3d_conv3d_out_dims", "c3d_conv_transpose3d_out_dims", "c3d_convT_bn
            "c3d_probe_mfma_f32")
 
 ALGO = {0: "direct", 1: "k1last", 2: "mfma333", 3: "sublattice", 4: "phase", 5: "bn_cells", 6: "bn_swap",
-        7: "scatter", 8: "bn_mfma"}
+        7: "scatter", 8: "bn_mfma", 9: "phase_group"}
 
 
 class C3DError(RuntimeError):
@@ -264,7 +264,9 @@ def set_variant(variant: int) -> int:
     3 = automatic, but convT_bn_avgpool's second algorithm (the output-phase classes on
         the matrix cores) where the swapped sums would apply,
     4 = automatic, but conv_transpose3d_fwd scatters into an LDS output tile,
-    5 = automatic, but convT_bn_avgpool runs its one-thread-per-cell fp32 kernel.
+    5 = automatic, but convT_bn_avgpool runs its one-thread-per-cell fp32 kernel,
+    6 = automatic, but conv_transpose3d_fwd runs one output phase per workgroup
+        (the per-phase kernel) wherever it applies.
     The setting is the calling thread's own (the library keeps it thread-local)."""
     return int(_lib().c3d_set_variant(int(variant)))
 

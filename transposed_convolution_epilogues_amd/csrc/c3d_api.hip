@@ -164,8 +164,9 @@ int convT_algo(const Geom& g) {
     const int v = t_variant;
     if (v == 1) return C3D_ALGO_DIRECT;
     if (v == 4 && c3d::convT_scatter_supported(g)) return C3D_ALGO_SCATTER;
-    if (v != 2 && c3d::convT_s2_sublattice_supported(g, nullptr, nullptr, nullptr))
+    if (v != 2 && v != 6 && c3d::convT_s2_sublattice_supported(g, nullptr, nullptr, nullptr))
         return C3D_ALGO_SUBLATTICE;
+    if (v != 6 && c3d::convT_phasegroup_supported(g)) return C3D_ALGO_PHASE_GROUP;
     if (c3d::convT_phase_mfma_supported(g, nullptr, nullptr, nullptr)) return C3D_ALGO_PHASE;
     return C3D_ALGO_DIRECT;
 }
@@ -297,6 +298,7 @@ c3d_status conv_transpose3d_fwd(const float* x, const int64_t x_shape[5], const 
     hipStream_t s = (hipStream_t)stream;
     switch (convT_algo(g)) {
         case C3D_ALGO_SUBLATTICE: return hip_status(c3d::launch_convT_s2_sublattice(x, w, bias, y, g, s));
+        case C3D_ALGO_PHASE_GROUP: return hip_status(c3d::launch_convT_phasegroup(x, w, bias, y, g, s));
         case C3D_ALGO_PHASE: return hip_status(c3d::launch_convT_phase_mfma(x, w, bias, y, g, s));
         case C3D_ALGO_SCATTER: return hip_status(c3d::launch_convT_scatter(x, w, bias, y, g, s));
         default: return hip_status(c3d::launch_convT_gather(x, w, bias, y, g, s));

@@ -94,6 +94,9 @@ hipError_t launch_convT_s2_sublattice(const float* x, const float* w, const floa
 bool convT_phase_mfma_supported(const Geom& g, const void* x, const void* w, const void* y);
 hipError_t launch_convT_phase_mfma(const float* x, const float* w, const float* bias, float* y, const Geom& g,
                                    hipStream_t st);
+bool convT_phasegroup_supported(const Geom& g);
+hipError_t launch_convT_phasegroup(const float* x, const float* w, const float* bias, float* y, const Geom& g,
+                                   hipStream_t st);
 bool convT_scatter_supported(const Geom& g);
 hipError_t launch_convT_scatter(const float* x, const float* w, const float* bias, float* y, const Geom& g,
                                 hipStream_t st);
