@@ -83,7 +83,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=4.0, help="target oracle seconds per workload sample")
-    ap.add_argument("--only", default=",".join(BENCH_KEYS), help="comma-separated subset (profiling runs)")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated subset of the workloads (or, with --widen, of its cases): profiling runs")
+    ap.add_argument("--no-generic", action="store_true",
+                    help="with --widen: skip the generic-kernel comparison (profiling runs)")
     ap.add_argument("--probe-mfma", action="store_true",
                     help="time the library's fp32 matrix-core throughput probe and print its TFLOP/s")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -113,7 +116,7 @@ def main():
     from transposed_convolution_epilogues_amd import binding as B
     from transposed_convolution_epilogues_amd import workloads as W
 
-    keys = [k for k in args.only.split(",") if k]
+    keys = [k for k in (args.only or ",".join(BENCH_KEYS)).split(",") if k]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     B.library()
@@ -351,9 +354,10 @@ def calibrate_copy(torch):
 def widen(torch, args):
     """Work beyond the five configurations, each timed through its automatic
     kernel and through the generic kernels for comparison:
-      - transposed convs on the per-output-phase MFMA path, the c3 module
-        through that general path instead of its sub-lattice kernel, and both
-        through the LDS-scatter algorithm;
+      - transposed convs on the shared-halo phase kernel and on the
+        one-phase-per-workgroup kernel, the c3 module through both general
+        paths instead of its sub-lattice kernel, and both through the
+        LDS-scatter algorithm;
       - the c4 module with BatchNorm in eval mode (running statistics), in
         training mode with the running-statistics update, and through its
         second algorithm (the output-phase classes on the matrix cores)."""
@@ -364,10 +368,15 @@ def widen(torch, args):
     torch.cuda.set_device(dev)
     B.library()
     c4 = W.CONFIGS["c4"]
-    cases = ([(k, wl, 0, "convT") for k, wl in W.WIDEN.items()] + [("c3_phase", W.CONFIGS["c3"], 2, "convT")] +
+    cases = ([(k, wl, 0, "convT") for k, wl in W.WIDEN.items()] +
+             [(k + "_per_phase", wl, 6, "convT") for k, wl in W.WIDEN.items()] +
+             [("c3_phase", W.CONFIGS["c3"], 2, "convT"), ("c3_per_phase", W.CONFIGS["c3"], 6, "convT")] +
              [("t1_scatter", W.WIDEN["t1"], 4, "convT"), ("c3_scatter", W.CONFIGS["c3"], 4, "convT")] +
              [("c4_eval", c4, 0, "bn_eval"), ("c4_train_running", c4, 0, "bn_running"),
               ("c4_phase_classes", c4, 3, "bn_second")])
+    if args.only:
+        sel = set(args.only.split(","))
+        cases = [c for c in cases if c[0] in sel]
     out = {}
     for key, wl, variant, kind in cases:
         inp = W.make_inputs(wl)
@@ -400,7 +409,8 @@ def widen(torch, args):
                                               "bn_running": "; training mode + running-statistics update",
                                               "bn_second": "; output-phase classes on the matrix cores"}[kind],
                    mac=mac, algo_bytes=nbytes)
-        for label, v, reps in (("fast", variant, args.steps), ("generic", 1, 3)):
+        legs = (("fast", variant, args.steps),) + (() if args.no_generic else (("generic", 1, 3),))
+        for label, v, reps in legs:
             old = B.set_variant(v)
             try:
                 row[label + "_algo"] = algo() if v != 1 else "generic"
@@ -424,7 +434,8 @@ def widen(torch, args):
         row["frac_fp32_peak"] = round(row["fast_tflops"] / FP32_PEAK_TFLOPS, 4)
         row["hbm_gbs"] = round(nbytes / (row["fast_ms_median"] * 1e-3) / 1e9, 1)
         row["frac_hbm_peak"] = round(row["hbm_gbs"] / HBM_PEAK_GBS, 4)
-        row["speedup_vs_generic"] = round(row["generic_ms_median"] / row["fast_ms_median"], 2)
+        if "generic_ms_median" in row:
+            row["speedup_vs_generic"] = round(row["generic_ms_median"] / row["fast_ms_median"], 2)
         out[key] = row
         print(f"[bench --widen] {key}: {row}", file=sys.stderr, flush=True)
         del x, w, b, y

@@ -82,6 +82,40 @@ struct GArgs {
     int32_t gres[kMaxGroups][kMaxPh];  // residues of phase p of group g: r0 | r1 << 4 | r2 << 8
 };
 
+// The two common strided layers with the tap structure fixed at compile time
+// (every dim alike, dilation 1): kernel 3, stride 2, padding 1 (the x2
+// upsampling layer, any output padding) and kernel 4, stride 2, padding 1.
+// Per dim, residue r takes the taps k with (r + p - k) even, from input
+// offset (r + p - k) / 2; the LDS offsets then become immediates.
+template <int K, int P>
+struct FixedDim {
+    static constexpr int n(int r) {
+        int c = 0;
+        for (int k = 0; k < K; ++k) c += ((r + P - k) % 2 + 2) % 2 == 0;
+        return c;
+    }
+    static constexpr int dmin() {
+        int m = 1 << 20;
+        for (int r = 0; r < 2; ++r)
+            for (int k = 0; k < K; ++k)
+                if (((r + P - k) % 2 + 2) % 2 == 0 && (r + P - k) / 2 < m) m = (r + P - k) / 2;
+        return m;
+    }
+    static constexpr int k(int r, int i) {
+        for (int k = 0, c = 0; k < K; ++k)
+            if (((r + P - k) % 2 + 2) % 2 == 0 && c++ == i) return k;
+        return 0;
+    }
+    static constexpr int off(int r, int i) { return (r + P - k(r, i)) / 2 - dmin(); }
+};
+// KS: 0 = any geometry (tap table), 1 = k3 s2 p1, 2 = k4 s2 p1
+template <int KS>
+struct Fixed;
+template <>
+struct Fixed<1> : FixedDim<3, 1> {};
+template <>
+struct Fixed<2> : FixedDim<4, 1> {};
+
 template <int ICC, int KV>
 struct Lay {
     static constexpr int kHalf = ICC / 2;  // K-steps per tap
@@ -94,7 +128,7 @@ struct Lay {
     static constexpr int kWPer = (kUnits + kThreads - 1) / kThreads;
 };
 
-template <int ICC, int KV>
+template <int ICC, int KV, int KS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void convT_phasegroup_kernel(
     GArgs a) {
     using L = Lay<ICC, KV>;
@@ -127,7 +161,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int h = lane >> 5, nn = lane & 31;
     const int wr0 = wv / kR1, wr1 = wv % kR1;
 
-    if (tid < a.kvol) taps[tid] = int2{a.tapw[tid], a.tapx[tid]};
+    if (KS == 0 && tid < a.kvol) taps[tid] = int2{a.tapw[tid], a.tapx[tid]};
 
     // ---- staging: halo positions of this thread
     const int64_t plane = (int64_t)a.S[0] * a.S[1] * a.S[2];
@@ -237,41 +271,74 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (more) load(c + 1);
         const float* bw = lds + (c & 1) * L::kBuf + wbase;
         const float* bx = lds + (c & 1) * L::kBuf + xbase;
+        if constexpr (KS != 0) {
+            // every phase and tap unrolled: the operand offsets are immediates,
+            // and a halo window shared by several phases is read once
+            using F = Fixed<KS>;
+            constexpr int kK = KS == 1 ? 3 : 4;
 #pragma unroll
-        for (int p = 0; p < kMaxPh; ++p) {
-            const int beg = a.gbeg[pg][p], end = a.gbeg[pg][p + 1];
-            // four taps per step: their offsets, then all operand reads, then
-            // the products, so the later taps' reads overlap the first tap's
-            // products; the remaining taps one at a time
-            int t = beg;
-            for (; t + 4 <= end; t += 4) {
-                int2 o[4];
-                VA av[4], bv[4];
+            for (int p = 0; p < kMaxPh; ++p) {
+                const int r0 = p >> 2, r1 = (p >> 1) & 1, r2 = p & 1;
 #pragma unroll
-                for (int k = 0; k < 4; ++k) o[k] = taps[t + k];
+                for (int u0 = 0; u0 < F::n(r0); ++u0)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    av[k] = *reinterpret_cast<const VA*>(bw + o[k].x);
-                    bv[k] = *reinterpret_cast<const VA*>(bx + o[k].y);
-                }
+                    for (int u1 = 0; u1 < F::n(r1); ++u1)
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
+                        for (int u2 = 0; u2 < F::n(r2); ++u2) {
+                            const int wo = ((F::k(r0, u0) * kK + F::k(r1, u1)) * kK + F::k(r2, u2)) * L::kWTS;
+                            const int xo = ((F::off(r0, u0) * kHX1 + F::off(r1, u1)) * kHX2 + F::off(r2, u2)) * H;
+                            const VA av = *reinterpret_cast<const VA*>(bw + wo);
+                            const VA bv = *reinterpret_cast<const VA*>(bx + xo);
 #pragma unroll
-                    for (int s = 0; s < H; ++s)
-                        acc[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[k][s], bv[k][s], acc[p], 0, 0, 0);
-                // keep the eight operand reads ahead of the products (the
-                // scheduler otherwise puts each tap's reads right before its
-                // products and waits for them there)
-                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 4 * H, 0);
+                            for (int s = 0; s < H; ++s)
+                                acc[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s], bv[s], acc[p], 0, 0, 0);
+                        }
             }
-            for (; t < end; ++t) {
-                const int2 o = taps[t];
-                const VA av = *reinterpret_cast<const VA*>(bw + o.x);
-                const VA bv = *reinterpret_cast<const VA*>(bx + o.y);
+            // operand reads run ahead of the products: a first batch, then a
+            // few reads behind every tap's products
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-                for (int s = 0; s < H; ++s)
-                    acc[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s], bv[s], acc[p], 0, 0, 0);
+            for (int i = 0; i < KV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, H, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+        } else {
+    #pragma unroll
+            for (int p = 0; p < kMaxPh; ++p) {
+                const int beg = a.gbeg[pg][p], end = a.gbeg[pg][p + 1];
+                // four taps per step: their offsets, then all operand reads, then
+                // the products, so the later taps' reads overlap the first tap's
+                // products; the remaining taps one at a time
+                int t = beg;
+                for (; t + 4 <= end; t += 4) {
+                    int2 o[4];
+                    VA av[4], bv[4];
+    #pragma unroll
+                    for (int k = 0; k < 4; ++k) o[k] = taps[t + k];
+    #pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        av[k] = *reinterpret_cast<const VA*>(bw + o[k].x);
+                        bv[k] = *reinterpret_cast<const VA*>(bx + o[k].y);
+                    }
+    #pragma unroll
+                    for (int k = 0; k < 4; ++k)
+    #pragma unroll
+                        for (int s = 0; s < H; ++s)
+                            acc[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[k][s], bv[k][s], acc[p], 0, 0, 0);
+                    // keep the eight operand reads ahead of the products (the
+                    // scheduler otherwise puts each tap's reads right before its
+                    // products and waits for them there)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4 * H, 0);
+                }
+                for (; t < end; ++t) {
+                    const int2 o = taps[t];
+                    const VA av = *reinterpret_cast<const VA*>(bw + o.x);
+                    const VA bv = *reinterpret_cast<const VA*>(bx + o.y);
+    #pragma unroll
+                    for (int s = 0; s < H; ++s)
+                        acc[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s], bv[s], acc[p], 0, 0, 0);
+                }
             }
         }
         if (more) store(c + 1, lds + ((c + 1) & 1) * L::kBuf);
@@ -465,6 +532,17 @@ bool build_any(const Geom& g, GArgs& a, bool& small) {
     return small ? build_gargs<8, 27>(g, a) : build_gargs<4, 64>(g, a);
 }
 
+// 1: kernel 3, stride 2, padding 1 in every dim; 2: kernel 4, stride 2,
+// padding 1 in every dim (dilation 1 both); 0: other geometries
+int fixed_kind(const Geom& g) {
+    for (int k : {3, 4}) {
+        bool all = true;
+        for (int j = 0; j < 3; ++j) all = all && g.k[j] == k && g.s[j] == 2 && g.p[j] == 1 && g.d[j] == 1;
+        if (all) return k == 3 ? 1 : 2;
+    }
+    return 0;
+}
+
 }  // namespace
 
 bool convT_phasegroup_supported(const Geom& g) {
@@ -488,10 +566,15 @@ hipError_t launch_convT_phasegroup(const float* x, const float* w, const float* 
     if ((a.vecs == 2 && ((uintptr_t)y & 7) != 0) || (a.vecs == 4 && ((uintptr_t)y & 15) != 0)) a.vecs = 0;
     static_assert(sizeof(GArgs) <= 4096, "kernel arguments");
     const unsigned blocks = (unsigned)grid_blocks(g, a);
-    if (small)
-        hipLaunchKernelGGL((convT_phasegroup_kernel<8, 27>), dim3(blocks), dim3(kThreads), 0, st, a);
+    const int fk = fixed_kind(g);
+    if (fk == 1)
+        hipLaunchKernelGGL((convT_phasegroup_kernel<8, 27, 1>), dim3(blocks), dim3(kThreads), 0, st, a);
+    else if (fk == 2)
+        hipLaunchKernelGGL((convT_phasegroup_kernel<4, 64, 2>), dim3(blocks), dim3(kThreads), 0, st, a);
+    else if (small)
+        hipLaunchKernelGGL((convT_phasegroup_kernel<8, 27, 0>), dim3(blocks), dim3(kThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((convT_phasegroup_kernel<4, 64>), dim3(blocks), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((convT_phasegroup_kernel<4, 64, 0>), dim3(blocks), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
