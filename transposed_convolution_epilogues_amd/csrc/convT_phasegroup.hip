@@ -73,6 +73,12 @@ struct GArgs {
     int32_t vecs;             // s2 when dim 2 is free, s2 > 1 and s2 divides O2: a lane's residues
                               // along dim 2 are contiguous and go out in one store; else 0
     int32_t nchunks;
+    int32_t fold;             // 2: rows of at most 16 positions, a wave takes two of them (a half-wave
+                              // each); 1 otherwise (always 1 for the fixed geometries)
+    int32_t hx1, hx2;         // halo layout strides of dims 1 and 2 (positions)
+    int32_t pg_inner;         // more than one phase group and at most two chunks: a workgroup stages
+                              // every input channel once and runs pg_per phase groups
+    int32_t pg_split, pg_per; // with pg_inner: workgroups per tile, phase groups per workgroup
     float inv_e2, inv_e12, inv_kvol;  // reciprocals for the staging index splits
     int64_t x_gstride, w_gstride, y_gstride;
     // tap table: LDS offsets (floats) of each tap's weights and halo window,
@@ -144,8 +150,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
     const int ocb = (int)(b % a.oc_blocks);
     b /= a.oc_blocks;
-    const int pg = (int)(b % a.pgroups);
-    b /= a.pgroups;
+    // the phase group (with pg_inner: the first of the workgroup's pg_per)
+    const int pgn = a.pg_inner ? a.pg_split : a.pgroups;
+    const int pg0 = (int)(b % pgn) * (a.pg_inner ? a.pg_per : 1);
+    b /= pgn;
     const int t2 = (int)(b % a.tiles[2]);
     b /= a.tiles[2];
     const int t1 = (int)(b % a.tiles[1]);
@@ -155,11 +163,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int grp = (int)(b % a.groups);
     const int64_t n = b / a.groups;
     const int oc0 = ocb * kOCB;
-    const int q0 = t0 * kR0, q1 = t1 * kR1, q2 = t2 * kTW;
+    // tile: kR0 x (kR1 fold) rows of kTW / fold positions; lane nn of wave
+    // (wr0, wr1) takes row (wr0, wr1 fold + nn / (kTW / fold)), position
+    // nn % (kTW / fold)
+    const int fold = KS == 0 ? a.fold : 1;
+    const int rw = kTW / fold;
+    const int hx1 = KS == 0 ? a.hx1 : kHX1, hx2 = KS == 0 ? a.hx2 : kHX2;
+    const int q0 = t0 * kR0, q1 = t1 * kR1 * fold, q2 = t2 * rw;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int h = lane >> 5, nn = lane & 31;
     const int wr0 = wv / kR1, wr1 = wv % kR1;
+    const int lr0 = wr0, lr1 = wr1 * fold + nn / rw, lp = nn % rw;
 
     if (KS == 0 && tid < a.kvol) taps[tid] = int2{a.tapw[tid], a.tapx[tid]};
 
@@ -169,7 +184,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int xsp[kHaloPer];  // spatial offset in an input channel plane, -1: zero padding
     int xlp[kHaloPer];  // LDS position, -1: no position
     {
-        const int e2 = kTW + a.ext[2], e12 = (kR1 + a.ext[1]) * e2;
+        const int e2 = rw + a.ext[2], e12 = (kR1 * fold + a.ext[1]) * e2;
         const int cnt = (kR0 + a.ext[0]) * e12;
 #pragma unroll
         for (int u = 0; u < kHaloPer; ++u) {
@@ -179,7 +194,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int g0 = q0 - a.org[0] + c0, g1 = q1 - a.org[1] + c1, g2 = q2 - a.org[2] + c2;
             const bool in = hp < cnt && g0 >= 0 && g0 < a.S[0] && g1 >= 0 && g1 < a.S[1] && g2 >= 0 && g2 < a.S[2];
             xsp[u] = in ? (g0 * a.S[1] + g1) * a.S[2] + g2 : -1;
-            xlp[u] = hp < cnt ? (c0 * kHX1 + c1) * kHX2 + c2 : -1;
+            xlp[u] = hp < cnt ? (c0 * hx1 + c1) * hx2 + c2 : -1;
         }
     }
     // ---- staging: weight units (half hh, channel oc, tap) of this thread,
@@ -261,16 +276,61 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // this lane's operand bases: weights of channel row nn, halo at its position
     const int wbase = L::kXF + (h * kOCB + nn) * H;
-    const int xbase = (h * kHPos + (wr0 * kHX1 + wr1) * kHX2 + nn) * H;
+    const int xbase = (h * kHPos + (lr0 * hx1 + lr1) * hx2 + lp) * H;
 
-    load(0);
-    store(0, lds);
-    __syncthreads();
-    for (int c = 0; c < a.nchunks; ++c) {
-        const bool more = c + 1 < a.nchunks;
-        if (more) load(c + 1);
-        const float* bw = lds + (c & 1) * L::kBuf + wbase;
-        const float* bx = lds + (c & 1) * L::kBuf + xbase;
+    // ---- epilogue: a lane holds position q2 + nn and channels
+    // oc0 + 8(i/4) + 4h + i%4; the channel offsets are uniform multiples of
+    // the channel stride, added to one row pointer per phase
+    const int64_t O1 = a.O[1], O2 = a.O[2];
+    const int64_t cst = (int64_t)a.O[0] * O1 * O2;  // floats between output channels
+    const int p0 = q0 + lr0, p1 = q1 + lr1, pq = q2 + lp;
+    const bool all_oc = oc0 + kOCB <= a.cout;       // uniform
+    float* yb = a.y + (int64_t)grp * a.y_gstride + (n * a.yC + oc0 + 4 * h) * cst;
+    auto load_bias = [&](float (&bs)[16]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int oc = oc0 + 8 * (i >> 2) + 4 * h + (i & 3);
+            bs[i] = (a.bias && oc < a.cout) ? a.bias[(int64_t)grp * a.cout + oc] : 0.f;
+        }
+    };
+    auto epilogue = [&](int pg, const float (&bs)[16]) {
+        const int vs = a.vecs;
+#pragma unroll
+        for (int p = 0; p < kMaxPh; ++p) {
+            if (p >= a.P) break;
+            if (vs && p % vs != 0) continue;
+            const int res = a.gres[pg][p];
+            const int r0 = res & 15, r1 = (res >> 4) & 15, r2 = res >> 8;
+            if (p0 >= a.Q[0][r0] || p1 >= a.Q[1][r1]) continue;
+            const int64_t row = ((int64_t)(a.s[0] * p0 + r0) * O1 + (a.s[1] * p1 + r1)) * O2;
+            // the residues of dim 2 are phases p .. p + vs - 1 when vs > 1
+            if (pq >= a.Q[2][vs ? 0 : r2]) continue;
+            float* rp = yb + row + (vs ? (int64_t)vs * pq : (int64_t)a.s[2] * pq + r2);
+            const int q1i = (p + 1) & (kMaxPh - 1), q2i = (p + 2) & (kMaxPh - 1), q3i = (p + 3) & (kMaxPh - 1);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (!all_oc && oc0 + 8 * (i >> 2) + 4 * h + (i & 3) >= a.cout) continue;
+                float* dst = rp + (8 * (i >> 2) + (i & 3)) * cst;
+                if (vs == 2) {
+                    *reinterpret_cast<f32x2*>(dst) = f32x2{acc[p][i] + bs[i], acc[q1i][i] + bs[i]};
+                } else if (vs == 4) {
+                    *reinterpret_cast<f32x4*>(dst) =
+                        f32x4{acc[p][i] + bs[i], acc[q1i][i] + bs[i], acc[q2i][i] + bs[i], acc[q3i][i] + bs[i]};
+                } else if (vs == 3) {
+                    dst[0] = acc[p][i] + bs[i];
+                    dst[1] = acc[q1i][i] + bs[i];
+                    dst[2] = acc[q2i][i] + bs[i];
+                } else {
+                    dst[0] = acc[p][i] + bs[i];
+                }
+            }
+        }
+    };
+
+    // products of one staged chunk (buffer buf) for the phases of group pg
+    auto compute = [&](const float* buf, int pg) {
+        const float* bw = buf + wbase;
+        const float* bx = buf + xbase;
         if constexpr (KS != 0) {
             // every phase and tap unrolled: the operand offsets are immediates,
             // and a halo window shared by several phases is read once
@@ -303,7 +363,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
         } else {
-    #pragma unroll
+#pragma unroll
             for (int p = 0; p < kMaxPh; ++p) {
                 const int beg = a.gbeg[pg][p], end = a.gbeg[pg][p + 1];
                 // four taps per step: their offsets, then all operand reads, then
@@ -313,16 +373,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 for (; t + 4 <= end; t += 4) {
                     int2 o[4];
                     VA av[4], bv[4];
-    #pragma unroll
+#pragma unroll
                     for (int k = 0; k < 4; ++k) o[k] = taps[t + k];
-    #pragma unroll
+#pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         av[k] = *reinterpret_cast<const VA*>(bw + o[k].x);
                         bv[k] = *reinterpret_cast<const VA*>(bx + o[k].y);
                     }
-    #pragma unroll
+#pragma unroll
                     for (int k = 0; k < 4; ++k)
-    #pragma unroll
+#pragma unroll
                         for (int s = 0; s < H; ++s)
                             acc[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[k][s], bv[k][s], acc[p], 0, 0, 0);
                     // keep the eight operand reads ahead of the products (the
@@ -335,64 +395,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     const int2 o = taps[t];
                     const VA av = *reinterpret_cast<const VA*>(bw + o.x);
                     const VA bv = *reinterpret_cast<const VA*>(bx + o.y);
-    #pragma unroll
+#pragma unroll
                     for (int s = 0; s < H; ++s)
                         acc[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s], bv[s], acc[p], 0, 0, 0);
                 }
             }
         }
+    };
+
+    if (KS == 0 && a.pg_inner) {
+        // every input channel fits the two buffers: stage them once and run
+        // every phase group from them (more than one group needs a stride
+        // above 2, so the fixed geometries never take this path)
+        load(0);
+        store(0, lds);
+        if (a.nchunks > 1) {
+            load(1);
+            store(1, lds + L::kBuf);
+        }
+        __syncthreads();
+        float bs[16];
+        load_bias(bs);
+        const int pg_end = pg0 + a.pg_per < a.pgroups ? pg0 + a.pg_per : a.pgroups;
+        for (int pg = pg0; pg < pg_end; ++pg) {
+#pragma unroll
+            for (int p = 0; p < kMaxPh; ++p)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[p][i] = 0.f;
+            for (int c = 0; c < a.nchunks; ++c) compute(lds + c * L::kBuf, pg);
+            epilogue(pg, bs);
+        }
+        return;
+    }
+
+    load(0);
+    store(0, lds);
+    __syncthreads();
+    for (int c = 0; c < a.nchunks; ++c) {
+        const bool more = c + 1 < a.nchunks;
+        if (more) load(c + 1);
+        compute(lds + (c & 1) * L::kBuf, pg0);
         if (more) store(c + 1, lds + ((c + 1) & 1) * L::kBuf);
         // the other buffer was last read in the previous chunk, which every wave
         // finished before the previous barrier; this one lets the next chunk
         // read what was just stored
         __syncthreads();
     }
-
-    // ---- epilogue: a lane holds position q2 + nn and channels
-    // oc0 + 8(i/4) + 4h + i%4; the channel offsets are uniform multiples of
-    // the channel stride, added to one row pointer per phase
-    const int64_t O1 = a.O[1], O2 = a.O[2];
-    const int64_t cst = (int64_t)a.O[0] * O1 * O2;  // floats between output channels
-    const int p0 = q0 + wr0, p1 = q1 + wr1, pq = q2 + nn;
-    const bool all_oc = oc0 + kOCB <= a.cout;       // uniform
-    float* yb = a.y + (int64_t)grp * a.y_gstride + (n * a.yC + oc0 + 4 * h) * cst;
     float bs[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int oc = oc0 + 8 * (i >> 2) + 4 * h + (i & 3);
-        bs[i] = (a.bias && oc < a.cout) ? a.bias[(int64_t)grp * a.cout + oc] : 0.f;
-    }
-    const int vs = a.vecs;
-#pragma unroll
-    for (int p = 0; p < kMaxPh; ++p) {
-        if (p >= a.P) break;
-        if (vs && p % vs != 0) continue;
-        const int res = a.gres[pg][p];
-        const int r0 = res & 15, r1 = (res >> 4) & 15, r2 = res >> 8;
-        if (p0 >= a.Q[0][r0] || p1 >= a.Q[1][r1]) continue;
-        const int64_t row = ((int64_t)(a.s[0] * p0 + r0) * O1 + (a.s[1] * p1 + r1)) * O2;
-        // the residues of dim 2 are phases p .. p + vs - 1 when vs > 1
-        if (pq >= a.Q[2][vs ? 0 : r2]) continue;
-        float* rp = yb + row + (vs ? (int64_t)vs * pq : (int64_t)a.s[2] * pq + r2);
-        const int q1i = (p + 1) & (kMaxPh - 1), q2i = (p + 2) & (kMaxPh - 1), q3i = (p + 3) & (kMaxPh - 1);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (!all_oc && oc0 + 8 * (i >> 2) + 4 * h + (i & 3) >= a.cout) continue;
-            float* dst = rp + (8 * (i >> 2) + (i & 3)) * cst;
-            if (vs == 2) {
-                *reinterpret_cast<f32x2*>(dst) = f32x2{acc[p][i] + bs[i], acc[q1i][i] + bs[i]};
-            } else if (vs == 4) {
-                *reinterpret_cast<f32x4*>(dst) =
-                    f32x4{acc[p][i] + bs[i], acc[q1i][i] + bs[i], acc[q2i][i] + bs[i], acc[q3i][i] + bs[i]};
-            } else if (vs == 3) {
-                dst[0] = acc[p][i] + bs[i];
-                dst[1] = acc[q1i][i] + bs[i];
-                dst[2] = acc[q2i][i] + bs[i];
-            } else {
-                dst[0] = acc[p][i] + bs[i];
-            }
-        }
-    }
+    load_bias(bs);
+    epilogue(pg0, bs);
 }
 
 // Taps of one dim: per residue r the kernel indices k[r][t] and input offsets
@@ -433,10 +484,17 @@ bool dim_taps(int32_t K, int32_t s, int32_t p, int32_t d, DimTaps& t) {
     return true;
 }
 
+int fixed_kind(const Geom& g);
+
 template <int ICC, int KV>
 bool build_gargs(const Geom& g, GArgs& a) {
     using L = Lay<ICC, KV>;
     a = GArgs{};
+    // rows of at most 16 positions fold two to a wave (tap-table kernels only)
+    a.fold = fixed_kind(g) == 0 && ceil_div(g.O[2], g.s[2]) <= kTW / 2 ? 2 : 1;
+    a.hx1 = kR1 * a.fold + 2;
+    a.hx2 = kTW / a.fold + 2;
+    static_assert(kHX0 * (kR1 * 2 + 2) * (kTW / 2 + 2) <= kHPos, "folded halo layout");
     const int kvol = g.k[0] * g.k[1] * g.k[2];
     if (kvol > KV || kvol > kMaxTaps) return false;
     DimTaps dt[3];
@@ -487,7 +545,7 @@ bool build_gargs(const Geom& g, GArgs& a) {
                     for (int u2 = 0; u2 < dt[2].n[r2]; ++u2) {
                         if (nt == kvol) return false;  // cannot happen: every tap lies in one phase
                         const int kv = (dt[0].k[r0][u0] * g.k[1] + dt[1].k[r1][u1]) * g.k[2] + dt[2].k[r2][u2];
-                        const int xo = (dt[0].off[r0][u0] * kHX1 + dt[1].off[r1][u1]) * kHX2 + dt[2].off[r2][u2];
+                        const int xo = (dt[0].off[r0][u0] * a.hx1 + dt[1].off[r1][u1]) * a.hx2 + dt[2].off[r2][u2];
                         a.tapw[nt] = kv * L::kWTS;
                         a.tapx[nt] = xo * L::kHalf;
                         ++nt;
@@ -501,19 +559,22 @@ bool build_gargs(const Geom& g, GArgs& a) {
     a.kvol = kvol;
     a.xC = g.Cin;
     a.yC = g.Cout;
-    const int R[3] = {kR0, kR1, kTW};
+    const int R[3] = {kR0, kR1 * a.fold, kTW / a.fold};
     for (int j = 0; j < 3; ++j) {
         const int64_t tl = ceil_div(ceil_div(g.O[j], g.s[j]), R[j]);
         if (tl > INT_MAX) return false;
         a.tiles[j] = (int32_t)tl;
     }
-    const int e2 = kTW + a.ext[2], e12 = (kR1 + a.ext[1]) * e2;
+    const int e2 = kTW / a.fold + a.ext[2], e12 = (kR1 * a.fold + a.ext[1]) * e2;
     a.inv_e2 = 1.0f / (float)e2;
     a.inv_e12 = 1.0f / (float)e12;
     a.inv_kvol = 1.0f / (float)kvol;
     a.oc_blocks = (int32_t)ceil_div(g.cout_g, kOCB);
     a.groups = g.groups;
     a.nchunks = (int32_t)ceil_div(g.cin_g, ICC);
+    a.pg_inner = a.pgroups > 1 && a.nchunks <= 2;
+    a.pg_split = a.pgroups;  // the most workgroups per tile; the launch may merge phase groups
+    a.pg_per = 1;
     a.x_gstride = (int64_t)g.cin_g * g.S[0] * g.S[1] * g.S[2];
     a.w_gstride = (int64_t)g.cin_g * g.cout_g * kvol;
     a.y_gstride = (int64_t)g.cout_g * g.O[0] * g.O[1] * g.O[2];
@@ -523,7 +584,20 @@ bool build_gargs(const Geom& g, GArgs& a) {
 }
 
 int64_t grid_blocks(const Geom& g, const GArgs& a) {
-    return g.N * (int64_t)g.groups * a.tiles[0] * a.tiles[1] * a.tiles[2] * a.pgroups * a.oc_blocks;
+    return g.N * (int64_t)g.groups * a.tiles[0] * a.tiles[1] * a.tiles[2] * (a.pg_inner ? a.pg_split : a.pgroups) *
+           a.oc_blocks;
+}
+
+int cu_count() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, v = 0;
+        cus = hipGetDevice(&dev) == hipSuccess &&
+                      hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0
+                  ? v
+                  : 256;
+    }
+    return cus;
 }
 
 bool build_any(const Geom& g, GArgs& a, bool& small) {
@@ -562,6 +636,14 @@ hipError_t launch_convT_phasegroup(const float* x, const float* w, const float* 
     a.w = w;
     a.bias = bias;
     a.y = y;
+    if (a.pg_inner) {
+        // enough workgroups for one per CU, each taking a run of phase groups
+        const int64_t base = g.N * (int64_t)g.groups * a.tiles[0] * a.tiles[1] * a.tiles[2] * a.oc_blocks;
+        const int64_t want = ceil_div(cu_count(), base);
+        const int split = (int)(want < a.pgroups ? want : a.pgroups);
+        a.pg_per = (int32_t)ceil_div(a.pgroups, split);
+        a.pg_split = (int32_t)ceil_div(a.pgroups, a.pg_per);
+    }
     // the 8- and 16-byte stores need y aligned to their size
     if ((a.vecs == 2 && ((uintptr_t)y & 7) != 0) || (a.vecs == 4 && ((uintptr_t)y & 15) != 0)) a.vecs = 0;
     static_assert(sizeof(GArgs) <= 4096, "kernel arguments");
