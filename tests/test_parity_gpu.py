@@ -215,6 +215,35 @@ def test_convT_phase_medium(name, pv):
         B.set_variant(old)
 
 
+UNALIGNED_Y = {
+    # the residues of dim 2 leave in one 8-, 16- or 12-byte store per lane when y allows it
+    "pairs": W.make("pu", "conv_transpose3d", (1, 8, 3, 5, 20), 40, 3, 2, 1, 1, 1, bias=True, seed=86),
+    "quads": W.make("pu", "conv_transpose3d", (1, 8, 3, 4, 9), 16, (3, 3, 4), (1, 2, 4), (1, 1, 0), bias=True,
+                    seed=87),
+    "triples": PHASE_MEDIUM["k3s3p1_op2_groups2"],
+}
+
+
+@pytest.mark.parametrize("name", list(UNALIGNED_Y))
+def test_convT_phase_group_unaligned_output(name):
+    """y 4 bytes off a 16-byte boundary: the shared-halo kernel falls back to
+    single-float stores where its packed stores need 8 or 16 bytes."""
+    wl = UNALIGNED_Y[name]
+    p = B.make_params(wl.kernel, wl.stride, wl.pad, wl.dilation, wl.output_pad, wl.groups)
+    assert B.conv_transpose3d_algo(wl.x_shape, wl.cout, p) == "phase_group"
+    inp = W.make_inputs(wl)
+    ref = O.run_workload(wl, inp)
+    flat = torch.full((int(np.prod(ref.shape)) + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    y = flat[1:].view(ref.shape)
+    assert y.data_ptr() % 16 == 4
+    print(f"[convT unaligned y {name}] {wl}", flush=True)
+    B.conv_transpose3d_fwd(dev(inp.x), dev(inp.w), dev(inp.b), wl.stride, wl.pad, wl.dilation, wl.output_pad,
+                           wl.groups, out=y)
+    torch.cuda.synchronize()
+    assert torch.isnan(flat[0]).item()  # nothing written before y
+    assert_close(f"unaligned y {name}", y.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("pv", list(PHASE_VARIANTS))
 @pytest.mark.parametrize("key", list(W.WIDEN))
 def test_convT_widen_full_size_sampled(key, pv):
