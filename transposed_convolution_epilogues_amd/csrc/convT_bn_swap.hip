@@ -151,6 +151,20 @@ constexpr int reduce_width() {
     return n_stat(C) > 64 ? 128 : (n_stat(C) > 16 ? 64 : 16);
 }
 
+// The statistics workgroup has two waves per (column, row group): the first
+// half of the waves takes the channel sums, lag 0 and the forward lags 0..5
+// ((0,0,1), (0,1,*), (1,-1,-1), (1,-1,0)), the second half the lags 6..12
+// ((1,-1,1), (1,0,*), (1,1,*)).  Each keeps 63 accumulators for 3 channels
+// instead of 126, so four waves fit a SIMD instead of two.
+constexpr int kStatThreads = 512;
+constexpr int kLagSplit = 6;
+template <int C>
+constexpr int half_a() { return C + C * (C + 1) / 2 + kLagSplit * C * C; }  // statistics of the first half
+template <int C>
+constexpr int half_width() {
+    return (half_a<C>() > n_stat(C) - half_a<C>() ? half_a<C>() : n_stat(C) - half_a<C>()) > 16 ? 64 : 16;
+}
+
 // ------------------------------------------------------------ statistics
 // A workgroup takes kSlab planes of one sample and one 32 x 32 tile of the
 // (p1, p2) plane.  Planes go through a ring of three LDS slots: plane p and
@@ -175,12 +189,17 @@ struct StatArgs {
     int32_t blocks;
 };
 
+// 16-byte units of a plane's tile (channel, row, quarter-row) per thread
 template <int CIN>
-__device__ __forceinline__ void fast_fetch(const float* xn, int p, int S0, float4 (&r)[CIN]) {
+constexpr int fetch_units() { return (CIN * 256 + kStatThreads - 1) / kStatThreads; }
+
+template <int CIN>
+__device__ __forceinline__ void fast_fetch(const float* xn, int p, int S0, float4 (&r)[fetch_units<CIN>()]) {
     const int pc = p < S0 ? p : S0 - 1;  // clamped plane, selected below
 #pragma unroll
-    for (int u = 0; u < CIN; ++u) {
-        const int f = u * kThreads + threadIdx.x;
+    for (int u = 0; u < fetch_units<CIN>(); ++u) {
+        int f = u * kStatThreads + threadIdx.x;
+        f = f < CIN * 256 ? f : 0;  // no unit: a valid address, not stored
         const int c = f >> 8, row = (f >> 3) & 31, q = f & 7;
         const float4 v = *reinterpret_cast<const float4*>(xn + ((int64_t)c * S0 + pc) * (kTile * kTile) + row * kTile + 4 * q);
         r[u] = p < S0 ? v : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -188,10 +207,11 @@ __device__ __forceinline__ void fast_fetch(const float* xn, int p, int S0, float
 }
 
 template <int CIN>
-__device__ __forceinline__ void fast_put(float* slot, const float4 (&r)[CIN]) {
+__device__ __forceinline__ void fast_put(float* slot, const float4 (&r)[fetch_units<CIN>()]) {
 #pragma unroll
-    for (int u = 0; u < CIN; ++u) {
-        const int f = u * kThreads + threadIdx.x;
+    for (int u = 0; u < fetch_units<CIN>(); ++u) {
+        const int f = u * kStatThreads + threadIdx.x;
+        if (f >= CIN * 256) continue;
         const int c = f >> 8, row = (f >> 3) & 31, q = f & 7;
         *reinterpret_cast<float4*>(slot + c * kChS + (row + 1) * kRS + 4 + 4 * q) = r[u];
     }
@@ -203,11 +223,11 @@ template <int CIN>
 __device__ void box_stage(const float* xn, int p, const StatArgs& a, int r0, int c0, float* slot) {
     const int S0 = a.S[0], S1 = a.S[1], S2 = a.S[2];
     constexpr int kBox = kRows * (kTile + 2);
-    for (int e0 = 0; e0 < CIN * kBox; e0 += 16 * kThreads) {
+    for (int e0 = 0; e0 < CIN * kBox; e0 += 16 * kStatThreads) {
         float v[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const int e = e0 + u * kThreads + threadIdx.x;
+            const int e = e0 + u * kStatThreads + threadIdx.x;
             const int c = e / kBox, rem = e % kBox;
             const int row = rem / (kTile + 2), col = rem % (kTile + 2);
             const int p1 = r0 + row, p2 = c0 + col;
@@ -217,7 +237,7 @@ __device__ void box_stage(const float* xn, int p, const StatArgs& a, int r0, int
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const int e = e0 + u * kThreads + threadIdx.x;
+            const int e = e0 + u * kStatThreads + threadIdx.x;
             if (e < CIN * kBox) {
                 const int c = e / kBox, rem = e % kBox;
                 slot[c * kChS + (rem / (kTile + 2)) * kRS + 3 + rem % (kTile + 2)] = v[u];
@@ -226,35 +246,35 @@ __device__ void box_stage(const float* xn, int p, const StatArgs& a, int r0, int
     }
 }
 
-// the 126 (3 channels) products of 4 rows of one column: A at plane p, B at
-// plane p + 1, both at the lane's first row and column
+// Products of 4 rows of one column: A at plane p, B at plane p + 1, both at
+// the lane's first row (tile row r = 4g) and column.  Statistic index:
+// channel sums c; lag 0 pairs c <= c' next; forward lag L of pair (c, c') at
+// F + (L C + c) C + c'.
+// First half (63 for 3 channels): sums, lag 0, lags (0,0,1), (0,1,d2), (1,-1,-1),
+// (1,-1,0).  Register window: row r of plane p at columns 0 and 1, row r + 1
+// of plane p (which becomes the next row's own values), row r - 1 of plane
+// p + 1 at columns -1 and 0.
 template <int CIN>
-__device__ __forceinline__ void stat_rows(const float* A, const float* B, float* acc) {
+__device__ __forceinline__ void stat_rows_a(const float* A, const float* B, float* acc) {
     constexpr int C = CIN;
     constexpr int F = C + C * (C + 1) / 2;
-    float bw[3][3][C];  // plane p + 1: rows r - 1, r, r + 1; columns -1, 0, 1
-    float an[3][C];     // plane p: row r + 1, columns -1, 0, 1
     float a0[C], a1[C];  // plane p: row r, columns 0 and 1
+    float an[3][C];      // plane p: row r + 1, columns -1, 0, 1
+    float bm[2][C];      // plane p + 1: row r - 1, columns -1, 0
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-#pragma unroll
-        for (int dc = 0; dc < 3; ++dc) {
-            bw[0][dc][c] = B[c * kChS - kRS + dc - 1];
-            bw[1][dc][c] = B[c * kChS + dc - 1];
-        }
         a0[c] = A[c * kChS];
         a1[c] = A[c * kChS + 1];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int ro = (i + 1) * kRS;
 #pragma unroll
-        for (int c = 0; c < C; ++c)
+        for (int c = 0; c < C; ++c) {
 #pragma unroll
-            for (int dc = 0; dc < 3; ++dc) {
-                bw[2][dc][c] = B[c * kChS + ro + dc - 1];
-                an[dc][c] = A[c * kChS + ro + dc - 1];
-            }
+            for (int dc = 0; dc < 3; ++dc) an[dc][c] = A[c * kChS + (i + 1) * kRS + dc - 1];
+#pragma unroll
+            for (int dc = 0; dc < 2; ++dc) bm[dc][c] = B[c * kChS + (i - 1) * kRS + dc - 1];
+        }
         int l0 = C;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -269,22 +289,62 @@ __device__ __forceinline__ void stat_rows(const float* A, const float* B, float*
                 for (int dc = 0; dc < 3; ++dc)
                     acc[F + ((1 + dc) * C + c) * C + cp] = fmaf(a0[c], an[dc][cp], acc[F + ((1 + dc) * C + c) * C + cp]);
 #pragma unroll
-                for (int d1 = 0; d1 < 3; ++d1)
-#pragma unroll
-                    for (int dc = 0; dc < 3; ++dc)
-                        acc[F + ((4 + 3 * d1 + dc) * C + c) * C + cp] =
-                            fmaf(a0[c], bw[d1][dc][cp], acc[F + ((4 + 3 * d1 + dc) * C + c) * C + cp]);
+                for (int dc = 0; dc < 2; ++dc)
+                    acc[F + ((4 + dc) * C + c) * C + cp] = fmaf(a0[c], bm[dc][cp], acc[F + ((4 + dc) * C + c) * C + cp]);
             }
         }
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-#pragma unroll
-            for (int dc = 0; dc < 3; ++dc) {
-                bw[0][dc][c] = bw[1][dc][c];
-                bw[1][dc][c] = bw[2][dc][c];
-            }
             a0[c] = an[1][c];
             a1[c] = an[2][c];
+        }
+    }
+}
+
+// Second half (63 for 3 channels): lags (1,-1,1), (1,0,d2), (1,1,d2), indexed
+// from half_a.  Register window: row r - 1 of plane p + 1 at column 1, rows r
+// and r + 1 at columns -1, 0, 1 (row r + 1 becomes the next row's r).
+template <int CIN>
+__device__ __forceinline__ void stat_rows_b(const float* A, const float* B, float* acc) {
+    constexpr int C = CIN;
+    constexpr int F = C + C * (C + 1) / 2;
+    constexpr int H0 = half_a<C>();
+    float a0[C];         // plane p: row r, column 0
+    float bp[C];         // plane p + 1: row r - 1, column 1
+    float b0[3][C];      // plane p + 1: row r
+    float b1[3][C];      // plane p + 1: row r + 1
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        bp[c] = B[c * kChS - kRS + 1];
+#pragma unroll
+        for (int dc = 0; dc < 3; ++dc) b0[dc][c] = B[c * kChS + dc - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            a0[c] = A[c * kChS + i * kRS];
+#pragma unroll
+            for (int dc = 0; dc < 3; ++dc) b1[dc][c] = B[c * kChS + (i + 1) * kRS + dc - 1];
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int cp = 0; cp < C; ++cp) {
+                acc[F + (6 * C + c) * C + cp - H0] = fmaf(a0[c], bp[cp], acc[F + (6 * C + c) * C + cp - H0]);
+#pragma unroll
+                for (int dc = 0; dc < 3; ++dc) {
+                    acc[F + ((7 + dc) * C + c) * C + cp - H0] =
+                        fmaf(a0[c], b0[dc][cp], acc[F + ((7 + dc) * C + c) * C + cp - H0]);
+                    acc[F + ((10 + dc) * C + c) * C + cp - H0] =
+                        fmaf(a0[c], b1[dc][cp], acc[F + ((10 + dc) * C + c) * C + cp - H0]);
+                }
+            }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            bp[c] = b0[2][c];
+#pragma unroll
+            for (int dc = 0; dc < 3; ++dc) b0[dc][c] = b1[dc][c];
         }
     }
 }
@@ -292,9 +352,11 @@ __device__ __forceinline__ void stat_rows(const float* A, const float* B, float*
 template <int CIN, bool FAST>
 __device__ __forceinline__ void stats_block(const StatArgs& a, float* lds, int blk) {
     constexpr int NS = n_stat(CIN);
-    constexpr int NA = reduce_width<CIN>();
+    constexpr int NA = half_width<CIN>();
+    constexpr int HA = half_a<CIN>();
     constexpr int kSlot = CIN * kChS;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const bool second = wv >= kStatThreads / 128;  // wave-uniform: which half of the statistics
     int b = blk;
     if ((a.blocks & 7) == 0) b = (b & 7) * (a.blocks >> 3) + (b >> 3);  // neighbouring slabs on one XCD
     const int t2 = b % a.T2;
@@ -311,12 +373,12 @@ __device__ __forceinline__ void stats_block(const StatArgs& a, float* lds, int b
     // Plane P is stored before the loop; plane p + 1 is stored at the top of
     // the iteration of plane p, before its barrier, so the loads fetched one
     // iteration earlier had a whole iteration of products to arrive.
-    float4 pre[CIN];
+    float4 pre[fetch_units<CIN>()];
     if constexpr (FAST) {
         // halos are zero and never written again; the interiors are fetched
-        for (int i = tid; i < 3 * kSlot / 4; i += kThreads)
+        for (int i = tid; i < 3 * kSlot / 4; i += kStatThreads)
             reinterpret_cast<float4*>(lds)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        float4 pre0[CIN];
+        float4 pre0[fetch_units<CIN>()];
         fast_fetch<CIN>(xn, P, S0, pre0);
         fast_fetch<CIN>(xn, P + 1, S0, pre);
         __syncthreads();
@@ -328,7 +390,7 @@ __device__ __forceinline__ void stats_block(const StatArgs& a, float* lds, int b
     float acc[NA];
 #pragma unroll
     for (int i = 0; i < NA; ++i) acc[i] = 0.f;
-    const int g = 2 * wv + (lane >> 5);
+    const int g = 2 * (wv % (kStatThreads / 128)) + (lane >> 5);
     const int lane_base = (4 * g + 1) * kRS + 4 + (lane & 31);
     for (int p = P; p < Pend; ++p) {
         const int i = p - P;
@@ -341,22 +403,29 @@ __device__ __forceinline__ void stats_block(const StatArgs& a, float* lds, int b
         if constexpr (FAST) {
             if (p + 1 < Pend) fast_fetch<CIN>(xn, p + 2, S0, pre);  // read by the next plane
         }
-        stat_rows<CIN>(lds + (i % 3) * kSlot + lane_base, lds + ((i + 1) % 3) * kSlot + lane_base, acc);
+        const float* pa = lds + (i % 3) * kSlot + lane_base;
+        const float* pb = lds + ((i + 1) % 3) * kSlot + lane_base;
+        if (second)
+            stat_rows_b<CIN>(pa, pb, acc);
+        else
+            stat_rows_a<CIN>(pa, pb, acc);
     }
     __syncthreads();
-    // every LDS read is done: the first slot takes the four waves' totals
+    // every LDS read is done: the first slot takes the waves' totals
     wave_reduce_to<NA>(acc, lds + wv * NA, lane);
     __syncthreads();
     if (tid < NS) {
-        float s = lds[tid];
+        constexpr int kHalfW = kStatThreads / 128;  // waves per half
+        const int w0 = tid < HA ? 0 : kHalfW, v = tid < HA ? tid : tid - HA;
+        float s = lds[w0 * NA + v];
 #pragma unroll
-        for (int w = 1; w < kThreads / 64; ++w) s += lds[w * NA + tid];
+        for (int w = 1; w < kHalfW; ++w) s += lds[(w0 + w) * NA + v];
         a.part[(int64_t)blk * kStatRow + tid] = s;
     }
 }
 
 template <int CIN, bool FAST>
-__global__ __launch_bounds__(kThreads) void swap_stats_kernel(StatArgs a) {
+__global__ __launch_bounds__(kStatThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void swap_stats_kernel(StatArgs a) {
     __shared__ __attribute__((aligned(16))) float lds[3 * CIN * kChS];
     stats_block<CIN, FAST>(a, lds, (int)blockIdx.x);
 }
@@ -415,7 +484,7 @@ __host__ __device__ inline int shell_lds_floats(int C, int Sa, int Sb) {
     return 2 * C * shell_cs(Sa, Sb) + 8 + 2 * (shell_rs(Sb) + 8) + 128;
 }
 
-template <int CIN>
+template <int CIN, int NT>
 __device__ void shell_block(const ShellArgs& a, int blk, float* pl) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -432,7 +501,7 @@ __device__ void shell_block(const ShellArgs& a, int blk, float* pl) {
     zoff += ((24 - zoff) % 64 + 64) % 64;
     int ooff = zoff + RS + 8;
     ooff += ((28 - ooff) % 64 + 64) % 64;
-    for (int i = tid; i < RS + 8; i += kThreads) {
+    for (int i = tid; i < RS + 8; i += NT) {
         pl[zoff + i] = 0.f;
         pl[ooff + i] = 1.f;
     }
@@ -440,12 +509,12 @@ __device__ void shell_block(const ShellArgs& a, int blk, float* pl) {
     // time; the index splits use float reciprocals (exact below 2^22)
     const int total = 2 * CIN * face;
     const float rface = 1.f / (float)face, rsb = 1.f / (float)Sb;
-    for (int e0 = 0; e0 < total; e0 += 12 * kThreads) {
+    for (int e0 = 0; e0 < total; e0 += 12 * NT) {
         float v[12];
         int dst[12];
 #pragma unroll
         for (int u = 0; u < 12; ++u) {
-            const int e = e0 + u * kThreads + tid;
+            const int e = e0 + u * NT + tid;
             const int ec = e < total ? e : total - 1;
             const int sc = (int)(((float)ec + 0.5f) * rface), idx = ec - sc * face;
             const int ia = (int)(((float)idx + 0.5f) * rsb), ib = idx - ia * Sb;
@@ -467,7 +536,7 @@ __device__ void shell_block(const ShellArgs& a, int blk, float* pl) {
         for (int ta = (ad < fi ? 1 : 0); ta <= (ad < fi ? 1 : 2); ++ta)
             for (int tb = (bd < fi ? 1 : 0); tb <= (bd < fi ? 1 : 2); ++tb) {
                 const bool big = ta == 1 && tb == 1;
-                const int owner = big ? side : 2 + ((small++) & 1);
+                const int owner = big ? side : 2 + (small++) % (NT / 64 - 2);
                 if (owner != wv) continue;  // uniform per wave
                 const int nM = (ta == 1) + (tb == 1);
                 const int na = ta == 1 ? Sa - 1 : 1, nb = tb == 1 ? Sb - 1 : 1;
@@ -512,11 +581,11 @@ __device__ void shell_block(const ShellArgs& a, int blk, float* pl) {
 // (measured: behind the statistics the shell work fills the tail; in front
 // it delays the statistics workgroups).
 template <int CIN, bool FAST>
-__global__ __launch_bounds__(kThreads) void swap_stats_shell_kernel(StatArgs a, ShellArgs sh) {
+__global__ __launch_bounds__(kStatThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void swap_stats_shell_kernel(StatArgs a, ShellArgs sh) {
     constexpr int kSlot = CIN * kChS;
     __shared__ __attribute__((aligned(16))) float lds[3 * kSlot];
     if ((int)blockIdx.x >= a.blocks) {
-        shell_block<CIN>(sh, (int)blockIdx.x - a.blocks, lds);
+        shell_block<CIN, kStatThreads>(sh, (int)blockIdx.x - a.blocks, lds);
         return;
     }
     stats_block<CIN, FAST>(a, lds, (int)blockIdx.x);
@@ -1257,13 +1326,13 @@ void launch_training(const SwapPlan& sp, hipStream_t s) {
     if (sp.shell_lds) {
         const unsigned nb = (unsigned)(sp.stat_blocks + sp.shell_blocks);
         if (sp.fast_stats)
-            hipLaunchKernelGGL((swap_stats_shell_kernel<CIN, true>), dim3(nb), dim3(kThreads), 0, s, sp.st, sp.sh);
+            hipLaunchKernelGGL((swap_stats_shell_kernel<CIN, true>), dim3(nb), dim3(kStatThreads), 0, s, sp.st, sp.sh);
         else
-            hipLaunchKernelGGL((swap_stats_shell_kernel<CIN, false>), dim3(nb), dim3(kThreads), 0, s, sp.st, sp.sh);
+            hipLaunchKernelGGL((swap_stats_shell_kernel<CIN, false>), dim3(nb), dim3(kStatThreads), 0, s, sp.st, sp.sh);
     } else if (sp.fast_stats) {
-        hipLaunchKernelGGL((swap_stats_kernel<CIN, true>), dim3((unsigned)sp.stat_blocks), dim3(kThreads), 0, s, sp.st);
+        hipLaunchKernelGGL((swap_stats_kernel<CIN, true>), dim3((unsigned)sp.stat_blocks), dim3(kStatThreads), 0, s, sp.st);
     } else {
-        hipLaunchKernelGGL((swap_stats_kernel<CIN, false>), dim3((unsigned)sp.stat_blocks), dim3(kThreads), 0, s, sp.st);
+        hipLaunchKernelGGL((swap_stats_kernel<CIN, false>), dim3((unsigned)sp.stat_blocks), dim3(kStatThreads), 0, s, sp.st);
     }
     if (!sp.shell_lds)
         hipLaunchKernelGGL(swap_shell_global_kernel<CIN>, dim3((unsigned)sp.shell_blocks), dim3(kThreads), 0, s, sp.sh);
