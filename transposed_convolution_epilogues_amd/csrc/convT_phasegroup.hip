@@ -216,15 +216,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         wel[u] = m < 2 * wrun ? wl | rem << 14 | hh << 25 | (oc0 + oc >= a.cout) << 26 : -1;
     }
 
+    using XR = float[kHaloPer][ICC];
+    using WR = float[L::kWPer][H];
     float xr[kHaloPer][ICC];
     float wr[L::kWPer][H];
-    auto load = [&](int c) {
+    // a chunk's halo and weights into registers xr_, wr_
+    auto load_to = [&](int c, XR& xr_, WR& wr_) {
         const int ic0 = c * ICC;
 #pragma unroll
         for (int i = 0; i < ICC; ++i) {
             const float* xc = xg + (ic0 + i < a.cin ? ic0 + i : 0) * plane;
 #pragma unroll
-            for (int u = 0; u < kHaloPer; ++u) xr[u][i] = xc[xsp[u] >= 0 ? xsp[u] : 0];
+            for (int u = 0; u < kHaloPer; ++u) xr_[u][i] = xc[xsp[u] >= 0 ? xsp[u] : 0];
         }
         // units of output channels past cout, and channels past cin (the
         // last chunk), read element 0
@@ -237,11 +240,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int s = 0; s < H; ++s) {
                 const int icl = hh * H + s;
-                wr[u][s] = wc[ok && ic0 + icl < a.cin ? icl * wic + off : 0];
+                wr_[u][s] = wc[ok && ic0 + icl < a.cin ? icl * wic + off : 0];
             }
         }
     };
-    auto store = [&](int c, float* buf) {
+    // registers xr_, wr_ of chunk c into LDS buffer buf
+    auto store_from = [&](int c, float* buf, const XR& xr_, const WR& wr_) {
         const int ic0 = c * ICC;
 #pragma unroll
         for (int u = 0; u < kHaloPer; ++u) {
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int hh = 0; hh < 2; ++hh) {
                 VA v;
 #pragma unroll
-                for (int s = 0; s < H; ++s) v[s] = (xsp[u] >= 0 && ic0 + hh * H + s < a.cin) ? xr[u][hh * H + s] : 0.f;
+                for (int s = 0; s < H; ++s) v[s] = (xsp[u] >= 0 && ic0 + hh * H + s < a.cin) ? xr_[u][hh * H + s] : 0.f;
                 *reinterpret_cast<VA*>(buf + (hh * kHPos + xlp[u]) * H) = v;
             }
         }
@@ -263,10 +267,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const bool ok = !((v >> 26) & 1);
             VA x;
 #pragma unroll
-            for (int s = 0; s < H; ++s) x[s] = (ok && ic0 + hh * H + s < a.cin) ? wr[u][s] : 0.f;
+            for (int s = 0; s < H; ++s) x[s] = (ok && ic0 + hh * H + s < a.cin) ? wr_[u][s] : 0.f;
             *reinterpret_cast<VA*>(wb + (v & 16383)) = x;
         }
     };
+    auto load = [&](int c) { load_to(c, xr, wr); };
+    auto store = [&](int c, float* buf) { store_from(c, buf, xr, wr); };
 
     f32x16 acc[kMaxPh];
 #pragma unroll
@@ -407,12 +413,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // every input channel fits the two buffers: stage them once and run
         // every phase group from them (more than one group needs a stride
         // above 2, so the fixed geometries never take this path)
+        // both chunks' loads in flight together
+        float xr1[kHaloPer][ICC];
+        float wr1[L::kWPer][H];
         load(0);
+        if (a.nchunks > 1) load_to(1, xr1, wr1);
         store(0, lds);
-        if (a.nchunks > 1) {
-            load(1);
-            store(1, lds + L::kBuf);
-        }
+        if (a.nchunks > 1) store_from(1, lds + L::kBuf, xr1, wr1);
         __syncthreads();
         float bs[16];
         load_bias(bs);
