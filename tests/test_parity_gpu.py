@@ -194,6 +194,16 @@ PHASE_MEDIUM = {
                     (1, 0, 0), bias=True, seed=85),
     # the stride-2 dilation-2 module of the transposed-conv workload, reduced
     "k3s2p1d2": W.CONFIGS["c3"].with_(x_shape=(2, 32, 5, 7, 19)),
+    # kernel = stride with more than 8 phases and 9-16 input channels per group:
+    # one tap per phase, every input channel staged once, 3 or 4 phases per group
+    # (dim-2 residues in one 12-, 16- or 8-byte store, or float by float);
+    # the first takes 3 phase groups per workgroup
+    "k3s3_one_tap_groups2": W.make("pm", "conv_transpose3d", (8, 32, 6, 9, 13), 32, 3, 3, 1, 1, 2, groups=2,
+                                   bias=True, seed=88),
+    "k4s4_one_tap": W.make("pm", "conv_transpose3d", (1, 8, 3, 4, 6), 16, 4, 4, (1, 2, 3), 1, (0, 1, 3),
+                           bias=True, seed=89),
+    "k322s322_one_tap": W.make("pm", "conv_transpose3d", (1, 10, 4, 5, 7), 24, (3, 2, 2), (3, 2, 2), (1, 0, 1), 1,
+                               (2, 1, 0), bias=True, seed=90),
 }
 
 
@@ -221,6 +231,7 @@ UNALIGNED_Y = {
     "quads": W.make("pu", "conv_transpose3d", (1, 8, 3, 4, 9), 16, (3, 3, 4), (1, 2, 4), (1, 1, 0), bias=True,
                     seed=87),
     "triples": PHASE_MEDIUM["k3s3p1_op2_groups2"],
+    "triples_one_tap": PHASE_MEDIUM["k3s3_one_tap_groups2"],
 }
 
 

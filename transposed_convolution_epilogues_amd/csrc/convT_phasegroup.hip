@@ -79,6 +79,9 @@ struct GArgs {
     int32_t pg_inner;         // more than one phase group and at most two chunks: a workgroup stages
                               // every input channel once and runs pg_per phase groups
     int32_t pg_split, pg_per; // with pg_inner: workgroups per tile, phase groups per workgroup
+    int32_t one_tap;          // with pg_inner: two chunks, at most 4 phases per group and one tap
+                              // per phase (kernel = stride in every dim); the tap of phase p of
+                              // group g is g P + p
     float inv_e2, inv_e12, inv_kvol;  // reciprocals for the staging index splits
     int64_t x_gstride, w_gstride, y_gstride;
     // tap table: LDS offsets (floats) of each tap's weights and halo window,
@@ -299,10 +302,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             bs[i] = (a.bias && oc < a.cout) ? a.bias[(int64_t)grp * a.cout + oc] : 0.f;
         }
     };
-    auto epilogue = [&](int pg, const float (&bs)[16]) {
+    // the accumulators A of group pg (NA = kMaxPh, or 4 on the one-tap path)
+    auto epilogue_of = [&](int pg, const float (&bs)[16], auto& A) {
+        constexpr int NA = std::extent<std::remove_reference_t<decltype(A)>>::value;
         const int vs = a.vecs;
 #pragma unroll
-        for (int p = 0; p < kMaxPh; ++p) {
+        for (int p = 0; p < NA; ++p) {
             if (p >= a.P) break;
             if (vs && p % vs != 0) continue;
             const int res = a.gres[pg][p];
@@ -312,26 +317,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // the residues of dim 2 are phases p .. p + vs - 1 when vs > 1
             if (pq >= a.Q[2][vs ? 0 : r2]) continue;
             float* rp = yb + row + (vs ? (int64_t)vs * pq : (int64_t)a.s[2] * pq + r2);
-            const int q1i = (p + 1) & (kMaxPh - 1), q2i = (p + 2) & (kMaxPh - 1), q3i = (p + 3) & (kMaxPh - 1);
+            const int q1i = (p + 1) & (NA - 1), q2i = (p + 2) & (NA - 1), q3i = (p + 3) & (NA - 1);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 if (!all_oc && oc0 + 8 * (i >> 2) + 4 * h + (i & 3) >= a.cout) continue;
                 float* dst = rp + (8 * (i >> 2) + (i & 3)) * cst;
                 if (vs == 2) {
-                    *reinterpret_cast<f32x2*>(dst) = f32x2{acc[p][i] + bs[i], acc[q1i][i] + bs[i]};
+                    *reinterpret_cast<f32x2*>(dst) = f32x2{A[p][i] + bs[i], A[q1i][i] + bs[i]};
                 } else if (vs == 4) {
                     *reinterpret_cast<f32x4*>(dst) =
-                        f32x4{acc[p][i] + bs[i], acc[q1i][i] + bs[i], acc[q2i][i] + bs[i], acc[q3i][i] + bs[i]};
+                        f32x4{A[p][i] + bs[i], A[q1i][i] + bs[i], A[q2i][i] + bs[i], A[q3i][i] + bs[i]};
                 } else if (vs == 3) {
-                    dst[0] = acc[p][i] + bs[i];
-                    dst[1] = acc[q1i][i] + bs[i];
-                    dst[2] = acc[q2i][i] + bs[i];
+                    dst[0] = A[p][i] + bs[i];
+                    dst[1] = A[q1i][i] + bs[i];
+                    dst[2] = A[q2i][i] + bs[i];
                 } else {
-                    dst[0] = acc[p][i] + bs[i];
+                    dst[0] = A[p][i] + bs[i];
                 }
             }
         }
     };
+    auto epilogue = [&](int pg, const float (&bs)[16]) { epilogue_of(pg, bs, acc); };
 
     // products of one staged chunk (buffer buf) for the phases of group pg
     auto compute = [&](const float* buf, int pg) {
@@ -424,6 +430,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         float bs[16];
         load_bias(bs);
         const int pg_end = pg0 + a.pg_per < a.pgroups ? pg0 + a.pg_per : a.pgroups;
+        if (a.one_tap) {
+            // one tap per phase (P = NP phases): every operand of the group is
+            // read before its products, each phase's first product starts from
+            // zero, and the next group's tap offsets are read before the stores
+            const f32x16 zero = {};
+            auto groups = [&](auto npc) {
+                constexpr int NP = decltype(npc)::value;
+                int2 o[NP];
+#pragma unroll
+                for (int p = 0; p < NP; ++p) o[p] = taps[pg0 * NP + p];
+                for (int pg = pg0; pg < pg_end; ++pg) {
+                    // indexed in whole vectors (every offset is a multiple of H floats),
+                    // so that each read is one 16- or 8-byte LDS read
+                    const VA* lv = reinterpret_cast<const VA*>(lds);
+                    VA av[NP][2], bv[NP][2];
+#pragma unroll
+                    for (int p = 0; p < NP; ++p)
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            av[p][c] = lv[(unsigned)(c * L::kBuf + wbase + o[p].x) / H];
+                            bv[p][c] = lv[(unsigned)(c * L::kBuf + xbase + o[p].y) / H];
+                        }
+                    f32x16 ac[4];
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        ac[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[p][0][0], bv[p][0][0], zero, 0, 0, 0);
+#pragma unroll
+                        for (int c = 0; c < 2; ++c)
+#pragma unroll
+                            for (int s = c == 0 ? 1 : 0; s < H; ++s)
+                                ac[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[p][c][s], bv[p][c][s], ac[p], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4 * NP, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * H * NP, 0);
+                    const int pn = pg + 1 < pg_end ? pg + 1 : pg;
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) o[p] = taps[pn * NP + p];
+                    epilogue_of(pg, bs, ac);
+                }
+            };
+            if (a.P == 3)
+                groups(std::integral_constant<int, 3>{});
+            else
+                groups(std::integral_constant<int, 4>{});
+            return;
+        }
         for (int pg = pg0; pg < pg_end; ++pg) {
 #pragma unroll
             for (int p = 0; p < kMaxPh; ++p)
@@ -582,6 +634,9 @@ bool build_gargs(const Geom& g, GArgs& a) {
     a.pg_inner = a.pgroups > 1 && a.nchunks <= 2;
     a.pg_split = a.pgroups;  // the most workgroups per tile; the launch may merge phase groups
     a.pg_per = 1;
+    a.one_tap = a.pg_inner && a.nchunks == 2 && (a.P == 3 || a.P == 4) && nt == a.pgroups * a.P;
+    for (int pg = 0; pg < a.pgroups && a.one_tap; ++pg)
+        for (int p = 0; p < a.P; ++p) a.one_tap = a.one_tap && a.gbeg[pg][p] == pg * a.P + p;
     a.x_gstride = (int64_t)g.cin_g * g.S[0] * g.S[1] * g.S[2];
     a.w_gstride = (int64_t)g.cin_g * g.cout_g * kvol;
     a.y_gstride = (int64_t)g.cout_g * g.O[0] * g.O[1] * g.O[2];
