@@ -196,14 +196,17 @@ PHASE_MEDIUM = {
     "k3s2p1d2": W.CONFIGS["c3"].with_(x_shape=(2, 32, 5, 7, 19)),
     # kernel = stride with more than 8 phases and 9-16 input channels per group:
     # one tap per phase, every input channel staged once, 3 or 4 phases per group
-    # (dim-2 residues in one 12-, 16- or 8-byte store, or float by float);
-    # the first takes 3 phase groups per workgroup
-    "k3s3_one_tap_groups2": W.make("pm", "conv_transpose3d", (8, 32, 6, 9, 13), 32, 3, 3, 1, 1, 2, groups=2,
+    # (dim-2 residues in one 12-, 16- or 8-byte store, or float by float); the
+    # first and last take 3 and 2 phase groups per workgroup with two sets of
+    # accumulators, one group's stores between the next group's products
+    "k3s3_one_tap_groups2": W.make("pm", "conv_transpose3d", (8, 32, 6, 9, 13), 64, 3, 3, 1, 1, 2, groups=2,
                                    bias=True, seed=88),
     "k4s4_one_tap": W.make("pm", "conv_transpose3d", (1, 8, 3, 4, 6), 16, 4, 4, (1, 2, 3), 1, (0, 1, 3),
                            bias=True, seed=89),
     "k322s322_one_tap": W.make("pm", "conv_transpose3d", (1, 10, 4, 5, 7), 24, (3, 2, 2), (3, 2, 2), (1, 0, 1), 1,
                                (2, 1, 0), bias=True, seed=90),
+    "k4s4_one_tap_quads": W.make("pm", "conv_transpose3d", (8, 8, 5, 6, 5), 32, 4, 4, (1, 2, 0), 1, (3, 1, 0),
+                                 bias=True, seed=91),
 }
 
 
@@ -232,6 +235,7 @@ UNALIGNED_Y = {
                     seed=87),
     "triples": PHASE_MEDIUM["k3s3p1_op2_groups2"],
     "triples_one_tap": PHASE_MEDIUM["k3s3_one_tap_groups2"],
+    "quads_one_tap": PHASE_MEDIUM["k4s4_one_tap_quads"],
 }
 
 

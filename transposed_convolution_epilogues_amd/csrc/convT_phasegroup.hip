@@ -40,6 +40,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x3 __attribute__((ext_vector_type(3)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
@@ -82,6 +83,10 @@ struct GArgs {
     int32_t one_tap;          // with pg_inner: two chunks, at most 4 phases per group and one tap
                               // per phase (kernel = stride in every dim); the tap of phase p of
                               // group g is g P + p
+    int32_t one_tap_db;       // with one_tap: the P phases of a group are the dim-2 residues and
+                              // leave in one P-float store per lane and channel (vecs == P), every
+                              // channel block is full and a block's output spans < 2^31 bytes:
+                              // the stores of a group are issued between the next group's products
     float inv_e2, inv_e12, inv_kvol;  // reciprocals for the staging index splits
     int64_t x_gstride, w_gstride, y_gstride;
     // tap table: LDS offsets (floats) of each tap's weights and halo window,
@@ -470,10 +475,118 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     epilogue_of(pg, bs, ac);
                 }
             };
-            if (a.P == 3)
+            // two accumulator sets: group g + 1's products are issued between
+            // group g's stores, which are range-checked buffer stores (lanes
+            // past the output get an offset past the block), so the products
+            // and the stores form one basic block
+            auto groups_db = [&](auto npc) {
+                constexpr int NP = decltype(npc)::value;
+                using VS = typename std::conditional<NP == 3, f32x3, f32x4>::type;
+                const int64_t cst64 = (int64_t)a.O[0] * a.O[1] * a.O[2];
+                float* yblk = a.y + (int64_t)grp * a.y_gstride + (n * a.yC + oc0) * cst64;
+                const unsigned cstb = (unsigned)cst64 * 4u;  // bytes between channels
+                const __amdgpu_buffer_rsrc_t rs =
+                    __builtin_amdgcn_make_buffer_rsrc((void*)yblk, (short)0, (int)(kOCB * cstb), 0x00020000);
+                // this lane's byte offset in the block for group pg, 0x80000000 when
+                // its row or position lies past the output (every store dropped)
+                auto lane_off = [&](int pg) -> unsigned {
+                    const int res = a.gres[pg][0];
+                    const int r0 = res & 15, r1 = (res >> 4) & 15;
+                    const bool ok = p0 < a.Q[0][r0] && p1 < a.Q[1][r1] && pq < a.Q[2][0];
+                    const unsigned e = (unsigned)(((a.s[0] * p0 + r0) * a.O[1] + a.s[1] * p1 + r1) * a.O[2] + NP * pq);
+                    return ok ? e * 4u + (unsigned)(4 * h) * cstb : 0x80000000u;
+                };
+                const VA* lv = reinterpret_cast<const VA*>(lds);
+                int2 o[NP];
+                VA av[NP][2], bv[NP][2];
+                auto operands = [&]() {
+#pragma unroll
+                    for (int p = 0; p < NP; ++p)
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            av[p][c] = lv[(unsigned)(c * L::kBuf + wbase + o[p].x) / H];
+                            bv[p][c] = lv[(unsigned)(c * L::kBuf + xbase + o[p].y) / H];
+                        }
+                };
+                auto products = [&](f32x16 (&ac)[NP]) {
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        ac[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[p][0][0], bv[p][0][0], zero, 0, 0, 0);
+#pragma unroll
+                        for (int c = 0; c < 2; ++c)
+#pragma unroll
+                            for (int s = c == 0 ? 1 : 0; s < H; ++s)
+                                ac[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[p][c][s], bv[p][c][s], ac[p], 0, 0, 0);
+                    }
+                };
+                auto stores = [&](unsigned lo, const f32x16 (&ac)[NP]) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        VS v;
+#pragma unroll
+                        for (int p = 0; p < NP; ++p) v[p] = ac[p][i] + bs[i];
+                        const unsigned off = lo + (unsigned)(8 * (i >> 2) + (i & 3)) * cstb;
+                        if constexpr (NP == 3)
+                            __builtin_amdgcn_raw_buffer_store_b96(v, rs, off, 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+                    }
+                };
+                auto taps_of = [&](int pg) {
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) o[p] = taps[pg * NP + p];
+                };
+                // operand reads, then the stores of the previous group between
+                // the products of this one
+                auto interleave = [&]() {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 4 * NP, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x040, 2, 0);
+#pragma unroll
+                    for (int k = 0; k < 14; ++k) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);
+                    }
+                };
+                f32x16 acA[NP], acB[NP];
+                taps_of(pg0);
+                operands();
+                products(acA);
+                int g = pg0;
+                for (;;) {
+                    const unsigned loA = lane_off(g);
+                    if (g + 1 >= pg_end) {
+                        stores(loA, acA);
+                        break;
+                    }
+                    taps_of(g + 1);
+                    operands();
+                    products(acB);
+                    stores(loA, acA);
+                    interleave();
+                    ++g;
+                    const unsigned loB = lane_off(g);
+                    if (g + 1 >= pg_end) {
+                        stores(loB, acB);
+                        break;
+                    }
+                    taps_of(g + 1);
+                    operands();
+                    products(acA);
+                    stores(loB, acB);
+                    interleave();
+                    ++g;
+                }
+            };
+            if (a.one_tap_db) {
+                if (a.P == 3)
+                    groups_db(std::integral_constant<int, 3>{});
+                else
+                    groups_db(std::integral_constant<int, 4>{});
+            } else if (a.P == 3) {
                 groups(std::integral_constant<int, 3>{});
-            else
+            } else {
                 groups(std::integral_constant<int, 4>{});
+            }
             return;
         }
         for (int pg = pg0; pg < pg_end; ++pg) {
@@ -708,6 +821,8 @@ hipError_t launch_convT_phasegroup(const float* x, const float* w, const float* 
     }
     // the 8- and 16-byte stores need y aligned to their size
     if ((a.vecs == 2 && ((uintptr_t)y & 7) != 0) || (a.vecs == 4 && ((uintptr_t)y & 15) != 0)) a.vecs = 0;
+    a.one_tap_db = a.one_tap && a.vecs == a.P && g.cout_g % kOCB == 0 &&
+                   (int64_t)kOCB * g.O[0] * g.O[1] * g.O[2] * 4 < ((int64_t)1 << 31);
     static_assert(sizeof(GArgs) <= 4096, "kernel arguments");
     const unsigned blocks = (unsigned)grid_blocks(g, a);
     const int fk = fixed_kind(g);
