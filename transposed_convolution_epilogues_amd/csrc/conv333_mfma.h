@@ -139,7 +139,17 @@ struct XRegs {
 template <int kMT>
 struct XOffsets {
     int32_t off[Geo<kMT>::XQ];  // spatial offset in the input plane, -1 outside
+    uint32_t vo[Geo<kMT>::XQ];  // the same in bytes for buffer loads; kOutside outside
 };
+
+// A buffer load or store whose offset is at least the resource's size touches
+// no memory (a load returns 0).  Resources here are below 2^31 bytes, so an
+// offset of kOutside (plus any channel offset below 2^31) always falls outside.
+constexpr uint32_t kOutside = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 template <int kMT>
 __device__ __forceinline__ XOffsets<kMT> x_offsets(const Args& a, const Tile& t, const int32_t (&pad)[3]) {
@@ -155,6 +165,7 @@ __device__ __forceinline__ XOffsets<kMT> x_offsets(const Args& a, const Tile& t,
         const bool inb = pos < HPOS && gd >= 0 && gd < a.S[0] && gh >= 0 && gh < a.S[1] && gw >= 0 &&
                          gw < a.S[2];
         o.off[q] = inb ? (int32_t)((gd * a.S[1] + gh) * a.S[2] + gw) : -1;
+        o.vo[q] = inb ? 4u * (uint32_t)o.off[q] : kOutside;
     }
     return o;
 }
@@ -173,6 +184,52 @@ __device__ __forceinline__ void load_x_slice(const Args& a, const Tile& t, const
     const float* xc = a.x + (t.n * a.xC + (icok ? ic : 0)) * plane;  // wave-uniform
 #pragma unroll
     for (int q = 0; q < Geo<kMT>::XQ; ++q) r.v[g][q][j] = xc[o.off[q] >= 0 ? o.off[q] : 0];
+}
+
+// The same slice with buffer loads: the chunk's 8 channels form one buffer
+// resource, the channel is a uniform offset, and positions outside the input
+// read 0 by the range check (no address arithmetic per load, no zero select).
+template <int kMT>
+__device__ __forceinline__ void load_x_slice_buf(const Args& a, const Tile& t, const XOffsets<kMT>& o, int64_t ic0,
+                                                 int g, int j, XRegs<kMT>& r) {
+    const int64_t plane = a.S[0] * a.S[1] * a.S[2];
+    const int c = 4 * g + j;
+    const bool icok = (int)ic0 + c < (int)a.Cin;  // 32-bit: a scalar compare
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(a.x + (t.n * a.xC + ic0) * plane, (uint32_t)(ICC * plane * 4));
+    const int soff = icok ? (int)(c * plane * 4) : 0;
+#pragma unroll
+    for (int q = 0; q < Geo<kMT>::XQ; ++q)
+        r.v[g][q][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, o.vo[q], soff, 0));
+}
+
+template <int kMT>
+__device__ __forceinline__ void load_x_buf(const Args& a, const Tile& t, const XOffsets<kMT>& o, int64_t ic0,
+                                           XRegs<kMT>& r) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) load_x_slice_buf(a, t, o, ic0, g, j, r);
+}
+
+// LDS write of a halo loaded by buffer loads (positions outside are already 0);
+// only the channels past Cin of a partial chunk are zeroed
+template <int kMT>
+__device__ __forceinline__ void store_x_buf(const Args& a, int64_t ic0, const XRegs<kMT>& r, float* lx) {
+    constexpr int HPOS = Geo<kMT>::HPOS;
+    const bool full = (int)ic0 + ICC <= (int)a.Cin;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int q = 0; q < Geo<kMT>::XQ; ++q) {
+            const int pos = threadIdx.x + q * kThreads;
+            f32x4 v = r.v[g][q];
+            if (!full) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = (int)ic0 + 4 * g + j < (int)a.Cin ? v[j] : 0.f;
+            }
+            if (pos < HPOS) *reinterpret_cast<f32x4*>(lx + (g * HPOS + pos) * 4) = v;
+        }
 }
 
 template <int kMT>
@@ -225,6 +282,56 @@ __device__ __forceinline__ void load_w_pair(const Args& a, const Tile& t, int64_
     const float* src = a.w + (ok ? first : 0);
 #pragma unroll
     for (int u = 0; u < UNIT_TAPS; ++u) r.v[q][u] = src[u];
+}
+
+// Buffer-load form of the weight unit loads: per thread and pair a byte
+// offset fixed for the tile (kOutside for output channels past Cout), the
+// input-channel chunk and kd plane as a uniform offset, the 9 taps as
+// immediate offsets.
+struct WOffsets {
+    uint32_t vo[W_PAIRS_PER_THREAD];
+};
+
+template <int kMode>
+__device__ __forceinline__ WOffsets w_offsets(const Args& a, const Tile& t) {
+    WOffsets o;
+#pragma unroll
+    for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) {
+        const int p = threadIdx.x + q * kThreads;
+        const int oc = p >> 3, j = p & 7;
+        const int64_t goc = t.oc0 + oc;
+        // first element of the pair's run for ic0 = 0, kd = 0 (transposed: without the 18 - 9 kd)
+        const int64_t first = kMode == kConvWeights ? (goc * a.Cin + j) * 27 : ((int64_t)j * a.Cout + goc) * 27;
+        o.vo[q] = goc < a.Cout ? (uint32_t)(first * 4) : kOutside;
+    }
+    return o;
+}
+
+template <int kMode>
+__device__ __forceinline__ void load_w_pair_buf(const Args& a, const WOffsets& o, int64_t ic0, int kd, int q,
+                                                WRegs& r) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.w, (uint32_t)(a.Cout * a.Cin * 27 * 4));
+    const int64_t ue = kMode == kConvWeights ? ic0 * 27 + kd * UNIT_TAPS : ic0 * a.Cout * 27 + (18 - kd * UNIT_TAPS);
+    const int j = (threadIdx.x + q * kThreads) & 7;
+    // channels past Cin (a partial last chunk) read nothing
+    const uint32_t vo = (int)ic0 + j < (int)a.Cin ? o.vo[q] : kOutside;
+#pragma unroll
+    for (int u = 0; u < UNIT_TAPS; ++u)
+        r.v[q][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo + 4u * u, (int)(ue * 4), 0));
+}
+
+// LDS write of a weight unit loaded by buffer loads (pairs outside are already 0)
+template <int kMode>
+__device__ __forceinline__ void store_w_buf(const WRegs& r, float* lw) {
+#pragma unroll
+    for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) {
+        const int p = threadIdx.x + q * kThreads;
+        const int oc = p >> 3, j = p & 7;
+        const int nt = oc >> 5, n = oc & 31, h = j >> 2, s = j & 3;
+        float* dst = lw + ((nt * 2 + h) * 32 + n) * 4 + s;
+#pragma unroll
+        for (int u = 0; u < UNIT_TAPS; ++u) dst[(kMode == kConvWeights ? u : 8 - u) * WTAP] = r.v[q][u];
+    }
 }
 
 template <int kMode>
@@ -290,13 +397,15 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
 
     const int64_t nchunks = ceil_div(a.Cin, ICC);
     const XOffsets<kMT> xo = x_offsets<kMT>(a, t, a.pad);
+    const WOffsets wo = w_offsets<kMode>(a, t);
     {
         XRegs<kMT> xr;
         WRegs wr;
-        load_x(a, t, xo, 0, xr);
-        load_w<kMode>(a, t, 0, 0, wr);
-        store_x(a, xo, 0, xr, lx);
-        store_w<kMode>(a, t, 0, wr, lw0);
+        load_x_buf(a, t, xo, 0, xr);
+#pragma unroll
+        for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) load_w_pair_buf<kMode>(a, wo, 0, 0, q, wr);
+        store_x_buf(a, 0, xr, lx);
+        store_w_buf<kMode>(wr, lw0);
         __syncthreads();
     }
     int buf = 0;
@@ -335,9 +444,9 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
                     // burst of all of them before the first tap cost about 1% on the
                     // fused conv-pool kernel and 2% on the transposed conv.
                     __builtin_amdgcn_sched_barrier(0);
-                    if (t9 < W_PAIRS_PER_THREAD && !last_unit) load_w_pair<kMode>(a, t, nc * ICC, nkd, t9, wr);
+                    if (t9 < W_PAIRS_PER_THREAD && !last_unit) load_w_pair_buf<kMode>(a, wo, nc * ICC, nkd, t9, wr);
                     if (t9 >= 1 && kd == 2 && !last_unit)
-                        load_x_slice(a, t, xo, nc * ICC, (t9 - 1) >> 2, (t9 - 1) & 3, xr);
+                        load_x_slice_buf(a, t, xo, nc * ICC, (t9 - 1) >> 2, (t9 - 1) & 3, xr);
                     __builtin_amdgcn_sched_barrier(0);
                     // side work goes behind the first tap's MFMAs: its stores issue
                     // while the matrix core runs them (about 2% faster on the
@@ -348,11 +457,11 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
             if (last_unit) break;
             if (kd == 2) {
                 __syncthreads();  // every wave is done with this chunk's halo
-                store_x(a, xo, nc * ICC, xr, lx);
+                store_x_buf(a, nc * ICC, xr, lx);
             }
             // the other weight buffer was last read by the previous unit, which
             // every wave finished before the previous barrier
-            store_w<kMode>(a, t, nc * ICC, wr, lw0 + (buf ^ 1) * LDS_W);
+            store_w_buf<kMode>(wr, lw0 + (buf ^ 1) * LDS_W);
             __syncthreads();
             buf ^= 1;
         }
@@ -515,6 +624,12 @@ __device__ __forceinline__ void acc_voxel(int lane, int wv, int mt, int i, int& 
 }
 
 inline bool fits_int32_tiles(int64_t v) { return v > 0 && v < (1ll << 30); }
+
+// The buffer resources of the K loop stay below 2^31 bytes: one chunk of input
+// channel planes, and the whole weight tensor.
+inline bool fits_buffers(const Geom& g) {
+    return (int64_t)ICC * g.S[0] * g.S[1] * g.S[2] * 4 < (1ll << 31) && g.Cout * g.Cin * 27 * 4 < (1ll << 31);
+}
 
 }  // namespace mfma333
 }  // namespace c3d

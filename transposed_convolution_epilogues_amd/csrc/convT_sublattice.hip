@@ -323,7 +323,7 @@ bool conv3x3x3_mfma_supported(const Geom& g, const void*, const void*, const voi
     for (int j = 0; j < 3; ++j)
         if (g.k[j] != 3 || g.s[j] != 1 || g.d[j] != 1 || g.p[j] != g.p[0]) return false;
     // the MFMA tile pays off once there are several input channels
-    return g.groups == 1 && g.Cin >= 4 && g.Cout >= 8 && mfma333::fits_int32_tiles(g.O[0]) &&
+    return g.groups == 1 && g.Cin >= 4 && g.Cout >= 8 && mfma333::fits_buffers(g) && mfma333::fits_int32_tiles(g.O[0]) &&
            mfma333::fits_int32_tiles(g.O[1]) && mfma333::fits_int32_tiles(g.O[2]);
 }
 
@@ -347,7 +347,7 @@ hipError_t launch_conv3x3x3_mfma(const float* x, const float* w, const float* bi
 bool convT_s2_sublattice_supported(const Geom& g, const void*, const void*, const void*) {
     for (int j = 0; j < 3; ++j)
         if (g.k[j] != 3 || g.s[j] != 2 || g.d[j] != 2 || g.p[j] != 1 || g.O[j] != 2 * g.S[j] + 1) return false;
-    if (g.groups != 1 || g.Cout > kMaxBiasLds || !mfma333::fits_int32_tiles(g.O[0]) ||
+    if (g.groups != 1 || g.Cout > kMaxBiasLds || !mfma333::fits_buffers(g) || !mfma333::fits_int32_tiles(g.O[0]) ||
         !mfma333::fits_int32_tiles(g.O[1]) || !mfma333::fits_int32_tiles(g.O[2]))
         return false;
     // the bias pass indexes a plane in 32 bits and decodes row slots below

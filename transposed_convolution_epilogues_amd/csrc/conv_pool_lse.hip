@@ -110,7 +110,7 @@ bool conv_pool_lse_mfma_supported(const PoolGeom& pg, const void*, const void*) 
     const Geom& g = pg.g;
     for (int j = 0; j < 3; ++j)
         if (g.k[j] != 3 || g.s[j] != 1 || g.d[j] != 1 || g.p[j] != g.p[0]) return false;
-    return g.groups == 1 && g.Cout <= OCB && pg.pool == 2 && mfma333::fits_int32_tiles(g.O[0]) &&
+    return g.groups == 1 && g.Cout <= OCB && pg.pool == 2 && mfma333::fits_buffers(g) && mfma333::fits_int32_tiles(g.O[0]) &&
            mfma333::fits_int32_tiles(g.O[1]) && mfma333::fits_int32_tiles(g.O[2]);
 }
 
