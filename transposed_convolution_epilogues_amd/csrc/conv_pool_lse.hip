@@ -93,11 +93,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 m[nt] = valid[nt] ? v + bias_v[nt] : -FLT_MAX;
             }
             const float M = half_max(fmaxf(m[0], m[1]));
-            const float S = half_sum(expf(m[0] - M) + expf(m[1] - M));
-            const float L = M + logf(S);
+            // the hardware exp2 / log2 (about 1 ulp each): every term lies in
+            // (0, 1] and S in [1, 64], so the result is within a few 1e-7 of
+            // the exactly rounded one
+            const float S = half_sum(__expf(m[0] - M) + __expf(m[1] - M));
+            const float L = M + __logf(S);
             if ((lane & 31) == 0) {
-                const int64_t j2 = (t.w0 >> 1) + (wv & 1) * 8 + 4 * ax + 2 * h + (q & 1);
-                if (j0 < a.P[0] && j1 < a.P[1] && j2 < a.P[2])
+                const int j2 = (int)(t.w0 >> 1) + (wv & 1) * 8 + 4 * ax + 2 * h + (q & 1);
+                if ((int)j0 < (int)a.P[0] && (int)j1 < (int)a.P[1] && j2 < (int)a.P[2])
                     a.y[((t.n * a.P[0] + j0) * a.P[1] + j1) * a.P[2] + j2] = L > 0.f ? L : 0.f;
             }
         }
