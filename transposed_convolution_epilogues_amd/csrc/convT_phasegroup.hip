@@ -41,6 +41,15 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x3 __attribute__((ext_vector_type(3)));
+
+// A buffer load or store whose offset is at least the resource's size touches
+// no memory (a load returns 0).  Resources here are below 2^31 bytes, so an
+// offset of kOutside (plus any uniform offset below 2^31) always falls outside.
+constexpr uint32_t kOutside = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
@@ -224,37 +233,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         wel[u] = m < 2 * wrun ? wl | rem << 14 | hh << 25 | (oc0 + oc >= a.cout) << 26 : -1;
     }
 
+    // byte offsets for the staging buffer loads: a halo position in its
+    // channel plane, a weight unit's first element relative to the group's
+    // weights (input channel ic0 + s added as a uniform offset); kOutside for
+    // zero padding, no unit and channels past cout: the range check makes
+    // those loads return 0 without touching memory
+    uint32_t xvo[kHaloPer], wvo[L::kWPer];
+#pragma unroll
+    for (int u = 0; u < kHaloPer; ++u) xvo[u] = xsp[u] >= 0 ? 4u * (uint32_t)xsp[u] : kOutside;
+#pragma unroll
+    for (int u = 0; u < L::kWPer; ++u) {
+        const int v = wel[u];
+        const int hh = (v >> 25) & 1, off = wbase0 + ((v >> 14) & 2047);
+        wvo[u] = v >= 0 && !((v >> 26) & 1) ? 4u * (uint32_t)(hh * H * wic + off) : kOutside;
+    }
+    const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(wg, (uint32_t)(a.w_gstride * 4));
+
     using XR = float[kHaloPer][ICC];
     using WR = float[L::kWPer][H];
     float xr[kHaloPer][ICC];
     float wr[L::kWPer][H];
-    // a chunk's halo and weights into registers xr_, wr_
+    // a chunk's halo and weights into registers xr_, wr_ (buffer loads: no
+    // address arithmetic per load); channels past cin (a partial last chunk)
+    // read channel ic0 of the halo, zeroed when stored, and nothing of the weights
     auto load_to = [&](int c, XR& xr_, WR& wr_) {
         const int ic0 = c * ICC;
+        const bool full = ic0 + ICC <= a.cin;
+        const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(xg + (int64_t)ic0 * plane, (uint32_t)(ICC * plane * 4));
 #pragma unroll
         for (int i = 0; i < ICC; ++i) {
-            const float* xc = xg + (ic0 + i < a.cin ? ic0 + i : 0) * plane;
+            const int soff = ic0 + i < a.cin ? (int)(i * plane * 4) : 0;
 #pragma unroll
-            for (int u = 0; u < kHaloPer; ++u) xr_[u][i] = xc[xsp[u] >= 0 ? xsp[u] : 0];
+            for (int u = 0; u < kHaloPer; ++u)
+                xr_[u][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xrs, xvo[u], soff, 0));
         }
-        // units of output channels past cout, and channels past cin (the
-        // last chunk), read element 0
-        const float* wc = wg + (int64_t)ic0 * wic;
 #pragma unroll
         for (int u = 0; u < L::kWPer; ++u) {
-            const int v = wel[u];
-            const int hh = (v >> 25) & 1, off = wbase0 + ((v >> 14) & 2047);
-            const bool ok = v >= 0 && !((v >> 26) & 1);
+            const int hh = (wel[u] >> 25) & 1;
 #pragma unroll
             for (int s = 0; s < H; ++s) {
-                const int icl = hh * H + s;
-                wr_[u][s] = wc[ok && ic0 + icl < a.cin ? icl * wic + off : 0];
+                const uint32_t vo = full || ic0 + hh * H + s < a.cin ? wvo[u] : kOutside;
+                wr_[u][s] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(wrs, vo, (int)((ic0 + s) * wic * 4), 0));
             }
         }
     };
     // registers xr_, wr_ of chunk c into LDS buffer buf
     auto store_from = [&](int c, float* buf, const XR& xr_, const WR& wr_) {
         const int ic0 = c * ICC;
+        const bool full = ic0 + ICC <= a.cin;
 #pragma unroll
         for (int u = 0; u < kHaloPer; ++u) {
             if (xlp[u] < 0) continue;
@@ -262,7 +289,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int hh = 0; hh < 2; ++hh) {
                 VA v;
 #pragma unroll
-                for (int s = 0; s < H; ++s) v[s] = (xsp[u] >= 0 && ic0 + hh * H + s < a.cin) ? xr_[u][hh * H + s] : 0.f;
+                for (int s = 0; s < H; ++s) v[s] = xr_[u][hh * H + s];
+                if (!full) {
+#pragma unroll
+                    for (int s = 0; s < H; ++s) v[s] = ic0 + hh * H + s < a.cin ? v[s] : 0.f;
+                }
                 *reinterpret_cast<VA*>(buf + (hh * kHPos + xlp[u]) * H) = v;
             }
         }
@@ -271,11 +302,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int u = 0; u < L::kWPer; ++u) {
             const int v = wel[u];
             if (v < 0) continue;
-            const int hh = (v >> 25) & 1;
-            const bool ok = !((v >> 26) & 1);
             VA x;
 #pragma unroll
-            for (int s = 0; s < H; ++s) x[s] = (ok && ic0 + hh * H + s < a.cin) ? wr_[u][s] : 0.f;
+            for (int s = 0; s < H; ++s) x[s] = wr_[u][s];
             *reinterpret_cast<VA*>(wb + (v & 16383)) = x;
         }
     };
@@ -753,8 +782,12 @@ bool build_gargs(const Geom& g, GArgs& a) {
     a.x_gstride = (int64_t)g.cin_g * g.S[0] * g.S[1] * g.S[2];
     a.w_gstride = (int64_t)g.cin_g * g.cout_g * kvol;
     a.y_gstride = (int64_t)g.cout_g * g.O[0] * g.O[1] * g.O[2];
-    // 32-bit offsets inside the kernel: a chunk's weights and an input plane
+    // 32-bit offsets inside the kernel: a chunk's weights and an input plane;
+    // the staging buffer resources (a chunk of input planes, a group's
+    // weights) stay below 2^31 bytes
     if ((int64_t)ICC * g.cout_g * kvol > INT_MAX || g.S[0] * g.S[1] * g.S[2] > INT_MAX) return false;
+    if ((int64_t)ICC * g.S[0] * g.S[1] * g.S[2] * 4 >= ((int64_t)1 << 31) || a.w_gstride * 4 >= ((int64_t)1 << 31))
+        return false;
     return true;
 }
 
