@@ -327,8 +327,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int64_t O1 = a.O[1], O2 = a.O[2];
     const int64_t cst = (int64_t)a.O[0] * O1 * O2;  // floats between output channels
     const int p0 = q0 + lr0, p1 = q1 + lr1, pq = q2 + lp;
-    const bool all_oc = oc0 + kOCB <= a.cout;       // uniform
-    float* yb = a.y + (int64_t)grp * a.y_gstride + (n * a.yC + oc0 + 4 * h) * cst;
     auto load_bias = [&](float (&bs)[16]) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -337,6 +335,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     };
     // the accumulators A of group pg (NA = kMaxPh, or 4 on the one-tap path)
+    // the stores are buffer stores into this workgroup's output channels
+    // oc0 .. (one resource ending at the last channel below cout): a lane past
+    // the output in any dim gets offset kOutside, so every store is one
+    // instruction with one address add and no branch
+    const unsigned cstb = (unsigned)cst * 4u;  // bytes between output channels
+    const int nvalid = a.cout - oc0 < kOCB ? a.cout - oc0 : kOCB;
+    const __amdgpu_buffer_rsrc_t yrs =
+        buffer_rsrc(a.y + (int64_t)grp * a.y_gstride + (n * a.yC + oc0) * cst, (uint32_t)nvalid * cstb);
     auto epilogue_of = [&](int pg, const float (&bs)[16], auto& A) {
         constexpr int NA = std::extent<std::remove_reference_t<decltype(A)>>::value;
         const int vs = a.vecs;
@@ -346,28 +352,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             if (vs && p % vs != 0) continue;
             const int res = a.gres[pg][p];
             const int r0 = res & 15, r1 = (res >> 4) & 15, r2 = res >> 8;
-            if (p0 >= a.Q[0][r0] || p1 >= a.Q[1][r1]) continue;
-            const int64_t row = ((int64_t)(a.s[0] * p0 + r0) * O1 + (a.s[1] * p1 + r1)) * O2;
             // the residues of dim 2 are phases p .. p + vs - 1 when vs > 1
-            if (pq >= a.Q[2][vs ? 0 : r2]) continue;
-            float* rp = yb + row + (vs ? (int64_t)vs * pq : (int64_t)a.s[2] * pq + r2);
+            const bool ok = p0 < a.Q[0][r0] && p1 < a.Q[1][r1] && pq < a.Q[2][vs ? 0 : r2];
+            const int64_t e = ((int64_t)(a.s[0] * p0 + r0) * O1 + (a.s[1] * p1 + r1)) * O2 +
+                              (vs ? (int64_t)vs * pq : (int64_t)a.s[2] * pq + r2);
+            const unsigned lo = ok ? (unsigned)e * 4u + (unsigned)(4 * h) * cstb : kOutside;
             const int q1i = (p + 1) & (NA - 1), q2i = (p + 2) & (NA - 1), q3i = (p + 3) & (NA - 1);
+            if (vs == 2) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (!all_oc && oc0 + 8 * (i >> 2) + 4 * h + (i & 3) >= a.cout) continue;
-                float* dst = rp + (8 * (i >> 2) + (i & 3)) * cst;
-                if (vs == 2) {
-                    *reinterpret_cast<f32x2*>(dst) = f32x2{A[p][i] + bs[i], A[q1i][i] + bs[i]};
-                } else if (vs == 4) {
-                    *reinterpret_cast<f32x4*>(dst) =
-                        f32x4{A[p][i] + bs[i], A[q1i][i] + bs[i], A[q2i][i] + bs[i], A[q3i][i] + bs[i]};
-                } else if (vs == 3) {
-                    dst[0] = A[p][i] + bs[i];
-                    dst[1] = A[q1i][i] + bs[i];
-                    dst[2] = A[q2i][i] + bs[i];
-                } else {
-                    dst[0] = A[p][i] + bs[i];
-                }
+                for (int i = 0; i < 16; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b64(f32x2{A[p][i] + bs[i], A[q1i][i] + bs[i]}, yrs,
+                                                          lo + (unsigned)(8 * (i >> 2) + (i & 3)) * cstb, 0, 0);
+            } else if (vs == 4) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        f32x4{A[p][i] + bs[i], A[q1i][i] + bs[i], A[q2i][i] + bs[i], A[q3i][i] + bs[i]}, yrs,
+                        lo + (unsigned)(8 * (i >> 2) + (i & 3)) * cstb, 0, 0);
+            } else if (vs == 3) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b96(f32x3{A[p][i] + bs[i], A[q1i][i] + bs[i], A[q2i][i] + bs[i]},
+                                                          yrs, lo + (unsigned)(8 * (i >> 2) + (i & 3)) * cstb, 0, 0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(A[p][i] + bs[i]), yrs,
+                                                          lo + (unsigned)(8 * (i >> 2) + (i & 3)) * cstb, 0, 0);
             }
         }
     };
@@ -788,6 +799,8 @@ bool build_gargs(const Geom& g, GArgs& a) {
     if ((int64_t)ICC * g.cout_g * kvol > INT_MAX || g.S[0] * g.S[1] * g.S[2] > INT_MAX) return false;
     if ((int64_t)ICC * g.S[0] * g.S[1] * g.S[2] * 4 >= ((int64_t)1 << 31) || a.w_gstride * 4 >= ((int64_t)1 << 31))
         return false;
+    // and the output resource of a workgroup's channel block
+    if ((int64_t)kOCB * g.O[0] * g.O[1] * g.O[2] * 4 >= ((int64_t)1 << 31)) return false;
     return true;
 }
 
