@@ -46,7 +46,18 @@ struct K1Args {
     int32_t R, RL, E;   // staged input rows per workgroup, staged row length, staged floats
     int32_t groups;     // row groups per (n, ocb): ceil(O0 / kRows)
     int32_t chunks;     // position chunks per row: ceil(J / kChunk)
+    // staged-box offset of tap k (input channel ic, kernel row k0, kernel column
+    // k1): (ic R + k0 d0) RL + k1 d1 S2; entries k >= K repeat entry 0
+    int32_t toff[2 * kMaxSteps];
 };
+
+// A buffer load whose offset is at least the resource's size touches no
+// memory and returns 0; the resources here are below 2^31 bytes.
+constexpr uint32_t kOutside = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 // Block of 128 output positions.  N tile t's column c is position j0 + 4c + t,
 // so after the MFMAs a lane holds 4 consecutive positions of each of its 16
@@ -94,28 +105,38 @@ __device__ __forceinline__ void store_block(float* yb, uint32_t ystride, const f
 // keep the HBM write queue full.  Box elements past the end of an input row or
 // below the last input row feed only outputs that are never stored, so their
 // loads are merely clamped into the image.
-__device__ __forceinline__ void stage(const K1Args& a, const float* xi, int64_t o0b, int64_t jc0, float* lds) {
-    constexpr int kBatch = 16;
-    const int32_t last = (int32_t)(a.Cin * a.S0 * a.S1S2 - 1);  // last element of this image
-    for (int e0 = 0; e0 < a.E; e0 += kBatch * kThreads) {
-        float v[kBatch];
+// The box is staged row by row: row pr = (ic, row) of the box starts at a
+// uniform offset of sample n's input, so every load is a buffer load at a
+// per-thread constant column offset and costs no index arithmetic; four rows'
+// loads are in flight before they are written.  Rows past the last input row
+// and columns past the end of a row read whatever lies there (or 0 past the
+// end of the sample).
+__device__ __forceinline__ void stage(const K1Args& a, const __amdgpu_buffer_rsrc_t& xs, int64_t o0b, int64_t jc0,
+                                      float* lds) {
+    constexpr int kPB = 4;   // box rows per batch
+    constexpr int kCI = 3;   // 256-column steps per row and batch
+    const int pairs = (int)a.Cin * a.R;
+    for (int c0 = 0; c0 < a.RL; c0 += kCI * kThreads)
+        for (int pr0 = 0; pr0 < pairs; pr0 += kPB) {
+            float v[kPB][kCI];
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            const int e = e0 + q * kThreads + threadIdx.x;
-            const int ic = e / (a.R * a.RL);
-            const int rem = e - ic * (a.R * a.RL);
-            const int row = rem / a.RL;
-            const int col = rem - row * a.RL;
-            const int64_t irow = o0b + row;
-            const int64_t g = (ic * a.S0 + irow) * a.S1S2 + jc0 + col;
-            v[q] = xi[g < last ? g : last];
-        }
+            for (int pb = 0; pb < kPB; ++pb) {
+                const int pr = pr0 + pb < pairs ? pr0 + pb : pairs - 1;
+                const int ic = pr / a.R, row = pr - ic * a.R;
+                const uint32_t soff = (uint32_t)(((ic * a.S0 + o0b + row) * a.S1S2 + jc0 + c0) * 4);
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-            const int e = e0 + q * kThreads + threadIdx.x;
-            if (e < a.E) lds[e] = v[q];
+                for (int ci = 0; ci < kCI; ++ci)
+                    v[pb][ci] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        xs, 4u * (uint32_t)(threadIdx.x + ci * kThreads), (int)soff, 0));
+            }
+#pragma unroll
+            for (int pb = 0; pb < kPB; ++pb)
+#pragma unroll
+                for (int ci = 0; ci < kCI; ++ci) {
+                    const int col = c0 + (int)threadIdx.x + ci * kThreads;
+                    if (pr0 + pb < pairs && col < a.RL) lds[(pr0 + pb) * a.RL + col] = v[pb][ci];
+                }
         }
-    }
 }
 
 template <int kSteps, bool kBias, bool kVec>
@@ -150,29 +171,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int64_t n = b / a.ocb;
     const int64_t o0b = kRows * grp;        // first output row of this workgroup
     const int64_t jc0 = chunk * kChunk;     // first position of this workgroup
-    const float* xi = a.x + n * a.Cin * a.S0 * a.S1S2;
-    stage(a, xi, o0b, jc0, lds);
+    const int64_t img = a.Cin * a.S0 * a.S1S2;  // floats per sample
+    stage(a, buffer_rsrc(a.x + n * img, (uint32_t)(img * 4)), o0b, jc0, lds);
     __syncthreads();
 
     // A operand (weights): lane holds W[oc][k] with oc = 64*ocb + 32*mt + r and
-    // k = 2s + h.  Padding rows k >= K get a zero weight and read a valid
-    // staged element.
+    // k = 2s + h (buffer loads at immediate offsets 8s; channels past Cout read
+    // 0).  Padding rows k >= K get a zero weight and read a valid staged element.
     float wa[2][kSteps];
     int loff[kSteps];
+    const __amdgpu_buffer_rsrc_t ws = buffer_rsrc(a.w, (uint32_t)(a.Cout * a.K * 4));
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int oc = 64 * (int)ocb + 32 * mt + r;
+        const uint32_t vo = oc < a.Cout ? 4u * (uint32_t)(oc * a.K + h) : kOutside;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+            wa[mt][s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ws, vo + 8u * s, 0, 0));
+    }
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-        const int k = 2 * s + h;
-        const bool kv = k < a.K;
-        const int kk = kv ? k : 0;
-        const int k1 = kk % a.k1n;
-        const int k0 = (kk / a.k1n) % a.k0n;
-        const int ic = kk / (a.k1n * a.k0n);
-        loff[s] = (ic * a.R + k0 * a.d0) * a.RL + k1 * a.d1S2 + 128 * wave + 4 * r;
+        const bool kv = 2 * s + h < a.K;
+        loff[s] = (h ? a.toff[2 * s + 1] : a.toff[2 * s]) + 128 * wave + 4 * r;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int64_t oc = 64 * ocb + 32 * mt + r;
-            wa[mt][s] = (kv && oc < a.Cout) ? a.w[oc * a.K + k] : 0.f;
-        }
+        for (int mt = 0; mt < 2; ++mt) wa[mt][s] = kv ? wa[mt][s] : 0.f;
     }
     // bias of the 32 output channels whose accumulators this lane holds
     float brow[2][16];
@@ -240,7 +262,8 @@ bool conv_k1last_supported(const Geom& g, const void*, const void*, const void*)
     // MFMA pays off with many output channels; K must fit the VGPR-resident
     // weights, the staged box the LDS, and offsets 32 bits
     return K >= 2 && K <= 2 * kMaxSteps && g.Cout >= 16 && E <= kMaxE &&
-           g.Cin * g.S[0] * g.S[1] * g.S[2] < (1ll << 30) && 64 * g.O[0] * g.O[1] * g.S[2] < (1ll << 30);
+           g.Cin * g.S[0] * g.S[1] * g.S[2] < (1ll << 28) && g.Cout * K < (1ll << 28) &&
+           64 * g.O[0] * g.O[1] * g.S[2] < (1ll << 30);
 }
 
 hipError_t launch_conv_k1last(const float* x, const float* w, const float* bias, float* y, const Geom& g,
@@ -268,6 +291,11 @@ hipError_t launch_conv_k1last(const float* x, const float* w, const float* bias,
     a.E = (int32_t)(g.Cin * a.R * a.RL);
     a.groups = (int32_t)ceil_div(g.O[0], kRows);
     a.chunks = (int32_t)ceil_div(a.J, kChunk);
+    for (int k = 0; k < 2 * kMaxSteps; ++k) {
+        const int kk = k < a.K ? k : 0;
+        const int k1 = kk % a.k1n, k0 = (kk / a.k1n) % a.k0n, ic = kk / (a.k1n * a.k0n);
+        a.toff[k] = (ic * a.R + k0 * a.d0) * a.RL + k1 * a.d1S2;
+    }
     const int64_t blocks = g.N * a.ocb * (int64_t)a.groups * a.chunks;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const int steps = (a.K + 1) / 2;
