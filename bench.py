@@ -89,6 +89,9 @@ def main():
                     help="with --widen: skip the generic-kernel comparison (profiling runs)")
     ap.add_argument("--probe-mfma", action="store_true",
                     help="time the library's fp32 matrix-core throughput probe and print its TFLOP/s")
+    ap.add_argument("--probe-valu", action="store_true",
+                    help="time the probe with 0, 2, 4, 8 and 16 independent FMAs after every 4 MFMAs of a wave "
+                         "(the cost of non-MFMA vector work beside the matrix cores) and print one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--widen", action="store_true",
@@ -108,6 +111,9 @@ def main():
         return
     if args.probe_mfma:
         probe_mfma(torch)
+        return
+    if args.probe_valu:
+        probe_valu(torch)
         return
     if args.widen:
         widen(torch, args)
@@ -287,6 +293,32 @@ def measure_probe(torch, reps=10):
 
 def probe_mfma(torch):
     print(json.dumps(measure_probe(torch)), flush=True)
+
+
+def probe_valu(torch, reps=7):
+    """MFMA throughput of the probe with v FMAs after every 4 MFMAs of a wave."""
+    from transposed_convolution_epilogues_amd import binding as B
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    iters = 2000
+    rows = []
+    for v in (0, 2, 4, 8, 16):
+        call = (lambda: B.probe_mfma_f32(iters, out)) if v == 0 else (lambda: B.probe_mfma_valu_f32(iters, v, out))
+        for _ in range(2):
+            flop = call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        med = ts[len(ts) // 2]
+        rows.append({"valu_per_mfma": v / 4, "ms_median": round(med, 4),
+                     "mfma_tflops": round(flop / (med * 1e-3) / 1e12, 2)})
+    print(json.dumps({"probe": "mfma_f32_32x32x2 with independent v_fma_f32 beside it", "rows": rows}), flush=True)
 
 
 def gpu_clocks():

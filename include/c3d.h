@@ -253,6 +253,15 @@ int c3d_set_variant(int variant);
  * nothing is launched then.  Time it with events on the same stream. */
 c3d_status c3d_probe_mfma_f32(int64_t iters, float* out, int64_t out_len, int64_t* flop, void* stream);
 
+/* Diagnostic: the same probe with valu_per_4 (2, 4, 8 or 16) independent
+ * fp32 FMAs on other registers after every 4 MFMAs of a wave, to measure what
+ * non-MFMA vector work beside the matrix cores costs them (not part of any
+ * operator).  Same launch, out, *flop (MFMA FLOP only) and output values as
+ * c3d_probe_mfma_f32.  Errors: as c3d_probe_mfma_f32, and C3D_ERR_PARAM for
+ * any other valu_per_4; nothing is launched then. */
+c3d_status c3d_probe_mfma_valu_f32(int64_t iters, int32_t valu_per_4, float* out, int64_t out_len, int64_t* flop,
+                                   void* stream);
+
 /* Kernel a call would use (under the current variant), for tests and
  * tuning; host-only, launches nothing. */
 enum {

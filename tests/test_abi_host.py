@@ -188,7 +188,7 @@ def test_binding_rejects_cpu_tensors():
 
 # ------------------------------------------- binding validation before launch
 LAUNCHES = ("conv3d_fwd", "conv_transpose3d_fwd", "convT_bn_avgpool", "convT_bn_avgpool_ex",
-            "conv_maxpool_lse_relu", "c3d_probe_mfma_f32")
+            "conv_maxpool_lse_relu", "c3d_probe_mfma_f32", "c3d_probe_mfma_valu_f32")
 
 
 class _NoLaunch:
@@ -329,6 +329,8 @@ def test_well_shaped_host_tensors_stop_at_the_device_check(no_launch):
                            running_mean=_z(16), running_var=_z(16))
     with pytest.raises(TypeError):
         B.probe_mfma_f32(10, _z(1 << 19))
+    with pytest.raises(TypeError):
+        B.probe_mfma_valu_f32(10, 4, _z(1 << 19))
 
 
 def test_variant_override_is_per_thread():
@@ -453,6 +455,20 @@ def test_mfma_probe_rejects_bad_arguments_before_launching():
     assert lib.c3d_probe_mfma_f32(0, fake, 1 << 20, ctypes.byref(flop), None) == _code("C3D_ERR_PARAM")
     assert lib.c3d_probe_mfma_f32(10, fake, 1000, ctypes.byref(flop), None) == _code("C3D_ERR_PARAM")
     assert lib.c3d_probe_mfma_f32(10, ctypes.c_void_p(4098), 1 << 20, ctypes.byref(flop), None) == \
+        _code("C3D_ERR_ALIGN")
+
+
+def test_mfma_valu_probe_rejects_bad_arguments_before_launching():
+    lib = B.library()
+    flop = ctypes.c_int64(0)
+    fake = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+    assert lib.c3d_probe_mfma_valu_f32(10, 4, None, 1 << 20, ctypes.byref(flop), None) == 1  # C3D_ERR_NULL
+    for bad in (0, 1, 3, 5, 32, -4):
+        assert lib.c3d_probe_mfma_valu_f32(10, bad, fake, 1 << 20, ctypes.byref(flop), None) == \
+            _code("C3D_ERR_PARAM"), bad
+    assert lib.c3d_probe_mfma_valu_f32(0, 4, fake, 1 << 20, ctypes.byref(flop), None) == _code("C3D_ERR_PARAM")
+    assert lib.c3d_probe_mfma_valu_f32(10, 4, fake, 1000, ctypes.byref(flop), None) == _code("C3D_ERR_PARAM")
+    assert lib.c3d_probe_mfma_valu_f32(10, 4, ctypes.c_void_p(4098), 1 << 20, ctypes.byref(flop), None) == \
         _code("C3D_ERR_ALIGN")
 
 

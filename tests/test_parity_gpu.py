@@ -765,3 +765,16 @@ def test_mfma_probe_matches_its_closed_form():
     got = out.view(-1, 256).cpu().numpy()
     np.testing.assert_allclose(got[:, :64], np.broadcast_to(want, (2048, 64)), rtol=1e-5, atol=1e-6)
     np.testing.assert_allclose(got[:, 64:128], got[:, :64], rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("valu_per_4", [2, 4, 8, 16])
+def test_mfma_valu_probe_keeps_the_mfma_results(valu_per_4):
+    """The probe variant with FMAs beside the MFMAs does the same MFMA work
+    (same FLOP count, bit-identical sums)."""
+    iters = 3
+    ref = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    out = torch.full((2048 * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    flop = B.probe_mfma_f32(iters, ref)
+    assert B.probe_mfma_valu_f32(iters, valu_per_4, out) == flop
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)

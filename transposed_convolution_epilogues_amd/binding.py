@@ -29,7 +29,7 @@ EXPORTS = ("c3d_conv3d_out_dims", "c3d_conv_transpose3d_out_dims", "c3d_convT_bn
            "conv_maxpool_lse_relu",
            "c3d_status_str",
            "c3d_set_variant", "c3d_conv3d_algo", "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo",
-           "c3d_probe_mfma_f32")
+           "c3d_probe_mfma_f32", "c3d_probe_mfma_valu_f32")
 
 ALGO = {0: "direct", 1: "k1last", 2: "mfma333", 3: "sublattice", 4: "phase", 5: "bn_cells", 6: "bn_swap",
         7: "scatter", 8: "bn_mfma", 9: "phase_group"}
@@ -109,12 +109,13 @@ def _lib():
     lib.c3d_conv_transpose3d_algo.argtypes = [i64p, i64, P, i32p]
     lib.c3d_convT_bn_avgpool_algo.argtypes = [i64p, i64, P, ctypes.c_int32, i32p]
     lib.c3d_probe_mfma_f32.argtypes = [i64, ctypes.c_void_p, i64, i64p, ctypes.c_void_p]
+    lib.c3d_probe_mfma_valu_f32.argtypes = [i64, ctypes.c_int32, ctypes.c_void_p, i64, i64p, ctypes.c_void_p]
     for name in ("c3d_conv3d_out_dims", "c3d_conv_transpose3d_out_dims", "c3d_convT_bn_avgpool_out_dims",
                  "c3d_conv_maxpool_lse_relu_out_dims", "conv3d_fwd", "conv_transpose3d_fwd",
                  "convT_bn_avgpool", "convT_bn_avgpool_ex", "conv_maxpool_lse_relu", "c3d_set_variant",
                  "c3d_conv3d_algo",
                  "c3d_conv_transpose3d_algo", "c3d_convT_bn_avgpool_algo", "c3d_probe_mfma_f32",
-                 "convT_bn_avgpool_noalloc"):
+                 "c3d_probe_mfma_valu_f32", "convT_bn_avgpool_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -255,6 +256,19 @@ def probe_mfma_f32(iters: int, out: torch.Tensor, stream=None) -> int:
         raise TypeError("out must be a contiguous float32 tensor on the GPU")
     _check(_lib().c3d_probe_mfma_f32(int(iters), ctypes.c_void_p(out.data_ptr()), int(out.numel()),
                                      ctypes.byref(flop), _stream(stream)), "c3d_probe_mfma_f32")
+    return int(flop.value)
+
+
+def probe_mfma_valu_f32(iters: int, valu_per_4: int, out: torch.Tensor, stream=None) -> int:
+    """Launch the probe with valu_per_4 independent FMAs after every 4 MFMAs
+    of a wave; returns the launch's MFMA FLOP count."""
+    flop = ctypes.c_int64(0)
+    out = _tensor(out, "out")
+    if out.dtype != torch.float32 or out.device.type != "cuda" or not out.is_contiguous():
+        raise TypeError("out must be a contiguous float32 tensor on the GPU")
+    _check(_lib().c3d_probe_mfma_valu_f32(int(iters), int(valu_per_4), ctypes.c_void_p(out.data_ptr()),
+                                          int(out.numel()), ctypes.byref(flop), _stream(stream)),
+           "c3d_probe_mfma_valu_f32")
     return int(flop.value)
 
 

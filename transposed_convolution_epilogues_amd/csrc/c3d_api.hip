@@ -207,6 +207,17 @@ c3d_status c3d_probe_mfma_f32(int64_t iters, float* out, int64_t out_len, int64_
     return hip_status(c3d::launch_mfma_probe(iters, out, (hipStream_t)stream));
 }
 
+c3d_status c3d_probe_mfma_valu_f32(int64_t iters, int32_t valu_per_4, float* out, int64_t out_len, int64_t* flop,
+                                   void* stream) {
+    if (!out || !flop) return C3D_ERR_NULL;
+    if (!aligned4(out)) return C3D_ERR_ALIGN;
+    if (iters < 1 || iters > ((int64_t)1 << 24) || out_len < c3d::mfma_probe_out_len() ||
+        !c3d::mfma_valu_probe_supported(valu_per_4))
+        return C3D_ERR_PARAM;
+    *flop = c3d::mfma_probe_flop(iters);
+    return hip_status(c3d::launch_mfma_valu_probe(iters, valu_per_4, out, (hipStream_t)stream));
+}
+
 const char* c3d_status_str(c3d_status status) {
     switch (status) {
         case C3D_OK: return "ok";

@@ -73,6 +73,8 @@ constexpr int kProbeWorkgroups = 2048;
 int64_t mfma_probe_out_len();
 int64_t mfma_probe_flop(int64_t iters);
 hipError_t launch_mfma_probe(int64_t iters, float* out, hipStream_t st);
+bool mfma_valu_probe_supported(int32_t valu_per_4);
+hipError_t launch_mfma_valu_probe(int64_t iters, int32_t valu_per_4, float* out, hipStream_t st);
 hipError_t launch_convT_bn_pool_phase1_direct(const float* x, const float* w, float* y, double* ws,
                                               const PoolGeom& pg, const BnEval& ev, hipStream_t st);
 hipError_t launch_bn_pool_phase2(float* y, const double* ws, int64_t parts_per_channel, const float* conv_bias,
