@@ -207,6 +207,9 @@ PHASE_MEDIUM = {
                                (2, 1, 0), bias=True, seed=90),
     "k4s4_one_tap_quads": W.make("pm", "conv_transpose3d", (8, 8, 5, 6, 5), 32, 4, 4, (1, 2, 0), 1, (3, 1, 0),
                                  bias=True, seed=91),
+    # two full 32-channel blocks on the two-accumulator path
+    "k3s3_one_tap_two_blocks": W.make("pm", "conv_transpose3d", (2, 16, 3, 4, 10), 64, 3, 3, 1, 1, (1, 2, 2),
+                                      bias=True, seed=92),
 }
 
 

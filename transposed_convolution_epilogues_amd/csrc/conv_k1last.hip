@@ -106,11 +106,11 @@ __device__ __forceinline__ void store_block(float* yb, uint32_t ystride, const f
 // below the last input row feed only outputs that are never stored, so their
 // loads are merely clamped into the image.
 // The box is staged row by row: row pr = (ic, row) of the box starts at a
-// uniform offset of sample n's input, so every load is a buffer load at a
-// per-thread constant column offset and costs no index arithmetic; four rows'
-// loads are in flight before they are written.  Rows past the last input row
-// and columns past the end of a row read whatever lies there (or 0 past the
-// end of the sample).
+// uniform element offset of sample n's input, so every load is a buffer load
+// at that offset plus the thread's column (one add); four rows' loads are in
+// flight before they are written.  Rows past the last input row and columns
+// past the end of a row read whatever lies there, and offsets past the end of
+// the sample read 0 (the whole offset is in the range-checked operand).
 __device__ __forceinline__ void stage(const K1Args& a, const __amdgpu_buffer_rsrc_t& xs, int64_t o0b, int64_t jc0,
                                       float* lds) {
     constexpr int kPB = 4;   // box rows per batch
@@ -123,11 +123,11 @@ __device__ __forceinline__ void stage(const K1Args& a, const __amdgpu_buffer_rsr
             for (int pb = 0; pb < kPB; ++pb) {
                 const int pr = pr0 + pb < pairs ? pr0 + pb : pairs - 1;
                 const int ic = pr / a.R, row = pr - ic * a.R;
-                const uint32_t soff = (uint32_t)(((ic * a.S0 + o0b + row) * a.S1S2 + jc0 + c0) * 4);
+                const uint32_t rbase = (uint32_t)((ic * a.S0 + o0b + row) * a.S1S2 + jc0 + c0);
 #pragma unroll
                 for (int ci = 0; ci < kCI; ++ci)
                     v[pb][ci] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                        xs, 4u * (uint32_t)(threadIdx.x + ci * kThreads), (int)soff, 0));
+                        xs, 4u * (rbase + threadIdx.x + ci * kThreads), 0, 0));
             }
 #pragma unroll
             for (int pb = 0; pb < kPB; ++pb)
