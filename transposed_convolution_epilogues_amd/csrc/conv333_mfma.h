@@ -127,10 +127,10 @@ __device__ __forceinline__ Tile tile_of(const Args& a) {
 
 // Input halo of one chunk, as two 4-channel groups: LDS layout [g][pos][4]
 // holds channels ic0 + 4g .. ic0 + 4g + 3 of halo position pos.  A thread
-// owns positions tid + 256q; the channel base pointers are wave-uniform, so a
-// thread keeps only its position offsets.  Loads are unconditional
-// (out-of-range positions read a clamped, valid address and are replaced by 0
-// with a select).
+// owns positions tid + 256q; the channel offsets are wave-uniform, so a
+// thread keeps only its position offsets.  Loads are unconditional buffer
+// loads: positions outside the input carry an offset past the resource and
+// read 0.
 template <int kMT>
 struct XRegs {
     f32x4 v[2][Geo<kMT>::XQ];
@@ -168,22 +168,6 @@ __device__ __forceinline__ XOffsets<kMT> x_offsets(const Args& a, const Tile& t,
         o.vo[q] = inb ? 4u * (uint32_t)o.off[q] : kOutside;
     }
     return o;
-}
-
-// The loads leave the raw values in registers; the zero padding is applied
-// when they are written to LDS.  A select right after a load would make the
-// wave wait for the load there, while the loads are meant to stay in flight
-// under a whole unit of MFMA work.
-// Channel ic0 + 4g + j of the halo (one of the 8 slices of a chunk's loads).
-template <int kMT>
-__device__ __forceinline__ void load_x_slice(const Args& a, const Tile& t, const XOffsets<kMT>& o, int64_t ic0,
-                                             int g, int j, XRegs<kMT>& r) {
-    const int64_t plane = a.S[0] * a.S[1] * a.S[2];
-    const int64_t ic = ic0 + 4 * g + j;
-    const bool icok = ic < a.Cin;
-    const float* xc = a.x + (t.n * a.xC + (icok ? ic : 0)) * plane;  // wave-uniform
-#pragma unroll
-    for (int q = 0; q < Geo<kMT>::XQ; ++q) r.v[g][q][j] = xc[o.off[q] >= 0 ? o.off[q] : 0];
 }
 
 // The same slice with buffer loads: the chunk's 8 channels form one buffer
@@ -232,31 +216,6 @@ __device__ __forceinline__ void store_x_buf(const Args& a, int64_t ic0, const XR
         }
 }
 
-template <int kMT>
-__device__ __forceinline__ void load_x(const Args& a, const Tile& t, const XOffsets<kMT>& o, int64_t ic0,
-                                       XRegs<kMT>& r) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) load_x_slice(a, t, o, ic0, g, j, r);
-}
-
-template <int kMT>
-__device__ __forceinline__ void store_x(const Args& a, const XOffsets<kMT>& o, int64_t ic0, const XRegs<kMT>& r,
-                                        float* lx) {
-    constexpr int HPOS = Geo<kMT>::HPOS;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int q = 0; q < Geo<kMT>::XQ; ++q) {
-            const int pos = threadIdx.x + q * kThreads;
-            f32x4 v;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = (ic0 + 4 * g + j < a.Cin && o.off[q] >= 0) ? r.v[g][q][j] : 0.f;
-            if (pos < HPOS) *reinterpret_cast<f32x4*>(lx + (g * HPOS + pos) * 4) = v;
-        }
-}
-
 // One weight unit: the 9 taps (kd, *, *) of 8 input channels x 64 output
 // channels, LDS layout [tap % 9][nt][h][n][s] with oc = oc0 + 32nt + n and
 // ic = ic0 + 4h + s.  A thread owns the (oc, ic) pairs tid and tid + 256 and
@@ -268,21 +227,6 @@ static_assert(ICC * OCB % kThreads == 0, "weight unit pairs");
 struct WRegs {
     float v[W_PAIRS_PER_THREAD][UNIT_TAPS];
 };
-
-// The 9 taps of (oc, ic) pair tid + 256q (one of the 2 slices of a unit's loads).
-template <int kMode>
-__device__ __forceinline__ void load_w_pair(const Args& a, const Tile& t, int64_t ic0, int kd, int q, WRegs& r) {
-    const int p = threadIdx.x + q * kThreads;
-    const int oc = p >> 3, j = p & 7;
-    const int64_t goc = t.oc0 + oc, gic = ic0 + j;
-    const bool ok = goc < a.Cout && gic < a.Cin;
-    // first source element of this unit's 9-tap run
-    const int64_t first = kMode == kConvWeights ? (goc * a.Cin + gic) * 27 + kd * UNIT_TAPS
-                                                : (gic * a.Cout + goc) * 27 + (18 - kd * UNIT_TAPS);
-    const float* src = a.w + (ok ? first : 0);
-#pragma unroll
-    for (int u = 0; u < UNIT_TAPS; ++u) r.v[q][u] = src[u];
-}
 
 // Buffer-load form of the weight unit loads: per thread and pair a byte
 // offset fixed for the tile (kOutside for output channels past Cout), the
@@ -320,7 +264,9 @@ __device__ __forceinline__ void load_w_pair_buf(const Args& a, const WOffsets& o
         r.v[q][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo + 4u * u, (int)(ue * 4), 0));
 }
 
-// LDS write of a weight unit loaded by buffer loads (pairs outside are already 0)
+// LDS write of a weight unit loaded by buffer loads (pairs outside are already
+// 0).  Conv: source tap kd*9 + u is unit tap u; transposed: source t = 18 - 9kd
+// + u is tap 26 - t = 8 + 9kd - u, i.e. unit tap 8 - u.
 template <int kMode>
 __device__ __forceinline__ void store_w_buf(const WRegs& r, float* lw) {
 #pragma unroll
@@ -331,31 +277,6 @@ __device__ __forceinline__ void store_w_buf(const WRegs& r, float* lw) {
         float* dst = lw + ((nt * 2 + h) * 32 + n) * 4 + s;
 #pragma unroll
         for (int u = 0; u < UNIT_TAPS; ++u) dst[(kMode == kConvWeights ? u : 8 - u) * WTAP] = r.v[q][u];
-    }
-}
-
-template <int kMode>
-__device__ __forceinline__ void load_w(const Args& a, const Tile& t, int64_t ic0, int kd, WRegs& r) {
-#pragma unroll
-    for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) load_w_pair<kMode>(a, t, ic0, kd, q, r);
-}
-
-template <int kMode>
-__device__ __forceinline__ void store_w(const Args& a, const Tile& t, int64_t ic0, const WRegs& r, float* lw) {
-#pragma unroll
-    for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) {
-        const int p = threadIdx.x + q * kThreads;
-        const int oc = p >> 3, j = p & 7;
-        const bool ok = t.oc0 + oc < a.Cout && ic0 + j < a.Cin;
-        const int nt = oc >> 5, n = oc & 31, h = j >> 2, s = j & 3;
-        float* dst = lw + ((nt * 2 + h) * 32 + n) * 4 + s;
-#pragma unroll
-        for (int u = 0; u < UNIT_TAPS; ++u) {
-            // conv: source tap kd*9 + u is unit tap u; transposed: source t = 18 - 9kd + u
-            // is tap 26 - t = 8 + 9kd - u, i.e. unit tap 8 - u
-            const int t9 = kMode == kConvWeights ? u : 8 - u;
-            dst[t9 * WTAP] = ok ? r.v[q][u] : 0.f;
-        }
     }
 }
 
@@ -511,19 +432,40 @@ __device__ __forceinline__ SlotTaps slot_taps(const TapSet& ts) {
     return st;
 }
 
-__device__ __forceinline__ void load_w_taps(const Args& a, const Tile& t, const TapSet& ts, const SlotTaps& st,
-                                            int64_t ic0, int i0, WRegs& r) {
-    const int ntu = ts.d[1].n * ts.d[2].n;
-    const int wk0 = pick3(ts.d[0].k, i0) * ts.K1 * ts.K2;
+// Weights of one unit of the tap-table K loop, by buffer loads: per thread and
+// pair a byte offset fixed for the tile (kOutside for output channels past
+// Cout), the chunk, the unit's dim-0 tap and each slot's dims-1/2 tap as
+// uniform offsets; pairs past Cin and slots past the unit's taps read 0.
+struct WTapOffsets {
+    uint32_t vo[W_PAIRS_PER_THREAD];
+};
+
+__device__ __forceinline__ WTapOffsets w_tap_offsets(const Args& a, const Tile& t, const TapSet& ts) {
+    WTapOffsets o;
 #pragma unroll
     for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) {
         const int p = threadIdx.x + q * kThreads;
         const int oc = p >> 3, j = p & 7;
-        const int64_t goc = t.oc0 + oc, gic = ic0 + j;
-        const bool ok = goc < a.Cout && gic < a.Cin;
-        const float* src = a.w + (ok ? (gic * a.Cout + goc) * ts.Kvol + wk0 : 0);
+        const int64_t goc = t.oc0 + oc;
+        o.vo[q] = goc < a.Cout ? (uint32_t)(((int64_t)j * a.Cout + goc) * ts.Kvol * 4) : kOutside;
+    }
+    return o;
+}
+
+__device__ __forceinline__ void load_w_taps_buf(const Args& a, const TapSet& ts, const SlotTaps& st,
+                                                const WTapOffsets& o, int64_t ic0, int i0, WRegs& r) {
+    const int ntu = ts.d[1].n * ts.d[2].n;
+    const int wk0 = pick3(ts.d[0].k, i0) * ts.K1 * ts.K2;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.w, (uint32_t)(a.Cin * a.Cout * ts.Kvol * 4));
+    const int base = (int)((ic0 * a.Cout * ts.Kvol + wk0) * 4);
 #pragma unroll
-        for (int u = 0; u < UNIT_TAPS; ++u) r.v[q][u] = u < ntu ? src[ok ? st.wk[u] : 0] : 0.f;
+    for (int q = 0; q < W_PAIRS_PER_THREAD; ++q) {
+        const int j = (threadIdx.x + q * kThreads) & 7;
+        const uint32_t vo = (int)ic0 + j < (int)a.Cin ? o.vo[q] : kOutside;
+#pragma unroll
+        for (int u = 0; u < UNIT_TAPS; ++u)
+            r.v[q][u] = u < ntu ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo, base + 4 * st.wk[u], 0))
+                                : 0.f;
     }
 }
 
@@ -557,13 +499,14 @@ __device__ __forceinline__ void mainloop_taps(const Args& a, const Tile& t, cons
     const SlotTaps st = slot_taps(ts);
     const int64_t nchunks = ceil_div(a.Cin, ICC);
     const XOffsets<kMT> xo = x_offsets<kMT>(a, t, pad);
+    const WTapOffsets wo = w_tap_offsets(a, t, ts);
     {
         XRegs<kMT> xr;
         WRegs wr;
-        load_x(a, t, xo, 0, xr);
-        load_w_taps(a, t, ts, st, 0, 0, wr);
-        store_x(a, xo, 0, xr, lx);
-        store_w<kConvWeights>(a, t, 0, wr, lw0);
+        load_x_buf(a, t, xo, 0, xr);
+        load_w_taps_buf(a, ts, st, wo, 0, 0, wr);
+        store_x_buf(a, 0, xr, lx);
+        store_w_buf<kConvWeights>(wr, lw0);
         __syncthreads();
     }
     int buf = 0;
@@ -576,8 +519,8 @@ __device__ __forceinline__ void mainloop_taps(const Args& a, const Tile& t, cons
             const int ni0 = chunk_end ? 0 : i0 + 1;
             WRegs wr;
             XRegs<kMT> xr;
-            if (!last_unit) load_w_taps(a, t, ts, st, nc * ICC, ni0, wr);
-            if (chunk_end && !last_unit) load_x(a, t, xo, nc * ICC, xr);
+            if (!last_unit) load_w_taps_buf(a, ts, st, wo, nc * ICC, ni0, wr);
+            if (chunk_end && !last_unit) load_x_buf(a, t, xo, nc * ICC, xr);
             const float* lw = lw0 + buf * LDS_W;
             const int xo0 = pick3(ts.d[0].off, i0) * HH * HW * 4;
 #pragma unroll
@@ -603,11 +546,11 @@ __device__ __forceinline__ void mainloop_taps(const Args& a, const Tile& t, cons
             if (last_unit) break;
             if (chunk_end) {
                 __syncthreads();  // every wave is done with this chunk's halo
-                store_x(a, xo, nc * ICC, xr, lx);
+                store_x_buf(a, nc * ICC, xr, lx);
             }
             // the other weight buffer was last read by the previous unit, which
             // every wave finished before the previous barrier
-            store_w<kConvWeights>(a, t, nc * ICC, wr, lw0 + (buf ^ 1) * LDS_W);
+            store_w_buf<kConvWeights>(wr, lw0 + (buf ^ 1) * LDS_W);
             __syncthreads();
             buf ^= 1;
         }

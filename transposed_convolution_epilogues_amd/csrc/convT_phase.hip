@@ -217,6 +217,11 @@ bool convT_phase_mfma_supported(const Geom& g, const void*, const void*, const v
     if (g.cin_g < 4 || g.cout_g < 8) return false;
     for (int j = 0; j < 3; ++j)
         if (!mfma333::fits_int32_tiles(g.O[j]) || g.k[j] > 16) return false;
+    // the K loop's buffer resources (a chunk of input planes, a group's
+    // weights) stay below 2^31 bytes
+    if ((int64_t)mfma333::ICC * g.S[0] * g.S[1] * g.S[2] * 4 >= (1ll << 31) ||
+        g.cin_g * g.cout_g * g.k[0] * g.k[1] * g.k[2] * 4 >= (1ll << 31))
+        return false;
     PhaseArgs pa;
     return build_phase_args(g, pa);
 }
