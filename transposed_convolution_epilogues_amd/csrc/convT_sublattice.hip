@@ -275,9 +275,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         mainloop<kMode, kMT>(a, t, lds, acc);
     }
 
-    // stage and write the tile 32 output channels (one N tile) at a time
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
+    if (kLattice == 2 && t.d0 + TD <= a.O[0] && t.h0 + TH <= a.O[1] && t.w0 + TW <= a.O[2]) {
+        // A tile wholly inside the sub-lattice writes the odd rows of its odd
+        // planes straight from the accumulators: a lane holds 4 consecutive
+        // tile voxels x0 .. x0 + 3 of one channel, i.e. destination columns
+        // 2x0 .. 2x0 + 7 alternating bias and value, two 16-byte stores.  The
+        // stores are buffer stores into the workgroup's channel block, so
+        // channels past Cout fall outside the resource and write nothing.
+        const int64_t vol = a.Y[0] * a.Y[1] * a.Y[2];
+        const int nvalid = (int)(a.Cout - t.oc0 < OCB ? a.Cout - t.oc0 : OCB);
+        const __amdgpu_buffer_rsrc_t ys =
+            buffer_rsrc(a.y + (t.n * a.Cout + t.oc0) * vol, (uint32_t)(nvalid * vol * 4));
+        const int h = lane >> 5, n = lane & 31;
+        const int Y1 = (int)a.Y[1], Y2 = (int)a.Y[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const float bv = sbias[32 * nt + n];
+            const unsigned cb = (unsigned)(32 * nt + n) * (unsigned)vol * 4u;
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+                for (int aa = 0; aa < 4; ++aa) {
+                    const int y = (aa >> 1) + 2 * (wv >> 1), x0 = 8 * (aa & 1) + 4 * h + 16 * (wv & 1);
+                    const int row = (2 * ((int)t.d0 + mt) + 1) * Y1 + 2 * ((int)t.h0 + y) + 1;
+                    const unsigned off = cb + 4u * (unsigned)(row * Y2 + 2 * ((int)t.w0 + x0));
+                    const f32x4 lo = {bv, acc[mt][nt][4 * aa] + bv, bv, acc[mt][nt][4 * aa + 1] + bv};
+                    const f32x4 hi = {bv, acc[mt][nt][4 * aa + 2] + bv, bv, acc[mt][nt][4 * aa + 3] + bv};
+                    __builtin_amdgcn_raw_buffer_store_b128(lo, ys, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(hi, ys, off + 16u, 0, 0);
+                    // the even column after the last tile voxel of a row ends the row
+                    if (x0 == TW - 4 && 2 * ((int)t.w0 + TW) < Y2)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bv), ys, off + 32u, 0, 0);
+                }
+        }
+        return;
+    }
+
+    // stage and write the tile 32 output channels (one N tile) at a time
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         __syncthreads();  // every wave is done reading the operand tiles, or the previous half
@@ -351,8 +387,9 @@ bool convT_s2_sublattice_supported(const Geom& g, const void*, const void*, cons
         !mfma333::fits_int32_tiles(g.O[1]) || !mfma333::fits_int32_tiles(g.O[2]))
         return false;
     // the bias pass indexes a plane in 32 bits and decodes row slots below
-    // 2^22 with float reciprocals
-    return g.O[1] * g.O[2] < (1 << 25);
+    // 2^22 with float reciprocals; the odd-row stores address a 64-channel
+    // block of the output with 32-bit byte offsets
+    return g.O[1] * g.O[2] < (1 << 25) && (int64_t)OCB * g.O[0] * g.O[1] * g.O[2] * 4 < (1ll << 31);
 }
 
 hipError_t launch_convT_s2_sublattice(const float* x, const float* w, const float* bias, float* y, const Geom& g,
