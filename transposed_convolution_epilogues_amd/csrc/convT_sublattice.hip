@@ -169,10 +169,13 @@ struct EvenPlanes {
     float* y;
     const float* bias;  // LDS copy of all Cout biases, or null for none
     int64_t P, vol;     // floats per plane and per (sample, channel) volume
-    int64_t units;      // (sample, channel) volumes x plane pairs
-    int pairs, Y0, Y2, R, SLp, SLr, Cout;
-    __device__ __forceinline__ void slot(float* run, int s, int L, float v) const {
-        const int e0 = 4 * s - (int)(((uintptr_t)run >> 2) & 3);
+    int units;          // (sample, channel) volumes x plane pairs
+    int pairs, Y0, Y2, R, SLr, Cout;
+    int q, rem;         // units per chunk of the n * gridDim chunks; the first rem chunks take one more
+    // the 16-byte slot s of a run of L floats whose start is m floats past a
+    // 16-byte boundary
+    __device__ __forceinline__ void slot(float* run, int m, int s, int L, float v) const {
+        const int e0 = 4 * s - m;
         if (e0 >= 0 && e0 + 3 < L) {
             *reinterpret_cast<f32x4*>(run + e0) = f32x4{v, v, v, v};
         } else {
@@ -181,32 +184,55 @@ struct EvenPlanes {
                 if (e0 + k >= 0 && e0 + k < L) run[e0 + k] = v;
         }
     }
-    __device__ void operator()(int64_t u, int64_t n) const {
+    // The unit bookkeeping is 32-bit and incremental (one division pair per
+    // call): 64-bit divisions here, a long scalar sequence each, held every
+    // wave's matrix-core work at each call.
+    __device__ void operator()(int64_t u, int64_t) const {
         // chunks in XCD-aware order: consecutive workgroup ids go round-robin
         // to the 8 XCDs, so remapped, each XCD writes one contiguous run of
         // the unit's chunks (about 0.5 % on the 32->64 stride-2 dilation-2
         // transposed conv of x[16,32,16,32,32])
-        const int64_t nb = gridDim.x;
-        int64_t bx = blockIdx.x;
+        const int nb = (int)gridDim.x;
+        int bx = (int)blockIdx.x;
         if ((nb & 7) == 0) bx = (bx & 7) * (nb >> 3) + (bx >> 3);
-        const int64_t nch = n * nb, chunk = u * nb + bx;
-        const int64_t q = units / nch, rem = units - q * nch;
-        const int64_t g0 = chunk * q + (chunk < rem ? chunk : rem);
-        const int64_t g1 = g0 + q + (chunk < rem ? 1 : 0);
+        const int chunk = (int)u * nb + bx;
+        const int g0 = chunk * q + (chunk < rem ? chunk : rem);
+        const int cnt = q + (chunk < rem ? 1 : 0);
+        if (cnt == 0) return;
+        int volume = g0 / pairs;
+        int k = g0 - volume * pairs;
+        int c = volume % Cout;
         const Div div_slr(SLr);
-        for (int64_t unit = g0; unit < g1; ++unit) {
-            const int64_t volume = unit / pairs;
-            const int k = (int)(unit - volume * pairs);
-            const float v = bias ? bias[volume % Cout] : 0.f;
-            float* base = y + volume * vol + (int64_t)(2 * k) * P;
-            for (int s = threadIdx.x; s < SLp; s += kThreads) slot(base, s, (int)P, v);
+        const int Pi = (int)P;
+        for (int i = 0; i < cnt; ++i) {
+            const float v = bias ? bias[c] : 0.f;
+            float* base = y + (int64_t)volume * vol + (int64_t)(2 * k) * P;
+            const int mb = (int)(((uintptr_t)base >> 2) & 3);
+            // plane 2k: the 16-byte aligned body by buffer stores at a
+            // per-thread constant offset from a uniform base, the up to 3
+            // floats before and after it one by one
+            {
+                const int head = (4 - mb) & 3, nbody = (Pi - head) >> 2, tail = (Pi - head) & 3;
+                const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base + head, (uint32_t)(nbody * 16));
+                const f32x4 vv = {v, v, v, v};
+                for (int g = threadIdx.x; g < nbody; g += kThreads)
+                    __builtin_amdgcn_raw_buffer_store_b128(vv, rs, 16u * (unsigned)g, 0, 0);
+                if ((int)threadIdx.x < head) base[threadIdx.x] = v;
+                if ((int)threadIdx.x < tail) base[head + 4 * nbody + threadIdx.x] = v;
+            }
             if (2 * k + 1 < Y0) {
                 float* odd = base + P;
                 const int items = R * SLr;
-                for (int i = threadIdx.x; i < items; i += kThreads) {
-                    const int r = div_slr.quot(i);
-                    slot(odd + (int64_t)(2 * r) * Y2, i - r * SLr, Y2, v);
+                for (int j = threadIdx.x; j < items; j += kThreads) {
+                    const int r = div_slr.quot(j);
+                    float* run = odd + (int64_t)(2 * r) * Y2;
+                    slot(run, (int)(((uintptr_t)run >> 2) & 3), j - r * SLr, Y2, v);
                 }
+            }
+            if (++k == pairs) {
+                k = 0;
+                ++volume;
+                if (++c == Cout) c = 0;
             }
         }
     }
@@ -263,11 +289,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         ep.P = a.Y[1] * a.Y[2];
         ep.vol = a.Y[0] * ep.P;
         ep.pairs = (int)((a.Y[0] + 1) / 2);
-        ep.units = a.N * a.Cout * ep.pairs;
+        ep.units = (int)(a.N * a.Cout * ep.pairs);
+        const int nch = 3 * (int)ceil_div(a.Cin, ICC) * (int)gridDim.x;  // K-loop units x workgroups
+        ep.q = ep.units / nch;
+        ep.rem = ep.units - ep.q * nch;
         ep.Y0 = (int)a.Y[0];
         ep.Y2 = (int)a.Y[2];
         ep.R = (int)((a.Y[1] + 1) / 2);
-        ep.SLp = (int)((ep.P + 6) >> 2);
         ep.SLr = (int)((a.Y[2] + 6) >> 2);
         ep.Cout = (int)a.Cout;
         mainloop<kMode, kMT>(a, t, lds, acc, ep);
@@ -386,10 +414,11 @@ bool convT_s2_sublattice_supported(const Geom& g, const void*, const void*, cons
     if (g.groups != 1 || g.Cout > kMaxBiasLds || !mfma333::fits_buffers(g) || !mfma333::fits_int32_tiles(g.O[0]) ||
         !mfma333::fits_int32_tiles(g.O[1]) || !mfma333::fits_int32_tiles(g.O[2]))
         return false;
-    // the bias pass indexes a plane in 32 bits and decodes row slots below
-    // 2^22 with float reciprocals; the odd-row stores address a 64-channel
-    // block of the output with 32-bit byte offsets
-    return g.O[1] * g.O[2] < (1 << 25) && (int64_t)OCB * g.O[0] * g.O[1] * g.O[2] * 4 < (1ll << 31);
+    // the bias pass indexes a plane in 32 bits, decodes row slots below 2^22
+    // with float reciprocals and counts its units in 32 bits; the odd-row
+    // stores address a 64-channel block of the output with 32-bit byte offsets
+    return g.O[1] * g.O[2] < (1 << 25) && (int64_t)OCB * g.O[0] * g.O[1] * g.O[2] * 4 < (1ll << 31) &&
+           g.N * g.Cout * ((g.O[0] + 1) / 2) < (1ll << 30);
 }
 
 hipError_t launch_convT_s2_sublattice(const float* x, const float* w, const float* bias, float* y, const Geom& g,
