@@ -305,10 +305,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
-    if (kLattice == 2 && t.d0 + TD <= a.O[0] && t.h0 + TH <= a.O[1] && t.w0 + TW <= a.O[2]) {
-        // A tile wholly inside the sub-lattice writes the odd rows of its odd
-        // planes straight from the accumulators: a lane holds 4 consecutive
-        // tile voxels x0 .. x0 + 3 of one channel, i.e. destination columns
+    if (t.d0 + TD <= a.O[0] && t.h0 + TH <= a.O[1] && t.w0 + TW <= a.O[2]) {
+        // A tile wholly inside the grid writes straight from the accumulators:
+        // a lane holds 4 consecutive tile voxels x0 .. x0 + 3 of one channel.
+        // Plain conv: destination columns x0 .. x0 + 3, one 16-byte store.
+        // Transposed conv: the odd rows of the odd planes, destination columns
         // 2x0 .. 2x0 + 7 alternating bias and value, two 16-byte stores.  The
         // stores are buffer stores into the workgroup's channel block, so
         // channels past Cout fall outside the resource and write nothing.
@@ -327,15 +328,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int aa = 0; aa < 4; ++aa) {
                     const int y = (aa >> 1) + 2 * (wv >> 1), x0 = 8 * (aa & 1) + 4 * h + 16 * (wv & 1);
-                    const int row = (2 * ((int)t.d0 + mt) + 1) * Y1 + 2 * ((int)t.h0 + y) + 1;
-                    const unsigned off = cb + 4u * (unsigned)(row * Y2 + 2 * ((int)t.w0 + x0));
-                    const f32x4 lo = {bv, acc[mt][nt][4 * aa] + bv, bv, acc[mt][nt][4 * aa + 1] + bv};
-                    const f32x4 hi = {bv, acc[mt][nt][4 * aa + 2] + bv, bv, acc[mt][nt][4 * aa + 3] + bv};
-                    __builtin_amdgcn_raw_buffer_store_b128(lo, ys, off, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b128(hi, ys, off + 16u, 0, 0);
-                    // the even column after the last tile voxel of a row ends the row
-                    if (x0 == TW - 4 && 2 * ((int)t.w0 + TW) < Y2)
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bv), ys, off + 32u, 0, 0);
+                    if (kLattice == 1) {
+                        const int row = ((int)t.d0 + mt) * Y1 + (int)t.h0 + y;
+                        const unsigned off = cb + 4u * (unsigned)(row * Y2 + (int)t.w0 + x0);
+                        const f32x4 v = {acc[mt][nt][4 * aa] + bv, acc[mt][nt][4 * aa + 1] + bv,
+                                         acc[mt][nt][4 * aa + 2] + bv, acc[mt][nt][4 * aa + 3] + bv};
+                        __builtin_amdgcn_raw_buffer_store_b128(v, ys, off, 0, 0);
+                    } else {
+                        const int row = (2 * ((int)t.d0 + mt) + 1) * Y1 + 2 * ((int)t.h0 + y) + 1;
+                        const unsigned off = cb + 4u * (unsigned)(row * Y2 + 2 * ((int)t.w0 + x0));
+                        const f32x4 lo = {bv, acc[mt][nt][4 * aa] + bv, bv, acc[mt][nt][4 * aa + 1] + bv};
+                        const f32x4 hi = {bv, acc[mt][nt][4 * aa + 2] + bv, bv, acc[mt][nt][4 * aa + 3] + bv};
+                        __builtin_amdgcn_raw_buffer_store_b128(lo, ys, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(hi, ys, off + 16u, 0, 0);
+                        // the even column after the last tile voxel of a row ends the row
+                        if (x0 == TW - 4 && 2 * ((int)t.w0 + TW) < Y2)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bv), ys, off + 32u, 0, 0);
+                    }
                 }
         }
         return;
@@ -387,7 +396,8 @@ bool conv3x3x3_mfma_supported(const Geom& g, const void*, const void*, const voi
     for (int j = 0; j < 3; ++j)
         if (g.k[j] != 3 || g.s[j] != 1 || g.d[j] != 1 || g.p[j] != g.p[0]) return false;
     // the MFMA tile pays off once there are several input channels
-    return g.groups == 1 && g.Cin >= 4 && g.Cout >= 8 && mfma333::fits_buffers(g) && mfma333::fits_int32_tiles(g.O[0]) &&
+    return g.groups == 1 && g.Cin >= 4 && g.Cout >= 8 && mfma333::fits_buffers(g) &&
+           (int64_t)OCB * g.O[0] * g.O[1] * g.O[2] * 4 < (1ll << 31) && mfma333::fits_int32_tiles(g.O[0]) &&
            mfma333::fits_int32_tiles(g.O[1]) && mfma333::fits_int32_tiles(g.O[2]);
 }
 
