@@ -105,10 +105,11 @@ struct Tile {
     int64_t oc0;
 };
 
+// (32-bit: the launchers keep the grid below 2^31 workgroups)
 template <int kMT>
 __device__ __forceinline__ Tile tile_of(const Args& a) {
-    const int64_t nb = (int64_t)gridDim.x;
-    int64_t b = blockIdx.x;
+    const int32_t nb = (int32_t)gridDim.x;
+    int32_t b = (int32_t)blockIdx.x;
     if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
     Tile t;
     t.oc0 = (b % a.oc_blocks) * OCB;
