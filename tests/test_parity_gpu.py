@@ -336,6 +336,11 @@ MEDIUM = {
     "convT_s2p1d2_cout80": W.CONFIGS["c3"].with_(x_shape=(1, 8, 3, 5, 6), cout=80),
     "convT_s2p1d2_bias": W.CONFIGS["c3"].with_(x_shape=(2, 5, 3, 4, 33), cout=16, bias=True),
     "convT_s2p1d2_bias_cout72": W.CONFIGS["c3"].with_(x_shape=(3, 6, 3, 3, 5), cout=72, bias=True),
+    # enough tiles per (sample, channel) volume that each K-loop unit's share of the bias-only planes is at
+    # most 3 plane pairs: the fixed-count form of that pass (c3's own); 8 tiles x 12 units for 64 x 3 pairs
+    "convT_s2p1d2_fixed_run": W.CONFIGS["c3"].with_(x_shape=(1, 32, 2, 16, 64)),
+    # the same with bias, 40 channels, partial tiles in two dims: 24 workgroups x 6 units for 2 x 40 x 4 pairs
+    "convT_s2p1d2_fixed_run_bias": W.CONFIGS["c3"].with_(x_shape=(2, 16, 3, 13, 70), cout=40, bias=True),
     "conv3d_k331_bias_dil": W.CONFIGS["c2"].with_(x_shape=(1, 2, 9, 12, 5), cout=20, dilation=(2, 2, 1),
                                                   bias=True),
     # rows of O1*S2 floats with O1*S2 % 4 == 0 and 64 channels: the float4 store path, with a partial

@@ -283,14 +283,15 @@ __device__ __forceinline__ void store_w_buf(const WRegs& r, float* lw) {
 
 // Side work of a kernel that does not overlap anything with the K loop.
 struct NoSideWork {
+    static constexpr int kTap = 0;
     __device__ void operator()(int64_t, int64_t) const {}
 };
 
 // Runs the whole K loop; acc[mt][nt] holds the 32x32 result tiles.  side(u, n)
-// is called once per weight unit u of n, after the unit's first tap of MFMAs
-// and its first slice of prefetch loads are issued: work placed there (stores
-// that do not depend on the result) overlaps the matrix-core work.  It must
-// not touch the operand LDS.
+// is called once per weight unit u of n, after the MFMAs and the slice of
+// prefetch loads of the unit's tap Side::kTap are issued: work placed there
+// (stores that do not depend on the result) overlaps the matrix-core work.
+// It must not touch the operand LDS.
 template <int kMode, int kMT, class Side = NoSideWork>
 __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* lds, f32x16 (&acc)[kMT][2],
                                          const Side& side = Side()) {
@@ -370,11 +371,11 @@ __device__ __forceinline__ void mainloop(const Args& a, const Tile& t, float* ld
                     if (t9 >= 1 && kd == 2 && !last_unit)
                         load_x_slice_buf(a, t, xo, nc * ICC, (t9 - 1) >> 2, (t9 - 1) & 3, xr);
                     __builtin_amdgcn_sched_barrier(0);
-                    // side work goes behind the first tap's MFMAs: its stores issue
-                    // while the matrix core runs them (about 2% faster on the
-                    // 32->64 stride-2 dilation-2 transposed conv of x[16,32,16,32,32]
-                    // than issuing it before the unit's MFMAs)
-                    if (t9 == 0) side(c * 3 + kd, nchunks * 3);
+                    // side work goes behind a tap's MFMAs: its stores issue while
+                    // the matrix core runs them (about 2% faster on the 32->64
+                    // stride-2 dilation-2 transposed conv of x[16,32,16,32,32] than
+                    // issuing it before the unit's MFMAs)
+                    if (t9 == Side::kTap) side(c * 3 + kd, nchunks * 3);
                 }
             if (last_unit) break;
             if (kd == 2) {
