@@ -166,8 +166,9 @@ struct TileValue {
 // address.  The units are split into n * gridDim chunks of near-equal size;
 // K-loop unit u of workgroup b writes chunk u * gridDim + b.
 // Limits of the bias pass's fixed-count form: plane pairs per call, 16-byte
-// stores per thread for an even plane's body and for an odd plane's even rows
-constexpr int kMaxRun = 3, kBodyIt = 5, kRowIt = 3;
+// stores per thread for one plane pair (an even plane and its odd plane's
+// even rows)
+constexpr int kMaxRun = 3, kPairIt = 7;
 
 template <bool kFixed>
 struct EvenPlanes {
@@ -177,9 +178,10 @@ struct EvenPlanes {
     int units;          // (sample, channel) volumes x plane pairs
     int pairs, Y0, Y2, R, SLr, Cout;
     int q, rem;         // units per chunk of the n * gridDim chunks; the first rem chunks take one more
-    // Fixed-count form (see below): this thread's byte offsets of its
-    // odd-plane row stores (kOutside where it has none)
-    uint32_t roff[kRowIt], rtoff;
+    // Fixed-count form (see below): this thread's byte offsets, from the
+    // even plane's start, of its 16-byte and 4-byte stores in a plane pair
+    // (kOutside where it has none)
+    uint32_t poff[kPairIt], ptoff;
     // the pass goes behind the first tap of each unit (taps 0-5 measured
     // within 0.5 % of each other; the last tap about 2.5 % slower)
     static constexpr int kTap = 0;
@@ -213,41 +215,23 @@ struct EvenPlanes {
         int k = g0 - volume * pairs;
         int c = volume % Cout;
         if (kFixed) {
-            // The same number of store instructions on every call, whatever
-            // its run: kMaxRun plane pairs (the ones past the run write
-            // nothing: their resources are empty), each with kBodyIt + 1
-            // stores for the even plane and kRowIt + 1 for the odd plane's
-            // even rows.  The compiler then knows how many memory operations
-            // follow the unit's prefetch loads and waits for those loads
-            // without waiting for these stores, which drain during the next
-            // unit.
+            // Branch-free: kMaxRun plane pairs (the ones past the run write
+            // nothing, their resources being empty), each kPairIt 16-byte and
+            // one 4-byte buffer store per thread at offsets fixed for the
+            // thread.  The even plane and the odd plane's even rows go out as
+            // 16-byte stores from their starts (4-byte aligned, which buffer
+            // stores allow), their last Y2 % 4 floats as single floats; the
+            // resource ends after the even plane when there is no odd plane.
 #pragma unroll
             for (int i = 0; i < kMaxRun; ++i) {
-                const bool ok = i < cnt;
                 const float v = bias ? bias[c] : 0.f;
                 const f32x4 vv = {v, v, v, v};
                 float* base = y + (int64_t)volume * vol + (int64_t)(2 * k) * P;
-                const int Pi = (int)P;
-                const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, ok ? (uint32_t)Pi * 4u : 0u);
-                const int mb = (int)(((uintptr_t)base >> 2) & 3);
-                const int head = (4 - mb) & 3, nbody = (Pi - head) >> 2, tail = (Pi - head) & 3;
+                const uint32_t bytes = i < cnt ? (uint32_t)P * (2 * k + 1 < Y0 ? 8u : 4u) : 0u;
+                const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, bytes);
 #pragma unroll
-                for (int m = 0; m < kBodyIt; ++m) {
-                    const int g = (int)threadIdx.x + m * kThreads;
-                    __builtin_amdgcn_raw_buffer_store_b128(vv, rs, g < nbody ? 4u * (unsigned)(head + 4 * g) : kOutside,
-                                                           0, 0);
-                }
-                // lanes 0-2 the head, lanes 3-5 the tail
-                const int l = (int)threadIdx.x;
-                const uint32_t ht = l < head                    ? 4u * (unsigned)l
-                                    : (l >= 3 && l - 3 < tail) ? 4u * (unsigned)(head + 4 * nbody + l - 3)
-                                                               : kOutside;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, ht, 0, 0);
-                const __amdgpu_buffer_rsrc_t ro =
-                    buffer_rsrc(base + P, ok && 2 * k + 1 < Y0 ? (uint32_t)Pi * 4u : 0u);
-#pragma unroll
-                for (int m = 0; m < kRowIt; ++m) __builtin_amdgcn_raw_buffer_store_b128(vv, ro, roff[m], 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ro, rtoff, 0, 0);
+                for (int m = 0; m < kPairIt; ++m) __builtin_amdgcn_raw_buffer_store_b128(vv, rs, poff[m], 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, ptoff, 0, 0);
                 if (++k == pairs) {
                     k = 0;
                     ++volume;
@@ -353,23 +337,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         ep.R = (int)((a.Y[1] + 1) / 2);
         ep.SLr = (int)((a.Y[2] + 6) >> 2);
         ep.Cout = (int)a.Cout;
-        {
-            // Fixed-count form: an odd plane's even rows (R rows of Y2 floats,
-            // 2 Y2 apart) as Y2 / 4 16-byte stores per row from the row start
-            // (4-byte aligned, which 16-byte buffer stores allow) and the Y2 % 4
-            // floats after them one by one.
-            // (the launcher picks kFixed where these counts suffice)
-            const int sl = ep.Y2 >> 2, rm = ep.Y2 & 3;
+        if (kFixed) {
+            // The plane pair's 16-byte items: the even plane's P / 4 from its
+            // start, then Y2 / 4 from the start of each of the odd plane's R
+            // even rows (2 Y2 apart, starting P floats on); its single floats:
+            // the even plane's last P % 4, then the last Y2 % 4 of each such
+            // row.  The launcher picks kFixed where kPairIt items per thread
+            // and one single float per thread suffice.
+            const int Pi = (int)ep.P, Y2 = ep.Y2;
+            const int nb = Pi >> 2, pr = Pi & 3, sl = Y2 >> 2, rm = Y2 & 3;
             const Div dsl(sl > 0 ? sl : 1), drm(rm > 0 ? rm : 1);
 #pragma unroll
-            for (int m = 0; m < kRowIt; ++m) {
+            for (int m = 0; m < kPairIt; ++m) {
                 const int i = (int)threadIdx.x + m * kThreads;
-                const int r = dsl.quot(i), j = i - r * sl;
-                ep.roff[m] = sl > 0 && r < ep.R ? 4u * (unsigned)(2 * r * ep.Y2 + 4 * j) : kOutside;
+                const int e = i - nb, r = dsl.quot(e > 0 ? e : 0), j = e - r * sl;
+                ep.poff[m] = i < nb                   ? 16u * (unsigned)i
+                             : sl > 0 && r < ep.R ? 4u * (unsigned)(Pi + 2 * r * Y2 + 4 * j)
+                                                  : kOutside;
             }
-            const int l = (int)threadIdx.x;
-            const int r = drm.quot(l), e = l - r * (rm > 0 ? rm : 1);
-            ep.rtoff = rm > 0 && r < ep.R ? 4u * (unsigned)(2 * r * ep.Y2 + 4 * sl + e) : kOutside;
+            const int l = (int)threadIdx.x, e = l - pr, r = drm.quot(e > 0 ? e : 0), f = e - r * (rm > 0 ? rm : 1);
+            ep.ptoff = l < pr                  ? 4u * (unsigned)(4 * nb + l)
+                       : rm > 0 && r < ep.R ? 4u * (unsigned)(Pi + 2 * r * Y2 + 4 * sl + f)
+                                            : kOutside;
         }
         mainloop<kMode, kMT>(a, t, lds, acc, ep);
     } else {
@@ -518,13 +507,13 @@ hipError_t launch_convT_s2_sublattice(const float* x, const float* w, const floa
     const int64_t blocks = a.N * (int64_t)a.tiles[0] * a.tiles[1] * a.tiles[2] * a.oc_blocks;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     // the bias pass's counts, as the kernel derives them: plane pairs per call
-    // (units over K-loop units x workgroups), 16-byte stores per even plane
-    // body and per odd plane's even rows, single floats after the rows
+    // (units over K-loop units x workgroups), 16-byte items and single floats
+    // per plane pair (an even plane and its odd plane's even rows)
     const int64_t P = g.O[1] * g.O[2], pairs = (g.O[0] + 1) / 2, R = (g.O[1] + 1) / 2;
     const int64_t units = g.N * g.Cout * pairs, nch = 3 * ceil_div(g.Cin, ICC) * blocks;
     const int64_t run = units / nch + (units % nch ? 1 : 0);
-    const bool fixed = run <= kMaxRun && (P >> 2) <= kBodyIt * kThreads && R * (g.O[2] >> 2) <= kRowIt * kThreads &&
-                       R * (g.O[2] & 3) <= kThreads;
+    const bool fixed = run <= kMaxRun && (P >> 2) + R * (g.O[2] >> 2) <= kPairIt * kThreads &&
+                       (P & 3) + R * (g.O[2] & 3) <= kThreads;
     if (fixed)
         hipLaunchKernelGGL((conv333_store_kernel<kConvTFlipped, 2, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
                            st, a);
