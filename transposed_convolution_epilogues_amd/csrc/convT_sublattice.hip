@@ -165,6 +165,15 @@ struct TileValue {
 // plane 2k + 1; each run is cut into 16-byte aligned slots counted from its
 // address.  The units are split into n * gridDim chunks of near-equal size;
 // K-loop unit u of workgroup b writes chunk u * gridDim + b.
+// Cache policy of the bias pass's stores: non-temporal (the nt bit), so the
+// 435 MB of bias-only planes of the 32->64 stride-2 dilation-2 transposed
+// conv of x[16,32,16,32,32] stream out instead of taking the caches from the
+// K loop's operands: 0.291 -> 0.257-0.264 ms there in back-to-back calls,
+// 0.289 -> 0.293-0.295 ms after a 512 MB write has left the caches dirty.
+// (Non-temporal stores of the interleaved odd rows instead cost 0.26 ->
+// 0.49 ms: they only pay for whole contiguous lines.)
+constexpr int kStream = 2;
+
 // Limits of the bias pass's fixed-count form: plane pairs per call, 16-byte
 // stores per thread for one plane pair (an even plane and its odd plane's
 // even rows)
@@ -230,8 +239,8 @@ struct EvenPlanes {
                 const uint32_t bytes = i < cnt ? (uint32_t)P * (2 * k + 1 < Y0 ? 8u : 4u) : 0u;
                 const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, bytes);
 #pragma unroll
-                for (int m = 0; m < kPairIt; ++m) __builtin_amdgcn_raw_buffer_store_b128(vv, rs, poff[m], 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, ptoff, 0, 0);
+                for (int m = 0; m < kPairIt; ++m) __builtin_amdgcn_raw_buffer_store_b128(vv, rs, poff[m], 0, kStream);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, ptoff, 0, kStream);
                 if (++k == pairs) {
                     k = 0;
                     ++volume;
