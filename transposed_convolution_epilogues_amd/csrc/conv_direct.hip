@@ -98,6 +98,62 @@ __global__ __launch_bounds__(kBlock) void conv3d_direct_kernel(const float* __re
     }
 }
 
+// The same for a 3x3x3 kernel: the 27 taps of an input channel are unrolled,
+// so their loads issue together (the loop above waits for one weight and one
+// input value per tap), and the index arithmetic is 32-bit (the launcher
+// checks the sizes).  Taps outside the input are skipped as above, so the
+// sum is formed in the same order.
+__global__ __launch_bounds__(kBlock) void conv3d_k3_direct_kernel(const float* __restrict__ x,
+                                                                  const float* __restrict__ w,
+                                                                  const float* __restrict__ bias,
+                                                                  float* __restrict__ y, Geom g, int32_t total) {
+    const int O0 = (int)g.O[0], O1 = (int)g.O[1], O2 = (int)g.O[2];
+    const int S0 = (int)g.S[0], S1 = (int)g.S[1], S2 = (int)g.S[2];
+    const int Cout = (int)g.Cout, Cin = (int)g.Cin, cin_g = (int)g.cin_g, cout_g = (int)g.cout_g;
+    const int64_t plane = (int64_t)S0 * S1 * S2;
+    for (int idx = (int)(blockIdx.x * blockDim.x + threadIdx.x); idx < total; idx += (int)(gridDim.x * blockDim.x)) {
+        int f = idx;
+        const int o2 = f % O2;
+        f /= O2;
+        const int o1 = f % O1;
+        f /= O1;
+        const int o0 = f % O0;
+        f /= O0;
+        const int oc = f % Cout;
+        const int n = f / Cout;
+        const int grp = oc / cout_g;
+        // the taps' offsets in an input plane, and whether they are inside it
+        int off[27];
+        bool ok[27];
+#pragma unroll
+        for (int k0 = 0; k0 < 3; ++k0)
+#pragma unroll
+            for (int k1 = 0; k1 < 3; ++k1)
+#pragma unroll
+                for (int k2 = 0; k2 < 3; ++k2) {
+                    const int t = (k0 * 3 + k1) * 3 + k2;
+                    const int i0 = o0 * g.s[0] - g.p[0] + k0 * g.d[0];
+                    const int i1 = o1 * g.s[1] - g.p[1] + k1 * g.d[1];
+                    const int i2 = o2 * g.s[2] - g.p[2] + k2 * g.d[2];
+                    ok[t] = i0 >= 0 && i0 < S0 && i1 >= 0 && i1 < S1 && i2 >= 0 && i2 < S2;
+                    // formed from in-range coordinates only, so it stays below the plane size
+                    off[t] = ((ok[t] ? i0 : 0) * S1 + (ok[t] ? i1 : 0)) * S2 + (ok[t] ? i2 : 0);
+                }
+        float acc = 0.f;
+        for (int icg = 0; icg < cin_g; ++icg) {
+            const float* xc = x + (int64_t)(n * Cin + grp * cin_g + icg) * plane;
+            const float* wc = w + (int64_t)(oc * cin_g + icg) * 27;
+            float v[27];
+#pragma unroll
+            for (int t = 0; t < 27; ++t) v[t] = xc[off[t]];
+#pragma unroll
+            for (int t = 0; t < 27; ++t) acc = ok[t] ? fmaf(wc[t], v[t], acc) : acc;
+        }
+        if (bias) acc += bias[oc];
+        y[idx] = acc;
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void convT_gather_kernel(const float* __restrict__ x,
                                                               const float* __restrict__ w,
                                                               const float* __restrict__ bias,
@@ -342,7 +398,18 @@ inline unsigned grid_for(int64_t total) {
 hipError_t launch_conv3d_direct(const float* x, const float* w, const float* bias, float* y, const Geom& g,
                                 hipStream_t st) {
     const int64_t total = g.N * g.Cout * g.O[0] * g.O[1] * g.O[2];
-    hipLaunchKernelGGL(conv3d_direct_kernel, dim3(grid_for(total)), dim3(kBlock), 0, st, x, w, bias, y, g, total);
+    const bool k3 = g.k[0] == 3 && g.k[1] == 3 && g.k[2] == 3;
+    // 32-bit arithmetic in the 3x3x3 kernel: output index, sample-channel index,
+    // weight row, and every input coordinate it forms
+    const int64_t reach = 2 * (int64_t)g.d[0] + 2 * (int64_t)g.d[1] + 2 * (int64_t)g.d[2];
+    const bool small = total < (1ll << 30) && g.N * g.Cin < (1ll << 31) && g.Cout * g.cin_g < (1ll << 26) &&
+                       g.S[0] * g.S[1] * g.S[2] < (1ll << 31) &&
+                       (g.O[0] + g.O[1] + g.O[2]) * 4 * (int64_t)(g.s[0] + g.s[1] + g.s[2]) + reach < (1ll << 30);
+    if (k3 && small)
+        hipLaunchKernelGGL(conv3d_k3_direct_kernel, dim3(grid_for(total)), dim3(kBlock), 0, st, x, w, bias, y, g,
+                           (int32_t)total);
+    else
+        hipLaunchKernelGGL(conv3d_direct_kernel, dim3(grid_for(total)), dim3(kBlock), 0, st, x, w, bias, y, g, total);
     return hipGetLastError();
 }
 
