@@ -37,7 +37,7 @@ BENCH_KEYS = ("c1", "c2", "c3", "c4", "c5")
 # kernel that carries each workload (the roofline object names the dominant one)
 CSRC = "transposed_convolution_epilogues_amd/csrc/"
 KERNELS = {
-    "c1": ("conv3d_direct_kernel", [CSRC + "conv_direct.hip"]),
+    "c1": ("conv3d_k3_direct_kernel", [CSRC + "conv_direct.hip"]),
     "c2": ("conv_k1last_kernel", [CSRC + "conv_k1last.hip"]),
     "c3": ("conv333_store_kernel", [CSRC + "convT_sublattice.hip", CSRC + "conv333_mfma.h"]),
     "c4": ("swap_pool_kernel", [CSRC + "convT_bn_swap.hip"]),
